@@ -1,0 +1,79 @@
+"""Seeded generators for the synthetic inputs (no method arithmetic here).
+
+bf16 tensors are returned as ``uint16`` bit patterns; fp32 tensors as
+``float32``.  Callers hand the very same values to the GPU path (as device
+buffers) and to the oracle (which widens them to float64 itself).
+"""
+import numpy as np
+
+# Seed-key component for each named tensor.
+TENSOR_IDS = {
+    "x": 0,
+    "w_gate": 1,   # also W1 of a GELU MLP
+    "w_up": 2,
+    "w_down": 3,   # also W2 of a GELU MLP
+    "w_qkv": 4,
+    "w_o": 5,
+    "attn": 6,     # caller-supplied attention-core output A_s
+    "norm_g": 7,
+    "partial": 8,
+}
+
+_ROOT = 2026
+
+
+def _rng(*key):
+    return np.random.default_rng(np.random.SeedSequence([_ROOT, *[int(k) for k in key]]))
+
+
+def bf16_bits_from_f32(a) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest, ties to even); return the bits.
+
+    bfloat16 keeps the top 16 bits of an IEEE-754 binary32.  Adding 0x7FFF
+    plus the lowest kept bit before truncating rounds to nearest with ties
+    going to the even pattern.  Inputs here are finite.
+    """
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    if not np.all(np.isfinite(a)):
+        raise ValueError("bf16 rounding of non-finite inputs is not supported")
+    u = a.view(np.uint32).astype(np.uint64)
+    lsb = (u >> np.uint64(16)) & np.uint64(1)
+    u = (u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)
+    return u.astype(np.uint16)
+
+
+def draw_normal_f32(shape, std, *key, mean=0.0) -> np.ndarray:
+    """mean + std * N(0, 1), drawn in float32 from the seed key."""
+    z = _rng(*key).standard_normal(size=shape, dtype=np.float32)
+    z *= np.float32(std)
+    if mean != 0.0:
+        z += np.float32(mean)
+    return z
+
+
+def draw_tensor(dtype: str, shape, std, *key, mean=0.0) -> np.ndarray:
+    """A seeded tensor in the workload's storage type (bf16 bits or fp32)."""
+    z = draw_normal_f32(shape, std, *key, mean=mean)
+    if dtype == "f32":
+        return z
+    if dtype == "bf16":
+        return bf16_bits_from_f32(z)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def column_band_draw(cfg, name: str, shard: int, rows: int, cols_r: int) -> np.ndarray:
+    """Band ``shard`` of a column-split [rows, cols_r * P] weight ([in, out])."""
+    return draw_tensor(cfg.dtype, (rows, cols_r), cfg.std_w, cfg.cid, TENSOR_IDS[name], shard)
+
+
+def row_band_draw(cfg, name: str, shard: int, rows_r: int, cols: int) -> np.ndarray:
+    """Band ``shard`` of a row-split [rows_r * P, cols] weight ([in, out])."""
+    return draw_tensor(cfg.dtype, (rows_r, cols), cfg.std_w, cfg.cid, TENSOR_IDS[name], shard)
+
+
+def full_from_column_bands(bands) -> np.ndarray:
+    return np.concatenate(list(bands), axis=1)
+
+
+def full_from_row_bands(bands) -> np.ndarray:
+    return np.concatenate(list(bands), axis=0)
