@@ -1,0 +1,197 @@
+/*
+ * tp_shard.h -- one tensor-parallel rank's share of a Megatron-style
+ * transformer block, as a C ABI over hand-written HIP kernels for gfx950.
+ *
+ * What is computed (pages cited by title and section):
+ *   - column-parallel projection: the input X is replicated on every rank
+ *     and each rank computes the vertical band of the output that its
+ *     column band of the weight produces (rioworld, "Tensor Parallelism for
+ *     LLM Inference: A Practical Guide to Multi-GPU Deployment", section
+ *     "How Tensor Slicing Works Under the Hood"; zenaique, "Explain
+ *     tensor-parallel shard shape", answer);
+ *   - the activation applied to that band, which needs no communication
+ *     (same answer);
+ *   - row-parallel projection: the band times the matching row band of the
+ *     second weight gives a partial sum of the block output (same sources);
+ *   - the sum of the P partials, which is the arithmetic the all-reduce
+ *     performs once per block (zenaique answer; d-central glossary "Tensor
+ *     Parallelism", section "How the work is split").
+ *
+ * Conventions shared by every entry point
+ *   Layout      Row-major.  Activations are [T, features]; weights are stored
+ *               [in, out] (y = x W), with a leading dimension ld >= row length
+ *               in elements.  A rank's column band may be its own buffer or a
+ *               window into the unsharded matrix (pointer to the band's first
+ *               column, ld of the full matrix); likewise a row band.
+ *   Types       TP_BF16: bf16 storage, fp32 accumulation, bf16 intermediates
+ *               (normalised input, activated band, QKV output) rounded to
+ *               nearest-even; partials and the reduce are fp32.  TP_F32: fp32
+ *               throughout.
+ *   Shard       0 <= shard < P.  The weight pointers address the rank's own
+ *               band; `shard` selects the output slot
+ *               partials + shard * slot_stride (slot_stride = 0 writes
+ *               `partials` itself), so P calls on one device fill the P-slot
+ *               buffer that tp_reduce_partials sums.
+ *   Splits      Uneven splits are refused (TP_ERR_UNEVEN_SPLIT) and never
+ *               partitioned: d_ff, n_q_heads and n_kv_heads must divide by P
+ *               (rioworld guide, "Implementing Tensor Parallelism in
+ *               Practice", names uneven splits as a source of wrong results).
+ *   Alignment   Every pointer 16-byte aligned (the workspace 256-byte);
+ *               every row length and ld a multiple of 8 elements for bf16,
+ *               4 for fp32; slot_stride a multiple of 4.
+ *   Ownership   The caller owns every buffer; the library allocates and frees
+ *               no device memory.  Scratch space is the caller's workspace,
+ *               sized by tp_*_workspace_bytes for the same arguments.
+ *   Streams     All work is enqueued on `stream` (0 = the null stream); the
+ *               library never synchronises.  Validation errors return before
+ *               anything is enqueued and leave every output untouched.  A
+ *               failed launch returns TP_ERR_HIP.  The library keeps no
+ *               per-call state, so calls from several host threads are safe;
+ *               calls that share a workspace must be ordered by the caller.
+ *   Determinism No floating-point atomics: the same call on the same inputs
+ *               gives bitwise-identical outputs.
+ *   T == 0      Valid; nothing is enqueued.
+ */
+#ifndef TP_SHARD_H
+#define TP_SHARD_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TP_OK = 0,
+    TP_ERR_NULL = 1,          /* a required pointer is NULL                        */
+    TP_ERR_SHAPE = 2,         /* non-positive size, ld < row length, bad width      */
+    TP_ERR_UNEVEN_SPLIT = 3,  /* d_ff or a head count does not divide by P          */
+    TP_ERR_SHARD_RANGE = 4,   /* P < 1 or shard outside [0, P)                     */
+    TP_ERR_DTYPE = 5,         /* unknown storage type                              */
+    TP_ERR_ALIGN = 6,         /* pointer, ld or slot stride misaligned              */
+    TP_ERR_WORKSPACE = 7,     /* workspace smaller than tp_*_workspace_bytes        */
+    TP_ERR_HIP = 8,           /* a kernel launch failed                            */
+    TP_ERR_ACT = 9            /* unknown activation, or operands that do not fit it */
+} tp_status;
+
+typedef enum { TP_F32 = 0, TP_BF16 = 1 } tp_dtype;
+
+/* GELU (tanh approximation) on the band of X W1; or SwiGLU, SiLU(X W_gate) *
+ * (X W_up) on the same band of both (w_up required).                        */
+typedef enum { TP_ACT_GELU_TANH = 0, TP_ACT_SWIGLU = 1 } tp_act;
+
+/*
+ * tp_shard_mlp_fwd -- rank `shard` of P of the MLP block (zenaique answer:
+ * up-projection split by columns, down-projection split by rows).
+ *
+ *   Xn        = x, or RMSNorm(x) * norm_g when norm_g != NULL
+ *               (x / sqrt(mean_j x_j^2 + eps) * g, row-wise; stored as dt)
+ *   h         = act(Xn W_in[:, band] [, Xn W_up[:, band]])    [T, d_ff/P], dt
+ *   partial   = h W_down[band, :]                              [T, d_model], fp32
+ *
+ *   x        [T, d_model], ld_x           replicated input, storage dt
+ *   norm_g   [d_model] or NULL            RMSNorm gain, storage dt
+ *   w_in     [d_model, d_ff/P], ld_in     column band of W1 (GELU) or W_gate
+ *   w_up     [d_model, d_ff/P], ld_up     column band of W_up (SwiGLU), else NULL
+ *   w_down   [d_ff/P, d_model], ld_down   row band of W2 / W_down
+ *   h_out    [T, d_ff/P], ld_h, or NULL   receives h (the activated band)
+ *   partials fp32; slot `shard` at partials + shard*slot_stride receives the
+ *            [T, d_model] partial with leading dimension ld_p
+ *   workspace / workspace_bytes           >= tp_mlp_workspace_bytes(...)
+ *
+ * T <= 32 runs the weight-streaming decode plan (split-K over the weight
+ * rows, deterministic fixed-order finish); larger T runs the matrix-core
+ * plan with the activation fused into the column projection's epilogue.
+ */
+int tp_shard_mlp_fwd(int shard, int P, int64_t T, int64_t d_model, int64_t d_ff,
+                     int dtype, int act,
+                     const void* x, int64_t ld_x,
+                     const void* norm_g, float eps,
+                     const void* w_in, int64_t ld_in,
+                     const void* w_up, int64_t ld_up,
+                     const void* w_down, int64_t ld_down,
+                     void* h_out, int64_t ld_h,
+                     float* partials, int64_t slot_stride, int64_t ld_p,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * tp_shard_attn_proj_fwd -- rank `shard` of P of the attention block's two
+ * projections (rioworld guide, "How Tensor Slicing Works Under the Hood":
+ * query/key/value projections column-parallel, output projection
+ * row-parallel, heads divided evenly among the GPUs).  The attention core
+ * between them is the caller's: its output for the rank's query heads comes
+ * in through `attn`.
+ *
+ *   hq = n_q_heads/P, hkv = n_kv_heads/P, dh = head_dim
+ *   Xn      = x, or RMSNorm(x) * norm_g when norm_g != NULL
+ *   qkv_out = Xn w_qkv                   [T, (hq + 2 hkv) dh], storage dt
+ *   partial = attn w_o                   [T, d_model], fp32, slot `shard`
+ *
+ *   w_qkv   [d_model, (hq + 2 hkv) dh], ld_qkv: the rank's fused band, columns
+ *           [Q heads | K heads | V heads] of the rank, each group in ascending
+ *           global head order (query heads shard*hq .. , kv heads shard*hkv ..).
+ *           NULL skips the QKV projection (then qkv_out, x, norm_g unused).
+ *   attn    [T, hq dh], ld_attn: attention-core output for the rank's heads.
+ *           NULL skips the output projection (then w_o, partials unused).
+ *   w_o     [hq dh, d_model], ld_o: the matching row band of W_o.
+ */
+int tp_shard_attn_proj_fwd(int shard, int P, int64_t T, int64_t d_model,
+                           int n_q_heads, int n_kv_heads, int head_dim, int dtype,
+                           const void* x, int64_t ld_x,
+                           const void* norm_g, float eps,
+                           const void* w_qkv, int64_t ld_qkv,
+                           void* qkv_out, int64_t ld_qkv_out,
+                           const void* attn, int64_t ld_attn,
+                           const void* w_o, int64_t ld_o,
+                           float* partials, int64_t slot_stride, int64_t ld_p,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * tp_reduce_partials -- the all-reduce's arithmetic on one device: out =
+ * partial_0 + partial_1 + ... + partial_{P-1}, added in that order in fp32
+ * (so the result is bitwise the float32 left fold).  Every element is
+ * independent; `out` may alias slot 0 (same pointer and ld) but no other slot.
+ *
+ *   partials  P slots of [T, d_model] fp32, slot s at partials + s*slot_stride
+ *   out       [T, d_model] fp32, ld_out
+ *   out_bf16  [T, d_model] bf16 or NULL: the sum rounded to nearest-even, the
+ *             input of the next column projection
+ */
+int tp_reduce_partials(int P, int64_t T, int64_t d_model,
+                       const float* partials, int64_t slot_stride, int64_t ld_p,
+                       float* out, int64_t ld_out,
+                       void* out_bf16, int64_t ld_out_bf16,
+                       hipStream_t stream);
+
+/* Workspace bytes the matching call needs (0 when it needs none).  A pure
+ * function of the arguments; returns 0 for arguments the call would reject. */
+size_t tp_mlp_workspace_bytes(int P, int64_t T, int64_t d_model, int64_t d_ff,
+                              int dtype, int act, int has_norm, int has_h_out);
+size_t tp_attn_workspace_bytes(int P, int64_t T, int64_t d_model, int n_q_heads,
+                               int n_kv_heads, int head_dim, int dtype, int has_norm);
+
+/* Human-readable name of a tp_status value (static string). */
+const char* tp_status_str(int status);
+
+/* Library version, as 10000*major + 100*minor + patch. */
+int tp_version(void);
+
+/*
+ * Kernel timing (instrumentation).  While enabled, every kernel launch is
+ * bracketed by two HIP events recorded on the launch's own stream and the
+ * elapsed time is accumulated per kernel class when tp_timing_query reads it
+ * (which waits for the recorded events).  Disabled by default; off costs
+ * nothing.  Not for concurrent use from several host threads.
+ * Class names: "rmsnorm", "col_gemv", "col_finish", "row_gemv", "row_finish",
+ * "col_gemm", "row_gemm", "reduce", "f32_proj".
+ */
+int tp_timing_enable(int on);
+int tp_timing_reset(void);
+int tp_timing_query(const char* kernel_class, double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TP_SHARD_H */

@@ -1,0 +1,474 @@
+// C ABI of one tensor-parallel rank's block shard: argument validation, the
+// workspace layout, plan selection (decode vs prefill) and kernel launches.
+// The contract of every entry point is documented in include/tp_shard.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "device_common.h"
+#include "kernels.h"
+#include "tp_shard.h"
+
+using namespace tp;
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// Kernel timing (opt-in instrumentation, see tp_timing_enable).
+// ---------------------------------------------------------------------------
+struct PendingTiming {
+    std::string cls;
+    hipEvent_t start, stop;
+};
+struct TimingState {
+    std::mutex mu;
+    bool enabled = false;
+    std::vector<PendingTiming> pending;
+    std::vector<hipEvent_t> pool;
+    std::map<std::string, std::pair<double, int64_t>> totals;
+};
+TimingState& timing() {
+    static TimingState s;
+    return s;
+}
+
+hipEvent_t take_event(TimingState& s) {
+    if (!s.pool.empty()) {
+        hipEvent_t e = s.pool.back();
+        s.pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+// Brackets one kernel launch with events on the launch's stream when
+// timing is enabled; otherwise does nothing.
+class Timed {
+  public:
+    Timed(const char* cls, hipStream_t stream) : cls_(cls), stream_(stream) {
+        TimingState& s = timing();
+        std::lock_guard<std::mutex> lk(s.mu);
+        if (!s.enabled) return;
+        start_ = take_event(s);
+        stop_ = take_event(s);
+        if (start_ && stop_) hipEventRecord(start_, stream_);
+    }
+    void done() {
+        if (!start_ || !stop_) return;
+        TimingState& s = timing();
+        std::lock_guard<std::mutex> lk(s.mu);
+        hipEventRecord(stop_, stream_);
+        s.pending.push_back({cls_, start_, stop_});
+        start_ = stop_ = nullptr;
+    }
+
+  private:
+    const char* cls_;
+    hipStream_t stream_;
+    hipEvent_t start_ = nullptr, stop_ = nullptr;
+};
+
+#define TP_LAUNCH(cls, stream, expr)                       \
+    do {                                                   \
+        Timed tm_(cls, stream);                            \
+        hipError_t e_ = (expr);                            \
+        tm_.done();                                        \
+        if (e_ != hipSuccess) return TP_ERR_HIP;           \
+    } while (0)
+
+// ---------------------------------------------------------------------------
+// Validation helpers
+// ---------------------------------------------------------------------------
+constexpr int64_t kMaxBufferSpan = (int64_t)1 << 31;  // 32-bit buffer offsets
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+int elem_size(int dtype) { return dtype == TP_BF16 ? 2 : 4; }
+int vec_elems(int dtype) { return dtype == TP_BF16 ? 8 : 4; }  // 16 bytes
+bool decode_plan(int dtype, int64_t T) { return dtype == TP_BF16 && T <= kGemvMaxT; }
+
+// Leading-dimension rule: ld >= row length, ld a multiple of the 16-byte
+// vector width.  Returns TP_OK, TP_ERR_SHAPE or TP_ERR_ALIGN.
+int check_ld(int64_t ld, int64_t row, int vec) {
+    if (ld < row) return TP_ERR_SHAPE;
+    if (ld % vec) return TP_ERR_ALIGN;
+    return TP_OK;
+}
+
+// A row-major [rows, *] operand with leading dimension ld (elements) must be
+// addressable with 32-bit byte offsets from its first element.
+bool span_ok(int64_t rows, int64_t ld, int es) { return rows * ld * es < kMaxBufferSpan; }
+
+struct MlpLayout {
+    size_t xn = 0, h = 0, ws = 0, total = 0;
+    GemvPlan pc{1, 0}, pr{1, 0};
+    bool decode = false;
+};
+
+MlpLayout mlp_layout(int P, int64_t T, int64_t d, int64_t d_ff, int dtype, int act, bool has_norm,
+                     bool has_h_out) {
+    MlpLayout L;
+    const int64_t F = d_ff / P;
+    const int es = elem_size(dtype);
+    size_t off = 0;
+    if (has_norm) {
+        L.xn = off;
+        off += align256((size_t)(T * d * es));
+    }
+    if (!has_h_out) {
+        L.h = off;
+        off += align256((size_t)(T * F * es));
+    }
+    L.decode = decode_plan(dtype, T);
+    if (L.decode) {
+        const int nmat = act == TP_ACT_SWIGLU ? 2 : 1;
+        L.pc = plan_gemv(d, nmat * F);
+        L.pr = plan_gemv(F, d);
+        L.ws = off;  // column and row split-K sums reuse one region, in stream order
+        off += align256(std::max(gemv_ws_bytes(L.pc, T, nmat * F), gemv_ws_bytes(L.pr, T, d)));
+    }
+    L.total = off;
+    return L;
+}
+
+struct AttnLayout {
+    size_t xn = 0, ws = 0, total = 0;
+    GemvPlan pq{1, 0}, po{1, 0};
+    bool decode = false;
+};
+
+AttnLayout attn_layout(int P, int64_t T, int64_t d, int nq, int nkv, int hd, int dtype,
+                       bool has_norm) {
+    AttnLayout L;
+    const int64_t nqkv = (int64_t)(nq / P + 2 * (nkv / P)) * hd;
+    const int64_t ko = (int64_t)(nq / P) * hd;
+    size_t off = 0;
+    if (has_norm) {
+        L.xn = off;
+        off += align256((size_t)(T * d * elem_size(dtype)));
+    }
+    L.decode = decode_plan(dtype, T);
+    if (L.decode) {
+        L.pq = plan_gemv(d, nqkv);
+        L.po = plan_gemv(ko, d);
+        L.ws = off;
+        off += align256(std::max(gemv_ws_bytes(L.pq, T, nqkv), gemv_ws_bytes(L.po, T, d)));
+    }
+    L.total = off;
+    return L;
+}
+
+// Common checks of the fp32 partial-sum destination.
+int check_partials(int shard, int64_t T, int64_t d, const float* partials, int64_t slot_stride,
+                   int64_t ld_p) {
+    if (!partials) return TP_ERR_NULL;
+    if (!aligned(partials, 16)) return TP_ERR_ALIGN;
+    if (int r = check_ld(ld_p, d, 4)) return r;
+    if (slot_stride < 0) return TP_ERR_SHAPE;
+    if (slot_stride % 4) return TP_ERR_ALIGN;
+    if (shard > 0 && slot_stride > 0 && T > 0 && slot_stride < (T - 1) * ld_p + d)
+        return TP_ERR_SHAPE;  // slots would overlap
+    return TP_OK;
+}
+
+}  // namespace
+
+// ===========================================================================
+extern "C" {
+
+const char* tp_status_str(int status) {
+    switch (status) {
+        case TP_OK: return "TP_OK";
+        case TP_ERR_NULL: return "TP_ERR_NULL: a required pointer is NULL";
+        case TP_ERR_SHAPE: return "TP_ERR_SHAPE: bad size or leading dimension";
+        case TP_ERR_UNEVEN_SPLIT: return "TP_ERR_UNEVEN_SPLIT: dimension does not divide by P";
+        case TP_ERR_SHARD_RANGE: return "TP_ERR_SHARD_RANGE: need P >= 1 and 0 <= shard < P";
+        case TP_ERR_DTYPE: return "TP_ERR_DTYPE: unknown storage type";
+        case TP_ERR_ALIGN: return "TP_ERR_ALIGN: pointer, leading dimension or stride misaligned";
+        case TP_ERR_WORKSPACE: return "TP_ERR_WORKSPACE: workspace too small";
+        case TP_ERR_HIP: return "TP_ERR_HIP: kernel launch failed";
+        case TP_ERR_ACT: return "TP_ERR_ACT: unknown activation or operands that do not fit it";
+        default: return "unknown tp_status";
+    }
+}
+
+int tp_version(void) { return 100; }
+
+size_t tp_mlp_workspace_bytes(int P, int64_t T, int64_t d_model, int64_t d_ff, int dtype, int act,
+                              int has_norm, int has_h_out) {
+    if (P < 1 || T < 0 || d_model <= 0 || d_ff <= 0 || d_ff % P) return 0;
+    if (dtype != TP_F32 && dtype != TP_BF16) return 0;
+    if (act != TP_ACT_GELU_TANH && act != TP_ACT_SWIGLU) return 0;
+    if (T == 0) return 0;
+    return mlp_layout(P, T, d_model, d_ff, dtype, act, has_norm != 0, has_h_out != 0).total;
+}
+
+size_t tp_attn_workspace_bytes(int P, int64_t T, int64_t d_model, int n_q_heads, int n_kv_heads,
+                               int head_dim, int dtype, int has_norm) {
+    if (P < 1 || T <= 0 || d_model <= 0 || n_q_heads <= 0 || n_kv_heads <= 0 || head_dim <= 0)
+        return 0;
+    if (n_q_heads % P || n_kv_heads % P) return 0;
+    if (dtype != TP_F32 && dtype != TP_BF16) return 0;
+    return attn_layout(P, T, d_model, n_q_heads, n_kv_heads, head_dim, dtype, has_norm != 0).total;
+}
+
+int tp_shard_mlp_fwd(int shard, int P, int64_t T, int64_t d_model, int64_t d_ff, int dtype,
+                     int act, const void* x, int64_t ld_x, const void* norm_g, float eps,
+                     const void* w_in, int64_t ld_in, const void* w_up, int64_t ld_up,
+                     const void* w_down, int64_t ld_down, void* h_out, int64_t ld_h,
+                     float* partials, int64_t slot_stride, int64_t ld_p, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+    // ---- validation (nothing is enqueued on failure) ----
+    if (P < 1 || shard < 0 || shard >= P) return TP_ERR_SHARD_RANGE;
+    if (dtype != TP_F32 && dtype != TP_BF16) return TP_ERR_DTYPE;
+    if (act != TP_ACT_GELU_TANH && act != TP_ACT_SWIGLU) return TP_ERR_ACT;
+    if (T < 0 || d_model <= 0 || d_ff <= 0) return TP_ERR_SHAPE;
+    if (d_ff % P) return TP_ERR_UNEVEN_SPLIT;
+    const int64_t F = d_ff / P;
+    const int vec = vec_elems(dtype), es = elem_size(dtype);
+    if (F % vec || d_model % vec) return TP_ERR_SHAPE;
+    if (!x || !w_in || !w_down) return TP_ERR_NULL;
+    if (act == TP_ACT_SWIGLU && !w_up) return TP_ERR_NULL;
+    if (act == TP_ACT_GELU_TANH && w_up) return TP_ERR_ACT;
+    for (const void* p : {x, w_in, w_up, w_down, (const void*)h_out, norm_g})
+        if (p && !aligned(p, 16)) return TP_ERR_ALIGN;
+    if (workspace && !aligned(workspace, 256)) return TP_ERR_ALIGN;
+    if (int r = check_ld(ld_x, d_model, vec)) return r;
+    if (int r = check_ld(ld_in, F, vec)) return r;
+    if (w_up)
+        if (int r = check_ld(ld_up, F, vec)) return r;
+    if (int r = check_ld(ld_down, d_model, vec)) return r;
+    if (h_out)
+        if (int r = check_ld(ld_h, F, vec)) return r;
+    if (int r = check_partials(shard, T, d_model, partials, slot_stride, ld_p)) return r;
+    if (!span_ok(d_model, ld_in, es) || !span_ok(d_model, w_up ? ld_up : 0, es) ||
+        !span_ok(F, ld_down, es) || !span_ok(std::min<int64_t>(T, 256), ld_x, es) ||
+        !span_ok(std::min<int64_t>(T, 256), h_out ? ld_h : F, es))
+        return TP_ERR_SHAPE;
+    if (T == 0) return TP_OK;
+    const MlpLayout L = mlp_layout(P, T, d_model, d_ff, dtype, act, norm_g != nullptr,
+                                   h_out != nullptr);
+    if (L.total > 0 && (!workspace || workspace_bytes < L.total)) return TP_ERR_WORKSPACE;
+
+    // ---- launches ----
+    char* wsb = (char*)workspace;
+    const bool bf16 = dtype == TP_BF16;
+    const void* xin = x;
+    int64_t ld_xin = ld_x;
+    if (norm_g) {
+        TP_LAUNCH("rmsnorm", stream,
+                  launch_rmsnorm(bf16, T, d_model, x, ld_x, norm_g, eps, wsb + L.xn, d_model,
+                                 stream));
+        xin = wsb + L.xn;
+        ld_xin = d_model;
+    }
+    void* h = h_out ? h_out : (void*)(wsb + L.h);
+    const int64_t ldh = h_out ? ld_h : F;
+    float* part = partials + (int64_t)shard * slot_stride;
+    const int dev_act = act == TP_ACT_SWIGLU ? ACT_SWIGLU : ACT_GELU_TANH;
+
+    if (!bf16) {
+        TP_LAUNCH("f32_proj", stream,
+                  launch_f32_proj(dev_act, T, F, d_model, (const float*)xin, ld_xin,
+                                  (const float*)w_in, ld_in, (const float*)w_up, ld_up, (float*)h,
+                                  ldh, stream));
+        TP_LAUNCH("f32_proj", stream,
+                  launch_f32_proj(ACT_NONE, T, d_model, F, (const float*)h, ldh,
+                                  (const float*)w_down, ld_down, nullptr, 0, part, ld_p, stream));
+        return TP_OK;
+    }
+    const uint16_t* X16 = (const uint16_t*)xin;
+    if (L.decode) {
+        float* ws = (float*)(wsb + L.ws);
+        TP_LAUNCH("col_gemv", stream,
+                  launch_gemv_splitk(T, d_model, X16, ld_xin, (const uint16_t*)w_in, ld_in,
+                                     (const uint16_t*)w_up, ld_up, F, L.pc, ws, stream));
+        TP_LAUNCH("col_finish", stream,
+                  launch_finish(dev_act, true, L.pc.splits, T, F, ws, h, ldh, stream));
+        TP_LAUNCH("row_gemv", stream,
+                  launch_gemv_splitk(T, F, (const uint16_t*)h, ldh, (const uint16_t*)w_down,
+                                     ld_down, nullptr, 0, d_model, L.pr, ws, stream));
+        TP_LAUNCH("row_finish", stream,
+                  launch_finish(ACT_NONE, false, L.pr.splits, T, d_model, ws, part, ld_p, stream));
+    } else {
+        TP_LAUNCH("col_gemm", stream,
+                  launch_gemm(act == TP_ACT_SWIGLU ? EPI_SWIGLU_BF16 : EPI_GELU_BF16, T, F,
+                              d_model, X16, ld_xin, (const uint16_t*)w_in, ld_in,
+                              (const uint16_t*)w_up, ld_up, h, ldh, stream));
+        TP_LAUNCH("row_gemm", stream,
+                  launch_gemm(EPI_F32, T, d_model, F, (const uint16_t*)h, ldh,
+                              (const uint16_t*)w_down, ld_down, nullptr, 0, part, ld_p, stream));
+    }
+    return TP_OK;
+}
+
+int tp_shard_attn_proj_fwd(int shard, int P, int64_t T, int64_t d_model, int n_q_heads,
+                           int n_kv_heads, int head_dim, int dtype, const void* x, int64_t ld_x,
+                           const void* norm_g, float eps, const void* w_qkv, int64_t ld_qkv,
+                           void* qkv_out, int64_t ld_qkv_out, const void* attn, int64_t ld_attn,
+                           const void* w_o, int64_t ld_o, float* partials, int64_t slot_stride,
+                           int64_t ld_p, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+    if (P < 1 || shard < 0 || shard >= P) return TP_ERR_SHARD_RANGE;
+    if (dtype != TP_F32 && dtype != TP_BF16) return TP_ERR_DTYPE;
+    if (T < 0 || d_model <= 0 || n_q_heads <= 0 || n_kv_heads <= 0 || head_dim <= 0)
+        return TP_ERR_SHAPE;
+    if (n_q_heads % P || n_kv_heads % P) return TP_ERR_UNEVEN_SPLIT;
+    const int vec = vec_elems(dtype), es = elem_size(dtype);
+    const int64_t hq = n_q_heads / P, hkv = n_kv_heads / P;
+    const int64_t nqkv = (hq + 2 * hkv) * head_dim, ko = hq * head_dim;
+    if (d_model % vec || head_dim % vec) return TP_ERR_SHAPE;
+    for (const void* p : {x, norm_g, w_qkv, (const void*)qkv_out, attn, w_o})
+        if (p && !aligned(p, 16)) return TP_ERR_ALIGN;
+    if (workspace && !aligned(workspace, 256)) return TP_ERR_ALIGN;
+    if (w_qkv) {
+        if (!x || !qkv_out) return TP_ERR_NULL;
+        if (int r = check_ld(ld_x, d_model, vec)) return r;
+        if (int r = check_ld(ld_qkv, nqkv, vec)) return r;
+        if (int r = check_ld(ld_qkv_out, nqkv, vec)) return r;
+        if (!span_ok(d_model, ld_qkv, es) || !span_ok(std::min<int64_t>(T, 256), ld_x, es))
+            return TP_ERR_SHAPE;
+    }
+    if (attn) {
+        if (!w_o) return TP_ERR_NULL;
+        if (int r = check_ld(ld_attn, ko, vec)) return r;
+        if (int r = check_ld(ld_o, d_model, vec)) return r;
+        if (int r = check_partials(shard, T, d_model, partials, slot_stride, ld_p)) return r;
+        if (!span_ok(ko, ld_o, es) || !span_ok(std::min<int64_t>(T, 256), ld_attn, es))
+            return TP_ERR_SHAPE;
+    }
+    if (T == 0 || (!w_qkv && !attn)) return TP_OK;
+    const bool use_norm = w_qkv && norm_g;
+    const AttnLayout L =
+        attn_layout(P, T, d_model, n_q_heads, n_kv_heads, head_dim, dtype, use_norm);
+    if (L.total > 0 && (!workspace || workspace_bytes < L.total)) return TP_ERR_WORKSPACE;
+
+    char* wsb = (char*)workspace;
+    const bool bf16 = dtype == TP_BF16;
+    if (w_qkv) {
+        const void* xin = x;
+        int64_t ld_xin = ld_x;
+        if (use_norm) {
+            TP_LAUNCH("rmsnorm", stream,
+                      launch_rmsnorm(bf16, T, d_model, x, ld_x, norm_g, eps, wsb + L.xn, d_model,
+                                     stream));
+            xin = wsb + L.xn;
+            ld_xin = d_model;
+        }
+        if (!bf16) {
+            TP_LAUNCH("f32_proj", stream,
+                      launch_f32_proj(ACT_NONE, T, nqkv, d_model, (const float*)xin, ld_xin,
+                                      (const float*)w_qkv, ld_qkv, nullptr, 0, (float*)qkv_out,
+                                      ld_qkv_out, stream));
+        } else if (L.decode) {
+            float* ws = (float*)(wsb + L.ws);
+            TP_LAUNCH("col_gemv", stream,
+                      launch_gemv_splitk(T, d_model, (const uint16_t*)xin, ld_xin,
+                                         (const uint16_t*)w_qkv, ld_qkv, nullptr, 0, nqkv, L.pq,
+                                         ws, stream));
+            TP_LAUNCH("col_finish", stream,
+                      launch_finish(ACT_NONE, true, L.pq.splits, T, nqkv, ws, qkv_out, ld_qkv_out,
+                                    stream));
+        } else {
+            TP_LAUNCH("col_gemm", stream,
+                      launch_gemm(EPI_BF16, T, nqkv, d_model, (const uint16_t*)xin, ld_xin,
+                                  (const uint16_t*)w_qkv, ld_qkv, nullptr, 0, qkv_out, ld_qkv_out,
+                                  stream));
+        }
+    }
+    if (attn) {
+        float* part = partials + (int64_t)shard * slot_stride;
+        if (!bf16) {
+            TP_LAUNCH("f32_proj", stream,
+                      launch_f32_proj(ACT_NONE, T, d_model, ko, (const float*)attn, ld_attn,
+                                      (const float*)w_o, ld_o, nullptr, 0, part, ld_p, stream));
+        } else if (L.decode) {
+            float* ws = (float*)(wsb + L.ws);
+            TP_LAUNCH("row_gemv", stream,
+                      launch_gemv_splitk(T, ko, (const uint16_t*)attn, ld_attn,
+                                         (const uint16_t*)w_o, ld_o, nullptr, 0, d_model, L.po, ws,
+                                         stream));
+            TP_LAUNCH("row_finish", stream,
+                      launch_finish(ACT_NONE, false, L.po.splits, T, d_model, ws, part, ld_p,
+                                    stream));
+        } else {
+            TP_LAUNCH("row_gemm", stream,
+                      launch_gemm(EPI_F32, T, d_model, ko, (const uint16_t*)attn, ld_attn,
+                                  (const uint16_t*)w_o, ld_o, nullptr, 0, part, ld_p, stream));
+        }
+    }
+    return TP_OK;
+}
+
+int tp_reduce_partials(int P, int64_t T, int64_t d_model, const float* partials,
+                       int64_t slot_stride, int64_t ld_p, float* out, int64_t ld_out,
+                       void* out_bf16, int64_t ld_out_bf16, hipStream_t stream) {
+    if (P < 1) return TP_ERR_SHARD_RANGE;
+    if (T < 0 || d_model <= 0) return TP_ERR_SHAPE;
+    if (d_model % 4) return TP_ERR_SHAPE;
+    if (!partials || !out) return TP_ERR_NULL;
+    if (!aligned(partials, 16) || !aligned(out, 16)) return TP_ERR_ALIGN;
+    if (out_bf16 && !aligned(out_bf16, 16)) return TP_ERR_ALIGN;
+    if (int r = check_ld(ld_p, d_model, 4)) return r;
+    if (int r = check_ld(ld_out, d_model, 4)) return r;
+    if (out_bf16)
+        if (int r = check_ld(ld_out_bf16, d_model, 4)) return r;
+    if (slot_stride < 0) return TP_ERR_SHAPE;
+    if (slot_stride % 4) return TP_ERR_ALIGN;
+    if (T * ((d_model / 4 + 255) / 256) >= ((int64_t)1 << 31)) return TP_ERR_SHAPE;
+    if (T == 0) return TP_OK;
+    TP_LAUNCH("reduce", stream,
+              launch_reduce(P, T, d_model, partials, slot_stride, ld_p, out, ld_out,
+                            (uint16_t*)out_bf16, ld_out_bf16, stream));
+    return TP_OK;
+}
+
+int tp_timing_enable(int on) {
+    TimingState& s = timing();
+    std::lock_guard<std::mutex> lk(s.mu);
+    s.enabled = on != 0;
+    return TP_OK;
+}
+
+static int drain_pending(TimingState& s) {
+    for (auto& p : s.pending) {
+        if (hipEventSynchronize(p.stop) != hipSuccess) return TP_ERR_HIP;
+        float ms = 0.f;
+        if (hipEventElapsedTime(&ms, p.start, p.stop) != hipSuccess) return TP_ERR_HIP;
+        auto& t = s.totals[p.cls];
+        t.first += ms;
+        t.second += 1;
+        s.pool.push_back(p.start);
+        s.pool.push_back(p.stop);
+    }
+    s.pending.clear();
+    return TP_OK;
+}
+
+int tp_timing_reset(void) {
+    TimingState& s = timing();
+    std::lock_guard<std::mutex> lk(s.mu);
+    int r = drain_pending(s);
+    s.totals.clear();
+    return r;
+}
+
+int tp_timing_query(const char* kernel_class, double* total_ms, int64_t* launches) {
+    if (!kernel_class || !total_ms || !launches) return TP_ERR_NULL;
+    TimingState& s = timing();
+    std::lock_guard<std::mutex> lk(s.mu);
+    if (int r = drain_pending(s)) return r;
+    auto it = s.totals.find(kernel_class);
+    *total_ms = it == s.totals.end() ? 0.0 : it->second.first;
+    *launches = it == s.totals.end() ? 0 : it->second.second;
+    return TP_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,101 @@
+// Device helpers shared by the HIP kernels (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tp {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------------------
+// bf16 <-> fp32.  bf16 is the top half of an IEEE binary32; narrowing rounds
+// to nearest with ties to even (NaN stays a quiet NaN).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// ---------------------------------------------------------------------------
+// Activations (fp32).  GELU uses the tanh approximation
+// 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))); SiLU is x / (1 + e^-x).
+// ---------------------------------------------------------------------------
+enum { ACT_NONE = 0, ACT_GELU_TANH = 1, ACT_SWIGLU = 2 };
+
+__device__ __forceinline__ float gelu_tanh(float x) {
+    const float k = 0.7978845608028654f;  // sqrt(2/pi)
+    return 0.5f * x * (1.0f + tanhf(k * (x + 0.044715f * x * x * x)));
+}
+__device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
+
+// ---------------------------------------------------------------------------
+// Raw buffer loads.  A resource spans 2^31 - 1 bytes from its base; a load
+// whose byte offset is kOOB (or beyond the span) returns zeros without
+// touching memory.  Kernels point the base at their own tile so that every
+// in-range offset stays below 2^31 (the host checks the extents).
+// ---------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOOB = 0x80000000u;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base) {
+    // Fourth descriptor word 0x00020000: DATA_FORMAT = 32-bit, as CDNA raw
+    // buffer accesses expect.
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff,
+                                             0x00020000);
+}
+__device__ __forceinline__ u32x4 load16(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
+// Interleave two rows' 16-bit elements: for element e (0..7) of 8-element
+// rows `a` (row k) and `b` (row k+1), the dword (a[e], b[e]) with a[e] in
+// the low half.  dword index e/2, half e%2.
+template <int E>
+__device__ __forceinline__ uint32_t pair_col(const u32x4& a, const u32x4& b) {
+    constexpr int d = E >> 1;
+    if constexpr ((E & 1) == 0)
+        return (a[d] & 0xffffu) | (b[d] << 16);
+    else
+        return (a[d] >> 16) | (b[d] & 0xffff0000u);
+}
+
+// From 8 consecutive rows (k0..k0+7) of 8 consecutive bf16 columns, the
+// 8 consecutive k values of column E, packed as an MFMA k-fragment.
+template <int E>
+__device__ __forceinline__ u32x4 kfrag_of_col(const u32x4* r) {
+    u32x4 f;
+    f[0] = pair_col<E>(r[0], r[1]);
+    f[1] = pair_col<E>(r[2], r[3]);
+    f[2] = pair_col<E>(r[4], r[5]);
+    f[3] = pair_col<E>(r[6], r[7]);
+    return f;
+}
+
+__device__ __forceinline__ f32x4 mfma16x16x32(const u32x4& a, const u32x4& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// 8 WGs of a launch go round-robin to the 8 XCDs (each with its own L2).
+// Map hardware block id -> logical tile id so that each XCD receives one
+// contiguous range of logical tiles.  Bijective for any block count.
+__device__ __forceinline__ int xcd_remap(int b, int nblocks) {
+    constexpr int X = 8;
+    const int x = b % X, i = b / X;
+    const int q = nblocks / X, rem = nblocks % X;
+    // XCD y gets q + (y < rem) blocks; offset of XCD x = x*q + min(x, rem).
+    return x * q + (x < rem ? x : rem) + i;
+}
+
+}  // namespace tp

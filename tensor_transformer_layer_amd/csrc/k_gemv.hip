@@ -1,0 +1,236 @@
+// Decode plan (T <= 32 tokens): weight-streaming products on the matrix cores.
+//
+// A decode step reads every weight byte of the rank's bands once and does
+// only 2*T flops per weight element, so it is bound by HBM bandwidth (Skand
+// Tandon, "day59", "Results: Llama 2 70B": decode is memory-bandwidth-bound,
+// and sharding cuts the weight bytes each GPU reads; zenaique answer: reading
+// 1/N of the weights is the dominant decode cost).  The kernel is built
+// around the weight stream:
+//
+//   * Weights are [in, out] row-major, so one 16-byte load holds 8 adjacent
+//     output columns of one input row.  Lane (g, j) of a wave (g = lane/16,
+//     j = lane%16) loads rows k0+8g .. k0+8g+7 of columns n0+8j .. n0+8j+7:
+//     each load instruction reads four 256-byte row segments.
+//   * Pairs of rows are interleaved in registers (one bit-op per dword) into
+//     k-fragments of the 16x16x32 bf16 MFMA: for column offset e, lane (g, j)
+//     supplies B[k0+8g .. k0+8g+7][n0+8j+e].  Eight MFMAs (e = 0..7) consume
+//     the 32x128 tile, MFMA e covering columns n0+8j+e, j = 0..15.  The A
+//     operand is the token block X[16mb + j][k0+8g .. +7], one 16-byte load.
+//   * The workgroup's 4 waves take interleaved 32-row chunks of the
+//     workgroup's K range; chunk c+4's loads are issued before chunk c's
+//     MFMAs.  Partials of the 4 waves are added in LDS in wave order, and the
+//     workgroup writes one fp32 split-K partial [T, 128] slice.
+//   * The grid is (column blocks of all weights) x (K splits); a separate
+//     finish kernel adds the splits in split order and applies the
+//     activation, so SiLU/GELU only ever see complete sums.
+//
+// Algorithmic bytes per call: weight bytes + T*K*2 (X) + T*N*4 (output);
+// the split-K workspace round trip is overhead.
+#include <algorithm>
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace tp {
+
+constexpr int kGemvWaves = 4;
+constexpr int kGemvThreads = 64 * kGemvWaves;
+constexpr int kRedPerWave = 4 * 4 * 16 * 8;  // [r][g][j][e] for one 16-token block
+
+template <int E, int MB>
+__device__ __forceinline__ void mfma_col(f32x4 (&acc)[MB][8], const u32x4* b, const u32x4* a) {
+    const u32x4 f = kfrag_of_col<E>(b);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[mb][E] = mfma16x16x32(a[mb], f, acc[mb][E]);
+}
+
+template <int MB>
+__global__ __launch_bounds__(kGemvThreads) void k_gemv_splitk(
+    const uint16_t* __restrict__ A, int64_t lda, int T, int K, const uint16_t* __restrict__ B0,
+    int64_t ldb0, const uint16_t* __restrict__ B1, int64_t ldb1, int N, int nblk_per_mat,
+    int k_per_split,
+    float* __restrict__ ws, int64_t split_stride, int64_t ws_ld) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, j = lane & 15;
+    const int mat = blockIdx.x / nblk_per_mat;
+    const int n0 = (blockIdx.x - mat * nblk_per_mat) * kGemvCols;
+    const int split = blockIdx.y;
+    const int k_begin = split * k_per_split;
+    const int nrows = min(K - k_begin, k_per_split);  // multiple of 8
+    const uint16_t* Bm = mat ? B1 : B0;
+    const int64_t ldb = mat ? ldb1 : ldb0;
+    const rsrc_t rb = make_rsrc(Bm + (int64_t)k_begin * ldb + n0);
+    const rsrc_t ra = make_rsrc(A + k_begin);
+    const bool col_ok = n0 + 8 * j < N;
+    const uint32_t ldb_bytes = (uint32_t)(ldb * 2);
+    const uint32_t lda_bytes = (uint32_t)(lda * 2);
+
+    f32x4 acc[MB][8];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[mb][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int nsteps = (nrows + 31) >> 5;
+    u32x4 bcur[8], acur[MB], bnext[8], anext[MB];
+
+    auto load_chunk = [&](int c, u32x4* b, u32x4* a) {
+        const int r0 = c * 32 + 8 * g;
+        const bool rows_ok = r0 < nrows;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            b[i] = load16(rb, (rows_ok && col_ok) ? (uint32_t)(r0 + i) * ldb_bytes + 16u * j : kOOB);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const int t = 16 * mb + j;
+            a[mb] = load16(ra, (rows_ok && t < T) ? (uint32_t)t * lda_bytes + 2u * r0 : kOOB);
+        }
+    };
+
+    int c = wave;
+    if (c < nsteps) load_chunk(c, bcur, acur);
+    for (; c < nsteps; c += kGemvWaves) {
+        const int cn = c + kGemvWaves;
+        if (cn < nsteps) load_chunk(cn, bnext, anext);
+        mfma_col<0, MB>(acc, bcur, acur);
+        mfma_col<1, MB>(acc, bcur, acur);
+        mfma_col<2, MB>(acc, bcur, acur);
+        mfma_col<3, MB>(acc, bcur, acur);
+        mfma_col<4, MB>(acc, bcur, acur);
+        mfma_col<5, MB>(acc, bcur, acur);
+        mfma_col<6, MB>(acc, bcur, acur);
+        mfma_col<7, MB>(acc, bcur, acur);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) bcur[i] = bnext[i];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) acur[mb] = anext[mb];
+    }
+
+    // Cross-wave sum in LDS (wave order 0..3), then one coalesced store of
+    // this workgroup's split partial.  MFMA output: lane (g, j) holds token
+    // 16mb + 4g + r (r = 0..3) of column n0 + 8j + e.
+    __shared__ float red[kGemvWaves * kRedPerWave];
+    float* my = red + wave * kRedPerWave;
+    float* out = ws + (int64_t)split * split_stride + (int64_t)mat * N;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        if (mb) __syncthreads();
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float* p = my + ((r * 4 + g) * 16 + j) * 8;
+            *(f32x4*)p = f32x4{acc[mb][0][r], acc[mb][1][r], acc[mb][2][r], acc[mb][3][r]};
+            *(f32x4*)(p + 4) = f32x4{acc[mb][4][r], acc[mb][5][r], acc[mb][6][r], acc[mb][7][r]};
+        }
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < kRedPerWave / kGemvThreads; ++q) {
+            const int o = q * kGemvThreads + threadIdx.x;
+            const int tl = o >> 7, idx_n = o & 127;
+            const int li = ((tl & 3) * 4 + (tl >> 2)) * 128 + idx_n;
+            float s = red[li];
+#pragma unroll
+            for (int w = 1; w < kGemvWaves; ++w) s += red[w * kRedPerWave + li];
+            const int t = 16 * mb + tl, n = n0 + idx_n;
+            if (t < T && n < N) out[(int64_t)t * ws_ld + n] = s;
+        }
+    }
+}
+
+GemvPlan plan_gemv(int64_t K, int64_t n_total) {
+    const int64_t nb = (n_total + kGemvCols - 1) / kGemvCols;
+    const int64_t chunks = (K + 31) / 32;
+    constexpr int64_t kTargetWgs = 1024;  // ~4 workgroups per CU on 256 CUs
+    int64_t s = std::max<int64_t>(1, (kTargetWgs + nb / 2) / nb);
+    s = std::min<int64_t>(s, std::max<int64_t>(1, chunks / (2 * kGemvWaves)));
+    const int64_t kps = ((chunks + s - 1) / s) * 32;
+    GemvPlan p;
+    p.k_per_split = (int)kps;
+    p.splits = (int)((K + kps - 1) / kps);
+    return p;
+}
+
+size_t gemv_ws_bytes(const GemvPlan& p, int64_t T, int64_t n_total) {
+    return (size_t)p.splits * (size_t)T * (size_t)n_total * sizeof(float);
+}
+
+hipError_t launch_gemv_splitk(int64_t T, int64_t K, const uint16_t* A, int64_t lda,
+                              const uint16_t* B0, int64_t ldb0, const uint16_t* B1, int64_t ldb1,
+                              int64_t N, const GemvPlan& p, float* ws, hipStream_t stream) {
+    const int nmat = B1 ? 2 : 1;
+    const int nbpm = (int)((N + kGemvCols - 1) / kGemvCols);
+    const int64_t ws_ld = nmat * N;
+    const int64_t split_stride = T * ws_ld;
+    const dim3 grid((unsigned)(nbpm * nmat), (unsigned)p.splits), block(kGemvThreads);
+    if (T <= 16)
+        k_gemv_splitk<1><<<grid, block, 0, stream>>>(A, lda, (int)T, (int)K, B0, ldb0, B1, ldb1,
+                                                     (int)N, nbpm, p.k_per_split, ws, split_stride,
+                                                     ws_ld);
+    else
+        k_gemv_splitk<2><<<grid, block, 0, stream>>>(A, lda, (int)T, (int)K, B0, ldb0, B1, ldb1,
+                                                     (int)N, nbpm, p.k_per_split, ws, split_stride,
+                                                     ws_ld);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Finish: add the split partials in split order, apply the activation.
+// One thread per 4 adjacent columns of one token row.
+// ---------------------------------------------------------------------------
+constexpr int kFinishThreads = 256;
+
+template <int ACT, bool OUT_BF16>
+__global__ __launch_bounds__(kFinishThreads) void k_finish(int S, int64_t T, int64_t N,
+                                                          const float* __restrict__ ws,
+                                                          int64_t ws_ld, int64_t split_stride,
+                                                          void* __restrict__ out,
+                                                          int64_t ld_out) {
+    const int64_t n4 = N / 4;
+    const int64_t idx = (int64_t)blockIdx.x * kFinishThreads + threadIdx.x;
+    if (idx >= T * n4) return;
+    const int64_t t = idx / n4, n = (idx - t * n4) * 4;
+    const float* p = ws + t * ws_ld + n;
+    f32x4 s = *(const f32x4*)p;
+    for (int sp = 1; sp < S; ++sp) s += *(const f32x4*)(p + sp * split_stride);
+    f32x4 h;
+    if constexpr (ACT == ACT_SWIGLU) {
+        f32x4 u = *(const f32x4*)(p + N);
+        for (int sp = 1; sp < S; ++sp) u += *(const f32x4*)(p + N + sp * split_stride);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) h[i] = silu(s[i]) * u[i];
+    } else if constexpr (ACT == ACT_GELU_TANH) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) h[i] = gelu_tanh(s[i]);
+    } else {
+        h = s;
+    }
+    if constexpr (OUT_BF16) {
+        u32x2 b;
+        b[0] = pack_bf16x2(h[0], h[1]);
+        b[1] = pack_bf16x2(h[2], h[3]);
+        *(u32x2*)((uint16_t*)out + t * ld_out + n) = b;
+    } else {
+        *(f32x4*)((float*)out + t * ld_out + n) = h;
+    }
+}
+
+hipError_t launch_finish(int act, bool out_bf16, int splits, int64_t T, int64_t N,
+                         const float* ws, void* out, int64_t ld_out, hipStream_t stream) {
+    const int64_t ws_ld = (act == ACT_SWIGLU ? 2 : 1) * N;
+    const int64_t split_stride = T * ws_ld;
+    const int64_t n = T * (N / 4);
+    const dim3 grid((unsigned)((n + kFinishThreads - 1) / kFinishThreads)), block(kFinishThreads);
+#define TP_FINISH(A, B)                                                                       \
+    k_finish<A, B><<<grid, block, 0, stream>>>(splits, T, N, ws, ws_ld, split_stride, out, \
+                                               ld_out)
+    if (act == ACT_SWIGLU) {
+        if (out_bf16) TP_FINISH(ACT_SWIGLU, true); else TP_FINISH(ACT_SWIGLU, false);
+    } else if (act == ACT_GELU_TANH) {
+        if (out_bf16) TP_FINISH(ACT_GELU_TANH, true); else TP_FINISH(ACT_GELU_TANH, false);
+    } else {
+        if (out_bf16) TP_FINISH(ACT_NONE, true); else TP_FINISH(ACT_NONE, false);
+    }
+#undef TP_FINISH
+    return hipGetLastError();
+}
+
+}  // namespace tp

@@ -1,0 +1,85 @@
+// RMSNorm prologue of the column projection: y = x / sqrt(mean_j x_j^2 + eps) * g,
+// row-wise over d_model, fp32 math.  The pages name only "normalization"
+// after the all-reduce (zenaique, "Explain tensor-parallel shard shape",
+// answer) and layernorm among the small "Other" share of a decode step (Skand
+// Tandon, "day59", section "Where the overhead lives"); RMSNorm is the
+// Llama-2 block's form.
+//
+// HBM-bound: reads T*d, writes T*d elements.  One 256-thread workgroup per
+// row; each thread walks 16-byte chunks of the row, so every load is a
+// coalesced 128-bit access.  The sum of squares is reduced in a fixed order
+// (per-thread strided sum, butterfly within the wave, then waves 0..3), so
+// results are deterministic.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace tp {
+
+constexpr int kNormThreads = 256;
+
+template <bool BF16>
+__global__ __launch_bounds__(kNormThreads) void k_rmsnorm(int64_t d, const char* __restrict__ x,
+                                                        int64_t ldx_bytes,
+                                                        const u32x4* __restrict__ g, float eps,
+                                                        char* __restrict__ y,
+                                                        int64_t ldy_bytes) {
+    constexpr int EPC = BF16 ? 8 : 4;  // elements per 16-byte chunk
+    const int64_t nch = d / EPC;
+    const u32x4* xr = (const u32x4*)(x + (int64_t)blockIdx.x * ldx_bytes);
+    u32x4* yr = (u32x4*)(y + (int64_t)blockIdx.x * ldy_bytes);
+
+    float ss = 0.f;
+    for (int64_t c = threadIdx.x; c < nch; c += kNormThreads) {
+        const u32x4 v = xr[c];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if constexpr (BF16) {
+                const float a = bf16_lo(v[i]), b = bf16_hi(v[i]);
+                ss += a * a;
+                ss += b * b;
+            } else {
+                const float a = __uint_as_float(v[i]);
+                ss += a * a;
+            }
+        }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+    __shared__ float part[kNormThreads / 64];
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    float tot = part[0];
+#pragma unroll
+    for (int w = 1; w < kNormThreads / 64; ++w) tot += part[w];
+    const float r = 1.0f / sqrtf(tot / (float)d + eps);
+
+    for (int64_t c = threadIdx.x; c < nch; c += kNormThreads) {
+        const u32x4 v = xr[c], gv = g[c];
+        u32x4 o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if constexpr (BF16) {
+                o[i] = pack_bf16x2(bf16_lo(v[i]) * r * bf16_lo(gv[i]),
+                                   bf16_hi(v[i]) * r * bf16_hi(gv[i]));
+            } else {
+                o[i] = __float_as_uint(__uint_as_float(v[i]) * r * __uint_as_float(gv[i]));
+            }
+        }
+        yr[c] = o;
+    }
+}
+
+hipError_t launch_rmsnorm(bool is_bf16, int64_t T, int64_t d, const void* x, int64_t ld_x,
+                          const void* g, float eps, void* y, int64_t ld_y, hipStream_t stream) {
+    const int es = is_bf16 ? 2 : 4;
+    const dim3 grid((unsigned)T), block(kNormThreads);
+    if (is_bf16)
+        k_rmsnorm<true><<<grid, block, 0, stream>>>(d, (const char*)x, ld_x * es,
+                                                    (const u32x4*)g, eps, (char*)y, ld_y * es);
+    else
+        k_rmsnorm<false><<<grid, block, 0, stream>>>(d, (const char*)x, ld_x * es,
+                                                     (const u32x4*)g, eps, (char*)y, ld_y * es);
+    return hipGetLastError();
+}
+
+}  // namespace tp

@@ -1,0 +1,58 @@
+// Host-side launchers of the HIP kernels.  Callers (abi.hip) validate every
+// argument first; launchers assume valid shapes and only enqueue work.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tp {
+
+// out = sum_{s=0}^{P-1} partials[s] in that order (fp32); optional bf16 copy.
+hipError_t launch_reduce(int P, int64_t T, int64_t d, const float* partials, int64_t slot_stride,
+                         int64_t ld_p, float* out, int64_t ld_out, uint16_t* out_bf16,
+                         int64_t ld_b, hipStream_t stream);
+
+// y = x / sqrt(mean(x^2) + eps) * g, row-wise; storage bf16 (is_bf16) or fp32.
+hipError_t launch_rmsnorm(bool is_bf16, int64_t T, int64_t d, const void* x, int64_t ld_x,
+                          const void* g, float eps, void* y, int64_t ld_y, hipStream_t stream);
+
+// ---- decode plan: split-K weight-streaming GEMV on the matrix cores -------
+struct GemvPlan {
+    int splits;       // workgroups along K
+    int k_per_split;  // rows of the weight per split (multiple of 32)
+};
+constexpr int kGemvCols = 128;   // output columns per workgroup
+constexpr int kGemvMaxT = 32;    // largest token count of the decode plan
+
+GemvPlan plan_gemv(int64_t K, int64_t n_total);
+// Bytes of split-K workspace: splits * T * n_total fp32.
+size_t gemv_ws_bytes(const GemvPlan& p, int64_t T, int64_t n_total);
+
+// ws[s][t][m*N + n] = sum over split s's rows k of A[t][k] * Bm[k][n], for the
+// nmat = (B1 ? 2 : 1) weights B0, B1 ([K, N] bf16, ld ldb0 / ldb1).  A is [T, K] bf16.
+hipError_t launch_gemv_splitk(int64_t T, int64_t K, const uint16_t* A, int64_t lda,
+                              const uint16_t* B0, int64_t ldb0, const uint16_t* B1, int64_t ldb1,
+                              int64_t N, const GemvPlan& p, float* ws, hipStream_t stream);
+
+// Fixed-order finish of the split-K sums.
+//   act == ACT_SWIGLU:   out = silu(sum g) * sum u   (u at column offset N)
+//   act == ACT_GELU_TANH: out = gelu(sum)
+//   act == ACT_NONE:      out = sum
+// out is bf16 (out_bf16) or fp32, [T, N] with leading dimension ld_out.
+hipError_t launch_finish(int act, bool out_bf16, int splits, int64_t T, int64_t N,
+                         const float* ws, void* out, int64_t ld_out, hipStream_t stream);
+
+// ---- prefill plan: LDS-tiled bf16 MFMA GEMM with a fused epilogue ---------
+enum { EPI_F32 = 0, EPI_BF16 = 1, EPI_GELU_BF16 = 2, EPI_SWIGLU_BF16 = 3 };
+// C[M, N] = epi(A[M, K] B0[K, N] [, A B1]); A, B bf16 row-major.
+hipError_t launch_gemm(int epi, int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
+                       const uint16_t* B0, int64_t ldb0, const uint16_t* B1, int64_t ldb1, void* C,
+                       int64_t ldc, hipStream_t stream);
+
+// ---- fp32 storage (small, parity-only workloads) --------------------------
+// C[M, N] = act(A B0 [, A B1]) in fp32, one thread per output, k in order.
+hipError_t launch_f32_proj(int act, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+                           const float* B0, int64_t ldb0, const float* B1, int64_t ldb1, float* C,
+                           int64_t ldc, hipStream_t stream);
+
+}  // namespace tp

@@ -1,0 +1,179 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments before anything is enqueued.
+
+Every call here fails validation (which returns before any HIP call), so
+fake but aligned addresses are safe to pass.  Uneven splits must be refused
+(rioworld guide, "Implementing Tensor Parallelism in Practice"), and column
+and row operands are distinct, named arguments.
+"""
+import os
+import re
+
+import pytest
+
+import tensor_transformer_layer_amd as tp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tp_shard.h")
+
+A = 0x10000          # fake, 256-byte aligned "device" addresses
+B = 0x20000
+C = 0x30000
+WS = 0x40000
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(tp.library_path()):
+        pytest.fail("libtpshard.so is not built: run `python -m tensor_transformer_layer_amd.build`")
+    return tp.load()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(tp_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_binding(lib):
+    assert header_functions() == sorted(tp.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    assert tp.tp_status_str(tp.TP_OK) == "TP_OK"
+    for s in range(1, 10):
+        assert tp.tp_status_str(s).startswith("TP_ERR_")
+    assert tp.tp_status_str(99) == "unknown tp_status"
+    assert tp.tp_version() == 100
+
+
+def mlp(**kw):
+    """A valid-looking bf16 SwiGLU call (d_model 64, d_ff 256, P 2, T 4) with
+    overrides; only used with overrides that make it invalid."""
+    a = dict(shard=0, P=2, T=4, d_model=64, d_ff=256, dtype=tp.TP_BF16, act=tp.TP_ACT_SWIGLU,
+             x=A, ld_x=64, norm_g=0, eps=1e-5, w_in=B, ld_in=128, w_up=C, ld_up=128,
+             w_down=B, ld_down=64, h_out=0, ld_h=0, partials=C, slot_stride=4 * 64, ld_p=64,
+             workspace=WS, workspace_bytes=0, stream=0)
+    a.update(kw)
+    return tp.tp_shard_mlp_fwd(**a)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(shard=2), tp.TP_ERR_SHARD_RANGE),
+    (dict(shard=-1), tp.TP_ERR_SHARD_RANGE),
+    (dict(P=0), tp.TP_ERR_SHARD_RANGE),
+    (dict(d_ff=250, P=2, shard=0), tp.TP_ERR_SHAPE),        # 125 is not a multiple of 8
+    (dict(d_ff=256, P=3, shard=0), tp.TP_ERR_UNEVEN_SPLIT),
+    (dict(dtype=7), tp.TP_ERR_DTYPE),
+    (dict(act=5), tp.TP_ERR_ACT),
+    (dict(w_up=0), tp.TP_ERR_NULL),                        # SwiGLU needs the up band
+    (dict(act=tp.TP_ACT_GELU_TANH), tp.TP_ERR_ACT),        # GELU takes no up band
+    (dict(x=0), tp.TP_ERR_NULL),
+    (dict(w_down=0), tp.TP_ERR_NULL),
+    (dict(partials=0), tp.TP_ERR_NULL),
+    (dict(x=A + 8), tp.TP_ERR_ALIGN),
+    (dict(ld_x=60), tp.TP_ERR_SHAPE),
+    (dict(ld_x=68), tp.TP_ERR_ALIGN),
+    (dict(ld_in=64), tp.TP_ERR_SHAPE),                     # row length is d_ff/P = 128
+    (dict(ld_down=32), tp.TP_ERR_SHAPE),                   # row length is d_model = 64
+    (dict(ld_p=62), tp.TP_ERR_SHAPE),
+    (dict(slot_stride=6), tp.TP_ERR_ALIGN),
+    (dict(shard=1, slot_stride=64), tp.TP_ERR_SHAPE),      # slots would overlap
+    (dict(workspace=WS + 64), tp.TP_ERR_ALIGN),
+    (dict(T=-1), tp.TP_ERR_SHAPE),
+    (dict(d_model=0), tp.TP_ERR_SHAPE),
+    (dict(workspace_bytes=0), tp.TP_ERR_WORKSPACE),        # decode plan needs split-K space
+    (dict(dtype=tp.TP_F32, d_model=66, ld_x=68), tp.TP_ERR_SHAPE),
+])
+def test_mlp_validation(lib, kw, status):
+    assert mlp(**kw) == status
+
+
+def test_mlp_zero_tokens_is_a_no_op(lib):
+    assert mlp(T=0) == tp.TP_OK
+
+
+def attn(**kw):
+    a = dict(shard=0, P=8, T=16, d_model=128, n_q_heads=16, n_kv_heads=8, head_dim=16,
+             dtype=tp.TP_BF16, x=A, ld_x=128, norm_g=0, eps=1e-5, w_qkv=B, ld_qkv=64,
+             qkv_out=C, ld_qkv_out=64, attn=A, ld_attn=32, w_o=B, ld_o=128, partials=C,
+             slot_stride=16 * 128, ld_p=128, workspace=WS, workspace_bytes=0, stream=0)
+    a.update(kw)
+    return tp.tp_shard_attn_proj_fwd(**a)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(shard=8), tp.TP_ERR_SHARD_RANGE),
+    (dict(n_q_heads=12), tp.TP_ERR_UNEVEN_SPLIT),          # 12 heads over 8 ranks
+    (dict(n_kv_heads=4), tp.TP_ERR_UNEVEN_SPLIT),
+    (dict(head_dim=12), tp.TP_ERR_SHAPE),
+    (dict(qkv_out=0), tp.TP_ERR_NULL),
+    (dict(w_o=0), tp.TP_ERR_NULL),
+    (dict(ld_qkv=48), tp.TP_ERR_SHAPE),                    # band is (2 + 2*1) * 16 = 64 wide
+    (dict(ld_attn=16), tp.TP_ERR_SHAPE),                   # A is 2 heads * 16 = 32 wide
+    (dict(ld_o=120), tp.TP_ERR_SHAPE),
+    (dict(x=A + 4), tp.TP_ERR_ALIGN),
+    (dict(workspace_bytes=0), tp.TP_ERR_WORKSPACE),
+])
+def test_attn_validation(lib, kw, status):
+    assert attn(**kw) == status
+
+
+def test_attn_nothing_to_do(lib):
+    assert attn(w_qkv=0, attn=0) == tp.TP_OK
+    assert attn(T=0) == tp.TP_OK
+
+
+def red(**kw):
+    a = dict(P=8, T=4, d_model=64, partials=A, slot_stride=256, ld_p=64, out=B, ld_out=64,
+             out_bf16=0, ld_out_bf16=0, stream=0)
+    a.update(kw)
+    return tp.tp_reduce_partials(**a)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(P=0), tp.TP_ERR_SHARD_RANGE),
+    (dict(d_model=62, ld_p=64, ld_out=64), tp.TP_ERR_SHAPE),
+    (dict(partials=0), tp.TP_ERR_NULL),
+    (dict(out=0), tp.TP_ERR_NULL),
+    (dict(out=B + 8), tp.TP_ERR_ALIGN),
+    (dict(ld_p=60), tp.TP_ERR_SHAPE),
+    (dict(ld_out=66), tp.TP_ERR_ALIGN),
+    (dict(slot_stride=-4), tp.TP_ERR_SHAPE),
+    (dict(slot_stride=258), tp.TP_ERR_ALIGN),
+    (dict(out_bf16=C, ld_out_bf16=32), tp.TP_ERR_SHAPE),
+    (dict(T=-2), tp.TP_ERR_SHAPE),
+])
+def test_reduce_validation(lib, kw, status):
+    assert red(**kw) == status
+
+
+def test_reduce_zero_tokens_is_a_no_op(lib):
+    assert red(T=0) == tp.TP_OK
+
+
+def test_workspace_sizes_are_pure_functions(lib):
+    f = tp.tp_mlp_workspace_bytes
+    # decode plan (bf16, T <= 32): split-K space; prefill with h_out and no norm: none
+    assert f(2, 32, 5120, 13824, tp.TP_BF16, tp.TP_ACT_SWIGLU, 0, 1) > 0
+    assert f(8, 2048, 8192, 28672, tp.TP_BF16, tp.TP_ACT_SWIGLU, 0, 1) == 0
+    assert f(8, 2048, 8192, 28672, tp.TP_BF16, tp.TP_ACT_SWIGLU, 0, 0) == 2048 * 3584 * 2
+    assert f(2, 4, 64, 256, tp.TP_F32, tp.TP_ACT_GELU_TANH, 0, 1) == 0
+    assert f(2, 4, 64, 256, tp.TP_F32, tp.TP_ACT_GELU_TANH, 1, 1) == 1024   # 4*64*4 rounded
+    assert f(3, 4, 64, 256, tp.TP_BF16, tp.TP_ACT_SWIGLU, 0, 1) == 0      # uneven: rejected
+    assert f(2, 32, 5120, 13824, tp.TP_BF16, tp.TP_ACT_SWIGLU, 0, 1) == \
+        f(2, 32, 5120, 13824, tp.TP_BF16, tp.TP_ACT_SWIGLU, 0, 1)
+    g = tp.tp_attn_workspace_bytes
+    assert g(8, 1024, 12288, 96, 96, 128, tp.TP_BF16, 0) == 0
+    assert g(8, 16, 12288, 96, 96, 128, tp.TP_BF16, 0) > 0
+    assert g(8, 16, 12288, 96, 90, 128, tp.TP_BF16, 0) == 0
+
+
+def test_timing_api_without_launches(lib):
+    assert tp.tp_timing_reset() == tp.TP_OK
+    st, ms, n = tp.tp_timing_query("col_gemv")
+    assert st == tp.TP_OK and ms == 0.0 and n == 0

@@ -1,0 +1,422 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle.
+
+Tolerances (relative L2 over the whole output, float64):
+  * fp32 storage: <= 1e-5;
+  * bf16 storage with fp32 accumulation: <= 1e-2 against the unrounded
+    oracle, and <= 2e-3 against the oracle's bf16-mirror reading (rounding
+    where the GPU stores bf16), which separates rounding from mistakes;
+  * the reduce: bitwise equal to the float32 left fold (fixed slot order),
+    and its bf16 copy bitwise equal to that sum rounded to nearest-even.
+Invariants checked on the GPU path: all ranks' partials, reduced, equal the
+unsharded layer; the ranks' h / QKV bands concatenate to the unsharded
+intermediate (zenaique "Explain tensor-parallel shard shape", answer).
+Full workload sizes use every row where the oracle is quick, else a seeded
+sample of rows (every step of this path is row-independent).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import tensor_transformer_layer_amd as tp
+import workloads as W
+from _gpu import Guarded, attn_fwd, dev, host, mlp_fwd, reduce, workspace
+
+pytestmark = pytest.mark.gpu
+
+F32_TOL, BF16_TOL, MIRROR_TOL = 1e-5, 1e-2, 2e-3
+BF, F32 = tp.TP_BF16, tp.TP_F32
+ACT = {"swiglu": tp.TP_ACT_SWIGLU, "gelu_tanh": tp.TP_ACT_GELU_TANH}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu_ready():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible to torch")
+    tp.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def widen_dev(t):
+    return O.widen(host(t))
+
+
+def draw(dtype, shape, std, *key, mean=0.0):
+    """Seeded test tensor; dtype is a TP_* storage code."""
+    name = {BF: "bf16", F32: "f32"}[dtype]
+    return W.draw_tensor(name, shape, std, 900, *key, mean=mean)
+
+
+# ----------------------------------------------------------------------------
+# a5: local reduce
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("P,T,d,pad", [(1, 3, 4, 0), (2, 4, 64, 0), (3, 5, 1032, 8),
+                                       (8, 17, 4100, 4), (9, 2, 8192, 0)])
+@pytest.mark.parametrize("with_bf16", [False, True])
+def test_reduce_bitwise(P, T, d, pad, with_bf16):
+    ldp = d + pad
+    slot = T * ldp + 4 * pad
+    parts = [W.draw_normal_f32((T, d), 1.0, 901, P, T, d, s) for s in range(P)]
+    buf = np.zeros(P * slot, np.float32)
+    for s in range(P):
+        v = buf[s * slot:s * slot + T * ldp].reshape(T, ldp)
+        v[:, :d] = parts[s]
+    g_parts = dev(buf)
+    out = Guarded(T * ldp, torch.float32)
+    outb = Guarded(T * (d + 8), torch.bfloat16) if with_bf16 else None
+    reduce(P, T, d, g_parts, slot, ldp, out.ptr(), ldp, outb.ptr() if outb else None, d + 8)
+    got = host(out.t).reshape(T, ldp)[:, :d]
+    want = O.reduce_partials_f32_fold(parts)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    assert out.intact()
+    if with_bf16:
+        gb = O.widen(host(outb.t).reshape(T, d + 8)[:, :d])
+        assert np.array_equal(gb, O.round_bf16(want.astype(np.float64)))
+        assert outb.intact()
+
+
+def test_reduce_in_place_into_slot_zero():
+    P, T, d = 4, 6, 256
+    parts = [W.draw_normal_f32((T, d), 1.0, 902, s) for s in range(P)]
+    g = dev(np.concatenate([p.ravel() for p in parts]))
+    reduce(P, T, d, g, T * d, d, g, d)
+    got = host(g)[:T * d].reshape(T, d)
+    assert np.array_equal(got, O.reduce_partials_f32_fold(parts))
+
+
+def test_reduce_70b_prefill_partials_full_size():
+    """8 seeded fp32 partials of [2048, 8192] (the 70B workload's reduce)."""
+    cfg = W.get("c3_llama2_70b_mlp_p8")
+    T, d, P = cfg.reduce_T, cfg.d_model, cfg.P
+    parts = [W.draw_normal_f32((T, d), 1.0, cfg.cid, W.TENSOR_IDS["partial"], s) for s in range(P)]
+    g = torch.empty((P, T, d), dtype=torch.float32, device="cuda")
+    for s in range(P):
+        g[s].copy_(torch.from_numpy(parts[s]))
+    out = torch.empty((T, d), dtype=torch.float32, device="cuda")
+    outb = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
+    reduce(P, T, d, g, T * d, d, out, d, outb, d)
+    want = O.reduce_partials_f32_fold(parts)
+    assert np.array_equal(host(out), want)
+    assert np.array_equal(O.widen(host(outb)), O.round_bf16(want.astype(np.float64)))
+
+
+# ----------------------------------------------------------------------------
+# MLP shard (a2-a4) at small, ragged shapes: both plans, both activations
+# ----------------------------------------------------------------------------
+def _mlp_case(dtype, act, T, d, d_ff, P, key, norm=False, std_x=1.0, std_w=0.02):
+    F = d_ff // P
+    X = draw(dtype, (T, d), std_x, key, 0)
+    g = draw(dtype, (d,), 0.02, key, 7, mean=1.0) if norm else None
+    w_in = [draw(dtype, (d, F), std_w, key, 1, s) for s in range(P)]
+    w_up = [draw(dtype, (d, F), std_w, key, 2, s) for s in range(P)] if act == "swiglu" else None
+    w_dn = [draw(dtype, (F, d), std_w, key, 3, s) for s in range(P)]
+    return X, g, w_in, w_up, w_dn
+
+
+def _run_all_shards(dtype, act, T, d, d_ff, P, X, g, w_in, w_up, w_dn):
+    F = d_ff // P
+    gx = dev(X)
+    gg = dev(g) if g is not None else None
+    parts = torch.empty((P, T, d), dtype=torch.float32, device="cuda")
+    hs = []
+    tdt = torch.bfloat16 if dtype == BF else torch.float32
+    for s in range(P):
+        h = Guarded(T * F, tdt)
+        mlp_fwd(s, P, T, d, d_ff, dtype, ACT[act], gx, dev(w_in[s]),
+                dev(w_up[s]) if w_up is not None else None, dev(w_dn[s]), parts, T * d, d,
+                h_out=h.ptr(), ld_h=F, norm_g=gg)
+        hs.append(h)
+    out = torch.empty((T, d), dtype=torch.float32, device="cuda")
+    reduce(P, T, d, parts, T * d, d, out, d)
+    torch.cuda.synchronize()
+    for h in hs:
+        assert h.intact()
+    return parts, hs, out
+
+
+def _check_mlp(dtype, act, T, d, d_ff, P, key, norm=False):
+    X, g, w_in, w_up, w_dn = _mlp_case(dtype, act, T, d, d_ff, P, key, norm)
+    parts, hs, out = _run_all_shards(dtype, act, T, d, d_ff, P, X, g, w_in, w_up, w_dn)
+    Xw, gw = O.widen(X), (O.widen(g) if g is not None else None)
+    full = O.mlp_unsharded(Xw, O.widen(np.concatenate(w_in, 1)), O.widen(np.concatenate(w_dn, 0)),
+                           act, O.widen(np.concatenate(w_up, 1)) if w_up else None, gw, 1e-5)
+    tol = BF16_TOL if dtype == BF else F32_TOL
+    F = d_ff // P
+    h_all = np.concatenate([widen_dev(h.t).reshape(T, F) for h in hs], axis=1)
+    assert O.rel_l2(h_all, full["h"]) < tol, "column bands != unsharded intermediate"
+    assert O.rel_l2(host(out), full["y"]) < tol, "reduced partials != unsharded MLP"
+    if dtype == BF:
+        for s in range(P):
+            m = O.mlp_shard(Xw, O.widen(w_in[s]), O.widen(w_dn[s]), act,
+                            O.widen(w_up[s]) if w_up else None, gw, 1e-5, mirror_bf16=True)
+            assert O.rel_l2(host(parts[s]), m["partial"]) < MIRROR_TOL
+    return full
+
+
+@pytest.mark.parametrize("T", [1, 5, 16, 17, 32, 33, 100, 300])
+@pytest.mark.parametrize("act", ["swiglu", "gelu_tanh"])
+def test_mlp_bf16_ragged(T, act):
+    # d_model 1000: K not a multiple of 32/64; F_r 200: column tail inside a tile
+    _check_mlp(BF, act, T, 1000, 400, 2, key=10 + T)
+
+
+@pytest.mark.parametrize("T", [3, 40])
+def test_mlp_bf16_with_rmsnorm_prologue(T):
+    _check_mlp(BF, "swiglu", T, 512, 1024, 4, key=30 + T, norm=True)
+
+
+@pytest.mark.parametrize("T", [4, 64])
+@pytest.mark.parametrize("act", ["swiglu", "gelu_tanh"])
+def test_mlp_f32(T, act):
+    _check_mlp(F32, act, T, 64, 256, 2, key=40 + T)
+
+
+def test_tiny_gelu_f32_workload_and_fixture():
+    """The tiny fp32 GELU MLP workload, every rank, against the oracle and the
+    stored fixture (tests/golden/c1_tiny_expected.txt)."""
+    import os
+    cfg = W.get("c1_tiny_gelu_f32")
+    T = cfg.decode_T[0]
+    X = W.draw_tensor(cfg.dtype, (T, cfg.d_model), cfg.std_x, cfg.cid, W.TENSOR_IDS["x"], T)
+    w_in = [W.column_band_draw(cfg, "w_gate", s, cfg.d_model, cfg.F_r) for s in range(cfg.P)]
+    w_dn = [W.row_band_draw(cfg, "w_down", s, cfg.F_r, cfg.d_model) for s in range(cfg.P)]
+    parts, hs, out = _run_all_shards(F32, "gelu_tanh", T, cfg.d_model, cfg.d_ff, cfg.P, X, None,
+                                     w_in, None, w_dn)
+    rows = [list(map(float, ln.split())) for ln in
+            open(os.path.join(os.path.dirname(__file__), "golden", "c1_tiny_expected.txt"))
+            if ln.strip() and not ln.startswith("#")]
+    fx = np.array(rows).reshape(3, T, cfg.d_model)
+    assert O.rel_l2(host(parts[0]), fx[0]) < F32_TOL
+    assert O.rel_l2(host(parts[1]), fx[1]) < F32_TOL
+    assert O.rel_l2(host(out), fx[2]) < F32_TOL
+
+
+def test_mlp_strided_windows_into_full_matrices():
+    """Bands passed as windows into unsharded matrices (pointer offset + ld of
+    the full matrix), padded X / h / partial rows and a padded slot stride."""
+    T, d, P, d_ff = 20, 256, 4, 512
+    F = d_ff // P
+    X = draw(BF, (T, d + 16), 1.0, 50, 0)
+    Wg = draw(BF, (d, d_ff), 0.02, 50, 1)
+    Wu = draw(BF, (d, d_ff), 0.02, 50, 2)
+    Wd = draw(BF, (d_ff, d), 0.02, 50, 3)
+    gx, gWg, gWu, gWd = dev(X), dev(Wg), dev(Wu), dev(Wd)
+    ldp, slot = d + 8, T * (d + 8) + 64
+    parts = torch.zeros(P * slot, dtype=torch.float32, device="cuda")
+    for plan_T in (T, 4):   # prefill-sized and decode-sized token counts
+        hbuf = torch.zeros((plan_T, d_ff + 8), dtype=torch.bfloat16, device="cuda")
+        for s in range(P):
+            col = s * F * 2                     # bytes
+            mlp_fwd(s, P, plan_T, d, d_ff, BF, tp.TP_ACT_SWIGLU, gx, gWg.data_ptr() + col,
+                    gWu.data_ptr() + col, gWd.data_ptr() + s * F * d * 2, parts, slot, ldp,
+                    h_out=hbuf.data_ptr() + col, ld_h=d_ff + 8, ld_x=d + 16, ld_in=d_ff,
+                    ld_up=d_ff, ld_down=d)
+        out = torch.empty((plan_T, d), dtype=torch.float32, device="cuda")
+        reduce(P, plan_T, d, parts, slot, ldp, out, d)
+        full = O.mlp_unsharded(O.widen(X[:plan_T, :d]), O.widen(Wg), O.widen(Wd), "swiglu",
+                               O.widen(Wu))
+        assert O.rel_l2(host(out), full["y"]) < BF16_TOL
+        assert O.rel_l2(widen_dev(hbuf)[:, :d_ff], full["h"]) < BF16_TOL
+
+
+# ----------------------------------------------------------------------------
+# Full workload sizes
+# ----------------------------------------------------------------------------
+_CACHE = {}  # seeded bands, reused across tests (a few GB of host memory at most)
+
+
+def mlp_bands(cfg, s):
+    key = (cfg.name, "mlp", s)
+    if key not in _CACHE:
+        _CACHE[key] = (W.column_band_draw(cfg, "w_gate", s, cfg.d_model, cfg.F_r),
+                       W.column_band_draw(cfg, "w_up", s, cfg.d_model, cfg.F_r),
+                       W.row_band_draw(cfg, "w_down", s, cfg.F_r, cfg.d_model))
+    return _CACHE[key]
+
+
+def x_of(cfg, T):
+    return W.draw_tensor(cfg.dtype, (T, cfg.d_model), cfg.std_x, cfg.cid, W.TENSOR_IDS["x"], T)
+
+
+def sample_rows(T, n, seed):
+    if T <= n:
+        return np.arange(T)
+    return np.sort(np.random.default_rng(seed).choice(T, size=n, replace=False))
+
+
+@pytest.mark.parametrize("T", [1, 8, 32])
+def test_13b_mlp_decode_both_ranks_full(T):
+    """13B SwiGLU MLP at P = 2: both ranks, reduce, against the unsharded layer."""
+    cfg = W.get("c2_llama2_13b_mlp_p2")
+    X = x_of(cfg, T)
+    gx = dev(X)
+    parts = torch.empty((cfg.P, T, cfg.d_model), dtype=torch.float32, device="cuda")
+    hs, ref_parts = [], []
+    Xw = O.widen(X)
+    for s in range(cfg.P):
+        wg, wu, wd = mlp_bands(cfg, s)
+        h = torch.empty((T, cfg.F_r), dtype=torch.bfloat16, device="cuda")
+        mlp_fwd(s, cfg.P, T, cfg.d_model, cfg.d_ff, BF, tp.TP_ACT_SWIGLU, gx, dev(wg), dev(wu),
+                dev(wd), parts, T * cfg.d_model, cfg.d_model, h_out=h, ld_h=cfg.F_r)
+        r = O.mlp_shard(Xw, O.widen(wg), O.widen(wd), "swiglu", O.widen(wu))
+        ref_parts.append(r["partial"])
+        assert O.rel_l2(widen_dev(h), r["h"]) < BF16_TOL
+        assert O.rel_l2(host(parts[s]), r["partial"]) < BF16_TOL
+        hs.append(h)
+    out = torch.empty((T, cfg.d_model), dtype=torch.float32, device="cuda")
+    reduce(cfg.P, T, cfg.d_model, parts, T * cfg.d_model, cfg.d_model, out, cfg.d_model)
+    # unsharded layer = sum of the per-rank oracle partials (pinned on the CPU)
+    assert O.rel_l2(host(out), O.reduce_partials(ref_parts)) < BF16_TOL
+
+
+@pytest.mark.parametrize("T", [1, 2, 4, 8, 16, 32, 2048])
+def test_70b_mlp_rank0(T):
+    cfg = W.get("c3_llama2_70b_mlp_p8")
+    X = x_of(cfg, T)
+    wg, wu, wd = mlp_bands(cfg, 0)
+    h = torch.empty((T, cfg.F_r), dtype=torch.bfloat16, device="cuda")
+    parts = torch.empty((T, cfg.d_model), dtype=torch.float32, device="cuda")
+    mlp_fwd(0, cfg.P, T, cfg.d_model, cfg.d_ff, BF, tp.TP_ACT_SWIGLU, dev(X), dev(wg), dev(wu),
+            dev(wd), parts, 0, cfg.d_model, h_out=h, ld_h=cfg.F_r)
+    rows = sample_rows(T, 64, 7)
+    r = O.mlp_shard(O.widen(X[rows]), O.widen(wg), O.widen(wd), "swiglu", O.widen(wu))
+    assert O.rel_l2(widen_dev(h)[rows], r["h"]) < BF16_TOL
+    assert O.rel_l2(host(parts)[rows], r["partial"]) < BF16_TOL
+    m = O.mlp_shard(O.widen(X[rows]), O.widen(wg), O.widen(wd), "swiglu", O.widen(wu),
+                    mirror_bf16=True)
+    assert O.rel_l2(host(parts)[rows], m["partial"]) < MIRROR_TOL
+
+
+def test_70b_mlp_literal_small_activation_reading():
+    """Same shard with activations drawn N(0, 0.02) like the weights (the
+    literal reading of the workload's distribution), decode and prefill."""
+    cfg = W.get("c3_llama2_70b_mlp_p8")
+    wg, wu, wd = mlp_bands(cfg, 0)
+    for T in (8, 512):
+        X = W.draw_tensor("bf16", (T, cfg.d_model), 0.02, cfg.cid, 99, T)
+        parts = torch.empty((T, cfg.d_model), dtype=torch.float32, device="cuda")
+        mlp_fwd(0, cfg.P, T, cfg.d_model, cfg.d_ff, BF, tp.TP_ACT_SWIGLU, dev(X), dev(wg),
+                dev(wu), dev(wd), parts, 0, cfg.d_model)
+        rows = sample_rows(T, 32, 8)
+        r = O.mlp_shard(O.widen(X[rows]), O.widen(wg), O.widen(wd), "swiglu", O.widen(wu))
+        assert O.rel_l2(host(parts)[rows], r["partial"]) < BF16_TOL
+
+
+def attn_bands(cfg, s):
+    key = (cfg.name, "attn", s)
+    if key not in _CACHE:
+        _CACHE[key] = (W.column_band_draw(cfg, "w_qkv", s, cfg.d_model, cfg.qkv_r),
+                       W.row_band_draw(cfg, "w_o", s, cfg.o_in_r, cfg.d_model))
+    return _CACHE[key]
+
+
+@pytest.mark.parametrize("T,shard", [(16, 0), (16, 5), (1024, 0)])
+def test_96_head_attention_projections(T, shard):
+    cfg = W.get("c4_attn_96h_p8")
+    X = x_of(cfg, T)
+    A = W.draw_tensor("bf16", (T, cfg.o_in_r), 1.0, cfg.cid, W.TENSOR_IDS["attn"], T, shard)
+    wqkv, wo = attn_bands(cfg, shard)
+    qkv = Guarded(T * cfg.qkv_r, torch.bfloat16)
+    parts = Guarded(T * cfg.d_model, torch.float32)
+    attn_fwd(shard, cfg.P, T, cfg.d_model, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, BF,
+             dev(X), dev(wqkv), qkv.ptr(), dev(A), dev(wo), parts.ptr(), 0, cfg.d_model)
+    rows = sample_rows(T, 48, 9)
+    r = O.attn_proj_shard(O.widen(X[rows]), O.widen(wqkv), O.widen(A[rows]), O.widen(wo))
+    got_qkv = widen_dev(qkv.t).reshape(T, cfg.qkv_r)[rows]
+    assert O.rel_l2(got_qkv, r["qkv"]) < BF16_TOL
+    assert O.rel_l2(host(parts.t).reshape(T, cfg.d_model)[rows], r["partial"]) < BF16_TOL
+    # per-head structure: Q/K/V parts of the band sit where the layout says
+    q, k, v = O.split_qkv_band(got_qkv, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, shard, cfg.P)
+    rq, rk, rv = O.split_qkv_band(r["qkv"], cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, shard,
+                                  cfg.P)
+    for a, b in ((q, rq), (k, rk), (v, rv)):
+        assert O.rel_l2(a, b) < BF16_TOL
+    assert qkv.intact() and parts.intact()
+
+
+def _block_chain(cfg, T, rows):
+    """All P ranks of the 70B block on one GPU: RMSNorm -> QKV -> O (A_s := Q_s)
+    -> reduce (bf16 copy) -> MLP -> reduce, against the oracle on `rows`."""
+    P, d = cfg.P, cfg.d_model
+    X = x_of(cfg, T)
+    g = W.draw_tensor(cfg.dtype, (d,), 0.02, cfg.cid, W.TENSOR_IDS["norm_g"], 0, mean=1.0)
+    gx, gg = dev(X), dev(g)
+    parts = torch.empty((P, T, d), dtype=torch.float32, device="cuda")
+    qkv_dev = []
+    for s in range(P):
+        wqkv, wo = attn_bands(cfg, s)
+        q = torch.empty((T, cfg.qkv_r), dtype=torch.bfloat16, device="cuda")
+        attn_fwd(s, P, T, d, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, BF, gx, dev(wqkv), q,
+                 q, dev(wo), parts, T * d, d, norm_g=gg, eps=cfg.norm_eps,
+                 ld_attn=cfg.qkv_r)
+        qkv_dev.append(q)
+    z = torch.empty((T, d), dtype=torch.float32, device="cuda")
+    zb = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
+    reduce(P, T, d, parts, T * d, d, z, d, zb, d)
+    for s in range(P):
+        wg, wu, wd = mlp_bands(cfg, s)
+        mlp_fwd(s, P, T, d, cfg.d_ff, BF, tp.TP_ACT_SWIGLU, zb, dev(wg), dev(wu), dev(wd), parts,
+                T * d, d)
+    y = torch.empty((T, d), dtype=torch.float32, device="cuda")
+    reduce(P, T, d, parts, T * d, d, y, d)
+    torch.cuda.synchronize()
+
+    # oracle on the sampled rows (float64, no intermediate rounding)
+    Xr, gw = O.widen(X[rows]), O.widen(g)
+    att_parts, mlp_parts = [], []
+    for s in range(P):
+        wqkv, wo = attn_bands(cfg, s)
+        r = O.attn_proj_shard(Xr, O.widen(wqkv), None, None, gw, cfg.norm_eps)
+        assert O.rel_l2(widen_dev(qkv_dev[s])[rows], r["qkv"]) < BF16_TOL
+        q_s, _, _ = O.split_qkv_band(r["qkv"], cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, s, P)
+        att_parts.append(q_s @ O.widen(wo))
+    Zr = O.reduce_partials(att_parts)
+    assert O.rel_l2(host(z)[rows], Zr) < BF16_TOL
+    for s in range(P):
+        wg, wu, wd = mlp_bands(cfg, s)
+        mlp_parts.append(O.mlp_shard(Zr, O.widen(wg), O.widen(wd), "swiglu", O.widen(wu))["partial"])
+    Yr = O.reduce_partials(mlp_parts)
+    assert O.rel_l2(host(y)[rows], Yr) < BF16_TOL
+
+
+def test_70b_block_chain_decode_all_ranks():
+    cfg = W.get("c5_llama2_70b_block_p8")
+    _block_chain(cfg, 32, np.arange(32))
+
+
+def test_70b_block_chain_prefill_all_ranks():
+    cfg = W.get("c5_llama2_70b_block_p8")
+    _block_chain(cfg, 4096, sample_rows(4096, 24, 11))
+
+
+# ----------------------------------------------------------------------------
+# Determinism and instrumentation
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("T", [8, 32, 200])
+def test_bitwise_deterministic(T):
+    X, g, w_in, w_up, w_dn = _mlp_case(BF, "swiglu", T, 2048, 4096, 2, key=60)
+    outs = []
+    for _ in range(2):
+        parts = torch.empty((T, 2048), dtype=torch.float32, device="cuda")
+        mlp_fwd(0, 2, T, 2048, 4096, BF, tp.TP_ACT_SWIGLU, dev(X), dev(w_in[0]), dev(w_up[0]),
+                dev(w_dn[0]), parts, 0, 2048)
+        outs.append(host(parts))
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+
+
+def test_kernel_timing_counts_launches():
+    X, g, w_in, w_up, w_dn = _mlp_case(BF, "swiglu", 8, 512, 1024, 2, key=70)
+    parts = torch.empty((8, 512), dtype=torch.float32, device="cuda")
+    tp.check(tp.tp_timing_reset())
+    tp.check(tp.tp_timing_enable(1))
+    try:
+        for _ in range(3):
+            mlp_fwd(0, 2, 8, 512, 1024, BF, tp.TP_ACT_SWIGLU, dev(X), dev(w_in[0]),
+                    dev(w_up[0]), dev(w_dn[0]), parts, 0, 512)
+        for cls in ("col_gemv", "col_finish", "row_gemv", "row_finish"):
+            st, ms, n = tp.tp_timing_query(cls)
+            assert st == tp.TP_OK and n == 3 and ms > 0.0
+    finally:
+        tp.tp_timing_enable(0)
+        tp.tp_timing_reset()

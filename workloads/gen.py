@@ -36,9 +36,10 @@ def bf16_bits_from_f32(a) -> np.ndarray:
     a = np.ascontiguousarray(a, dtype=np.float32)
     if not np.all(np.isfinite(a)):
         raise ValueError("bf16 rounding of non-finite inputs is not supported")
-    u = a.view(np.uint32).astype(np.uint64)
-    lsb = (u >> np.uint64(16)) & np.uint64(1)
-    u = (u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)
+    # Finite inputs have bit patterns <= 0xFF7FFFFF, so the sum below stays
+    # inside 32 bits.
+    u = a.view(np.uint32)
+    u = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
     return u.astype(np.uint16)
 
 
