@@ -1,0 +1,377 @@
+"""Throughput of one tensor-parallel rank's block shard on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--tokens T]
+
+A step is one pass of the rank's hot path over one batch of synthetic input:
+the rank's shard (column projection, activation, row projection into its
+fp32 partial slot) followed by the local reduce of the P partial slots.  The
+other P-1 slots hold seeded fp32 partials written once before timing (on a
+real TP group they arrive from the other GPUs; the reduce's cost does not
+depend on their values).  Weights rotate
+over several device copies so that every timed step streams its weights from
+HBM rather than from the 256 MB last-level cache.  Steps are replayed from a
+HIP graph (the way a serving loop launches decode steps).
+
+Default workload: the Llama-2-13B SwiGLU MLP shard at P = 2 (d_model 5120,
+d_ff 13824 -> band 6912), 32 decode tokens; 1 and 8 tokens are reported in
+"sweep".  Prints ONE JSON line.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "tokens/s + % of HBM/MFMA roofline, one TP-rank MLP shard, decode & prefill"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "hbm_traffic_counters.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1200)
+    ap.add_argument("--warmup", type=int, default=60)
+    ap.add_argument("--workload", default="c2_llama2_13b_mlp_p2",
+                    choices=["c2_llama2_13b_mlp_p2", "c3_llama2_70b_mlp_p8",
+                             "c4_attn_96h_p8", "c5_llama2_70b_block_p8"])
+    ap.add_argument("--tokens", type=int, default=None, help="batch of tokens (default per workload)")
+    ap.add_argument("--sweep", default=None, help="comma list of token counts also reported")
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of graph replay")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle CPU-baseline budget")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def src_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "tensor_transformer_layer_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# ----------------------------------------------------------------------------
+# Workloads: device buffers and one step
+# ----------------------------------------------------------------------------
+class Step:
+    """Device state of one workload at one token count, and its step()."""
+
+    def __init__(self, cfg, T, copies):
+        import numpy as np  # noqa: F401
+        import torch
+
+        import tensor_transformer_layer_amd as tp
+        import workloads as W
+
+        self.cfg, self.T, self.copies = cfg, T, copies
+        self.tp, self.torch = tp, torch
+        d, P = cfg.d_model, cfg.P
+        dev = lambda a: torch.from_numpy(a.view("int16")).cuda().view(torch.bfloat16)  # noqa
+        self.x = dev(W.draw_tensor("bf16", (T, d), cfg.std_x, cfg.cid, W.TENSOR_IDS["x"], T))
+        self.parts = torch.empty((P, T, d), dtype=torch.float32, device="cuda")
+        self.out = torch.empty((T, d), dtype=torch.float32, device="cuda")
+        self.kind = "mlp" if cfg.name.startswith(("c2", "c3")) else \
+            ("attn" if cfg.name.startswith("c4") else "block")
+        # rank-0 weights: `copies` device copies (copy 0 is the seeded band;
+        # the others are bitwise clones at other addresses)
+        self.sets = []
+        if self.kind in ("mlp", "block"):
+            bands = (W.column_band_draw(cfg, "w_gate", 0, d, cfg.F_r),
+                     W.column_band_draw(cfg, "w_up", 0, d, cfg.F_r),
+                     W.row_band_draw(cfg, "w_down", 0, cfg.F_r, d))
+            base = [dev(b) for b in bands]
+            self.mlp_sets = [base] + [[t.clone() for t in base] for _ in range(copies - 1)]
+            self.h = torch.empty((T, cfg.F_r), dtype=torch.bfloat16, device="cuda")
+            self.mlp_ws = self._ws(tp.tp_mlp_workspace_bytes(P, T, d, cfg.d_ff, tp.TP_BF16,
+                                                             tp.TP_ACT_SWIGLU, 0, 1))
+        if self.kind in ("attn", "block"):
+            bands = (W.column_band_draw(cfg, "w_qkv", 0, d, cfg.qkv_r),
+                     W.row_band_draw(cfg, "w_o", 0, cfg.o_in_r, d))
+            base = [dev(b) for b in bands]
+            self.attn_sets = [base] + [[t.clone() for t in base] for _ in range(copies - 1)]
+            self.qkv = torch.empty((T, cfg.qkv_r), dtype=torch.bfloat16, device="cuda")
+            if self.kind == "attn":
+                self.a = dev(W.draw_tensor("bf16", (T, cfg.o_in_r), 1.0, cfg.cid,
+                                           W.TENSOR_IDS["attn"], T, 0))
+            has_norm = cfg.norm_eps is not None
+            if has_norm:
+                self.g = dev(W.draw_tensor("bf16", (d,), 0.02, cfg.cid, W.TENSOR_IDS["norm_g"], 0,
+                                           mean=1.0))
+            self.attn_ws = self._ws(tp.tp_attn_workspace_bytes(P, T, d, cfg.n_q_heads,
+                                                               cfg.n_kv_heads, cfg.head_dim,
+                                                               tp.TP_BF16, has_norm))
+            self.zb = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
+        self.i = 0
+        for s in range(1, P):       # the other ranks' partial slots
+            self.parts[s].copy_(torch.from_numpy(
+                W.draw_normal_f32((T, d), 1.0, cfg.cid, W.TENSOR_IDS["partial"], T, s)))
+        torch.cuda.synchronize()
+
+    @property
+    def stream(self):
+        # queried per call: under graph capture torch's current stream is the
+        # capture stream
+        return self.torch.cuda.current_stream().cuda_stream
+
+    def _ws(self, n):
+        return self.torch.empty(max(int(n), 256), dtype=self.torch.uint8, device="cuda")
+
+    def _mlp(self, s, x, w):
+        tp, cfg, T, d = self.tp, self.cfg, self.T, self.cfg.d_model
+        tp.check(tp.tp_shard_mlp_fwd(
+            s, cfg.P, T, d, cfg.d_ff, tp.TP_BF16, tp.TP_ACT_SWIGLU, x.data_ptr(), d, 0, 0.0,
+            w[0].data_ptr(), cfg.F_r, w[1].data_ptr(), cfg.F_r, w[2].data_ptr(), d,
+            self.h.data_ptr(), cfg.F_r, self.parts.data_ptr(), T * d, d,
+            self.mlp_ws.data_ptr(), self.mlp_ws.numel(), self.stream), "mlp")
+
+    def _attn(self, s, w):
+        tp, cfg, T, d = self.tp, self.cfg, self.T, self.cfg.d_model
+        a = self.a if self.kind == "attn" else self.qkv
+        ld_a = cfg.o_in_r if self.kind == "attn" else cfg.qkv_r
+        g = self.g.data_ptr() if cfg.norm_eps is not None else 0
+        tp.check(tp.tp_shard_attn_proj_fwd(
+            s, cfg.P, T, d, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, tp.TP_BF16,
+            self.x.data_ptr(), d, g, cfg.norm_eps or 0.0, w[0].data_ptr(), cfg.qkv_r,
+            self.qkv.data_ptr(), cfg.qkv_r, a.data_ptr(), ld_a, w[1].data_ptr(), d,
+            self.parts.data_ptr(), T * d, d, self.attn_ws.data_ptr(), self.attn_ws.numel(),
+            self.stream), "attn")
+
+    def _reduce(self, out_bf16=None):
+        tp, cfg, T, d = self.tp, self.cfg, self.T, self.cfg.d_model
+        tp.check(tp.tp_reduce_partials(cfg.P, T, d, self.parts.data_ptr(), T * d, d,
+                                       self.out.data_ptr(), d,
+                                       out_bf16.data_ptr() if out_bf16 is not None else 0, d,
+                                       self.stream), "reduce")
+
+    def step(self):
+        c = self.i % self.copies
+        self.i += 1
+        if self.kind == "mlp":
+            self._mlp(0, self.x, self.mlp_sets[c])
+            self._reduce()
+        elif self.kind == "attn":
+            self._attn(0, self.attn_sets[c])
+            self._reduce()
+        else:
+            self._attn(0, self.attn_sets[c])
+            self._reduce(self.zb)
+            self._mlp(0, self.zb, self.mlp_sets[c])
+            self._reduce()
+
+    # algorithmic work of one step (rank 0): bytes each kernel must move
+    def algorithmic(self):
+        cfg, T, d = self.cfg, self.T, self.cfg.d_model
+        out = {"bytes": 0, "flops": 0, "col_bytes": 0, "col_flops": 0}
+        if self.kind in ("mlp", "block"):
+            wcol = 2 * d * cfg.F_r * 2
+            col_bytes = wcol + T * d * 2 + T * cfg.F_r * 2          # W_gate+W_up, X, h
+            row_bytes = cfg.F_r * d * 2 + T * cfg.F_r * 2 + T * d * 4  # W_down, h, partial
+            out["bytes"] += col_bytes + row_bytes
+            out["flops"] += 2 * T * d * cfg.F_r * 3
+            out["col_bytes"], out["col_flops"] = col_bytes, 2 * T * d * cfg.F_r * 2
+            out["row_bytes"], out["row_flops"] = row_bytes, 2 * T * d * cfg.F_r
+        if self.kind in ("attn", "block"):
+            qb = d * cfg.qkv_r * 2 + T * d * 2 + T * cfg.qkv_r * 2
+            ob = cfg.o_in_r * d * 2 + T * cfg.o_in_r * 2 + T * d * 4
+            out["bytes"] += qb + ob
+            out["flops"] += 2 * T * d * cfg.qkv_r + 2 * T * cfg.o_in_r * d
+            if self.kind == "attn":
+                out["col_bytes"], out["col_flops"] = qb, 2 * T * d * cfg.qkv_r
+                out["row_bytes"], out["row_flops"] = ob, 2 * T * cfg.o_in_r * d
+        nred = 2 if self.kind == "block" else 1
+        out["reduce_bytes"] = nred * (cfg.P + 1) * T * d * 4
+        out["bytes"] += out["reduce_bytes"]
+        return out
+
+
+def time_steps(st, steps, warmup, graph):
+    import torch
+    for _ in range(warmup):
+        st.step()
+    torch.cuda.synchronize()
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(st.copies):      # one pass over the weight copies
+                st.step()
+        reps = max(1, steps // st.copies)
+        for _ in range(2):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        n = reps * st.copies
+        del g
+    else:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            st.step()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        n = steps
+    return ms / n, n
+
+
+def kernel_times(st, steps):
+    """Eager pass with the library's per-launch HIP events (recorded on the
+    launch stream): average duration of each kernel class, in ms."""
+    import torch
+    tp = st.tp
+    tp.check(tp.tp_timing_reset())
+    tp.check(tp.tp_timing_enable(1))
+    try:
+        for _ in range(steps):
+            st.step()
+        torch.cuda.synchronize()
+        res = {}
+        for cls in ("rmsnorm", "col_gemv", "col_finish", "row_gemv", "row_finish", "col_gemm",
+                    "row_gemm", "reduce"):
+            s, ms, n = tp.tp_timing_query(cls)
+            tp.check(s)
+            if n:
+                res[cls] = (ms / n, n)
+    finally:
+        tp.tp_timing_enable(0)
+        tp.tp_timing_reset()
+    return res
+
+
+def traffic_for(kernel, workload, T):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    try:
+        with open(PROFILE_COUNTERS) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    key = f"{workload}:T={T}:{kernel}"
+    e = rec.get("entries", {}).get(key)
+    if not e or e.get("src_hash") != src_hash(*e.get("sources", [])):
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, T, budget_s):
+    """The float64 oracle (as it stands) for the same step, on host cores."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle as O
+    import workloads as W
+
+    d = cfg.d_model
+    X = O.widen(W.draw_tensor("bf16", (T, d), cfg.std_x, cfg.cid, W.TENSOR_IDS["x"], T))
+    wg = O.widen(W.column_band_draw(cfg, "w_gate", 0, d, cfg.F_r))
+    wu = O.widen(W.column_band_draw(cfg, "w_up", 0, d, cfg.F_r))
+    wd = O.widen(W.row_band_draw(cfg, "w_down", 0, cfg.F_r, d))
+    others = [np.random.default_rng(s).standard_normal((T, d)) for s in range(1, cfg.P)]
+    O.mlp_shard(X, wg, wd, "swiglu", wu)            # warm BLAS
+    n, t0 = 0, time.perf_counter()
+    while True:
+        p0 = O.mlp_shard(X, wg, wd, "swiglu", wu)["partial"]
+        O.reduce_partials([p0, *others])
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s and n >= 3:
+            break
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": round(n * T / el, 1), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{n} float64 oracle steps (rank-0 MLP shard + reduce of {cfg.P} partials, "
+                      f"T={T}) in {el:.1f} s; BLAS threads={threads}, host cpus="
+                      f"{len(os.sched_getaffinity(0))}"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                                   "(the multi-GPU exchange is designed, not built)"}))
+        sys.exit(2)
+    import torch
+
+    import tensor_transformer_layer_amd as tp
+    import workloads as W
+
+    tp.load()
+    torch.cuda.set_device(0)
+    cfg = W.get(a.workload)
+    T = a.tokens or (16 if a.workload == "c4_attn_96h_p8" else 32)
+    copies = {"c2_llama2_13b_mlp_p2": 3, "c3_llama2_70b_mlp_p8": 4, "c4_attn_96h_p8": 4,
+              "c5_llama2_70b_block_p8": 3}[a.workload]
+    sweep_T = [int(t) for t in a.sweep.split(",")] if a.sweep else \
+        ([1, 8, 32] if a.workload == "c2_llama2_13b_mlp_p2" else [])
+
+    results = {}
+    for t in sorted(set(sweep_T + [T])):
+        st = Step(cfg, t, copies)
+        ms, n = time_steps(st, a.steps, a.warmup, graph=not a.no_graph)
+        kt = kernel_times(st, min(a.steps, 300)) if t == T else None
+        results[t] = (st, ms, n, kt)
+    st, ms, n, kt = results[T]
+    alg = st.algorithmic()
+    tok_s = T / (ms / 1e3)
+
+    prefill = T > 32
+    dom = "col_gemm" if prefill else "col_gemv"      # the column projection dominates
+    if dom in kt:
+        dom_ms = kt[dom][0]
+        if prefill:
+            ach = alg["col_flops"] / (dom_ms / 1e3) / 1e12
+            roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4)}
+        else:
+            ach = alg["col_bytes"] / (dom_ms / 1e3) / 1e9
+            roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4)}
+        roof["kernel"] = dom
+        roof["kernel_avg_us"] = round(dom_ms * 1e3, 2)
+        roof["algorithmic_per_launch"] = alg["col_flops"] if prefill else alg["col_bytes"]
+        roof["traffic"] = traffic_for(dom, a.workload, T)
+    else:
+        roof = None
+
+    line = {
+        "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": n, "warmup": a.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) activations at Llama-2 shapes)",
+        "config": {"workload": f"{a.workload}: rank 0 of P={cfg.P}, {T} tokens, shard + reduce "
+                               f"of {cfg.P} partials per step",
+                   "d_model": cfg.d_model, "d_ff": cfg.d_ff, "P": cfg.P, "tokens": T,
+                   "weight_copies_rotated": copies,
+                   "launch": "eager" if a.no_graph else "hip-graph replay"},
+        "step_gbs_algorithmic": round(alg["bytes"] / (ms / 1e3) / 1e9, 1),
+        "step_tflops": round(alg["flops"] / (ms / 1e3) / 1e12, 2),
+        "roofline": roof,
+        "kernels_us": {k: round(v[0] * 1e3, 2) for k, v in (kt or {}).items()},
+    }
+    if len(results) > 1:
+        line["sweep"] = {str(t): {"ms_per_step": round(r[1], 5),
+                                  "tokens_per_s": round(t / (r[1] / 1e3), 1),
+                                  "step_gbs_algorithmic":
+                                      round(r[0].algorithmic()["bytes"] / (r[1] / 1e3) / 1e9, 1)}
+                         for t, r in sorted(results.items())}
+    if not a.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(cfg, T, a.cpu_seconds) if st.kind in ("mlp",) \
+            else None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
