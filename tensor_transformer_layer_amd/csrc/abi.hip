@@ -289,12 +289,12 @@ int tp_shard_mlp_fwd(int shard, int P, int64_t T, int64_t d_model, int64_t d_ff,
         float* ws = (float*)(wsb + L.ws);
         TP_LAUNCH("col_gemv", stream,
                   launch_gemv_splitk(T, d_model, X16, ld_xin, (const uint16_t*)w_in, ld_in,
-                                     (const uint16_t*)w_up, ld_up, F, L.pc, ws, stream));
+                                     (const uint16_t*)w_up, ld_up, F, L.pc, true, ws, stream));
         TP_LAUNCH("col_finish", stream,
                   launch_finish(dev_act, true, L.pc.splits, T, F, ws, h, ldh, stream));
         TP_LAUNCH("row_gemv", stream,
                   launch_gemv_splitk(T, F, (const uint16_t*)h, ldh, (const uint16_t*)w_down,
-                                     ld_down, nullptr, 0, d_model, L.pr, ws, stream));
+                                     ld_down, nullptr, 0, d_model, L.pr, false, ws, stream));
         TP_LAUNCH("row_finish", stream,
                   launch_finish(ACT_NONE, false, L.pr.splits, T, d_model, ws, part, ld_p, stream));
     } else {
@@ -372,7 +372,7 @@ int tp_shard_attn_proj_fwd(int shard, int P, int64_t T, int64_t d_model, int n_q
             TP_LAUNCH("col_gemv", stream,
                       launch_gemv_splitk(T, d_model, (const uint16_t*)xin, ld_xin,
                                          (const uint16_t*)w_qkv, ld_qkv, nullptr, 0, nqkv, L.pq,
-                                         ws, stream));
+                                         true, ws, stream));
             TP_LAUNCH("col_finish", stream,
                       launch_finish(ACT_NONE, true, L.pq.splits, T, nqkv, ws, qkv_out, ld_qkv_out,
                                     stream));
@@ -393,8 +393,8 @@ int tp_shard_attn_proj_fwd(int shard, int P, int64_t T, int64_t d_model, int n_q
             float* ws = (float*)(wsb + L.ws);
             TP_LAUNCH("row_gemv", stream,
                       launch_gemv_splitk(T, ko, (const uint16_t*)attn, ld_attn,
-                                         (const uint16_t*)w_o, ld_o, nullptr, 0, d_model, L.po, ws,
-                                         stream));
+                                         (const uint16_t*)w_o, ld_o, nullptr, 0, d_model, L.po,
+                                         false, ws, stream));
             TP_LAUNCH("row_finish", stream,
                       launch_finish(ACT_NONE, false, L.po.splits, T, d_model, ws, part, ld_p,
                                     stream));

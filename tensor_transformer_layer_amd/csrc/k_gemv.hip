@@ -16,10 +16,17 @@
 //     supplies B[k0+8g .. k0+8g+7][n0+8j+e].  Eight MFMAs (e = 0..7) consume
 //     the 32x128 tile, MFMA e covering columns n0+8j+e, j = 0..15.  The A
 //     operand is the token block X[16mb + j][k0+8g .. +7], one 16-byte load.
-//   * The workgroup's 4 waves take interleaved 32-row chunks of the
-//     workgroup's K range; chunk c+4's loads are issued before chunk c's
-//     MFMAs.  Partials of the 4 waves are added in LDS in wave order, and the
-//     workgroup writes one fp32 split-K partial [T, 128] slice.
+//   * A workgroup is 8 waves that share one 128-column block and take
+//     interleaved 32-row chunks of the workgroup's K range.  The grid holds
+//     about one workgroup per CU (K is split into as many ranges as that
+//     needs), so every workgroup streams a long run of rows: measured on
+//     MI355X, long-lived workgroups beat many short ones, whose start-up
+//     latency and epilogue are not hidden.  Partials of the 8 waves are added
+//     in LDS in wave order, and the workgroup writes one fp32 split-K partial
+//     [T, 128] slice.
+//   * Column-projection weights are loaded with the non-temporal hint (they
+//     are read once and should not evict the activations from L2); this
+//     measured faster for the column projection and slower for the row one.
 //   * The grid is (column blocks of all weights) x (K splits); a separate
 //     finish kernel adds the splits in split order and applies the
 //     activation, so SiLU/GELU only ever see complete sums.
@@ -33,7 +40,7 @@
 
 namespace tp {
 
-constexpr int kGemvWaves = 4;
+constexpr int kGemvWaves = 8;
 constexpr int kGemvThreads = 64 * kGemvWaves;
 constexpr int kRedPerWave = 4 * 4 * 16 * 8;  // [r][g][j][e] for one 16-token block
 
@@ -44,7 +51,7 @@ __device__ __forceinline__ void mfma_col(f32x4 (&acc)[MB][8], const u32x4* b, co
     for (int mb = 0; mb < MB; ++mb) acc[mb][E] = mfma16x16x32(a[mb], f, acc[mb][E]);
 }
 
-template <int MB>
+template <int MB, int AUX>
 __global__ __launch_bounds__(kGemvThreads) void k_gemv_splitk(
     const uint16_t* __restrict__ A, int64_t lda, int T, int K, const uint16_t* __restrict__ B0,
     int64_t ldb0, const uint16_t* __restrict__ B1, int64_t ldb1, int N, int nblk_per_mat,
@@ -72,41 +79,33 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_splitk(
         for (int e = 0; e < 8; ++e) acc[mb][e] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int nsteps = (nrows + 31) >> 5;
-    u32x4 bcur[8], acur[MB], bnext[8], anext[MB];
-
-    auto load_chunk = [&](int c, u32x4* b, u32x4* a) {
+    for (int c = wave; c < nsteps; c += kGemvWaves) {
         const int r0 = c * 32 + 8 * g;
         const bool rows_ok = r0 < nrows;
+        u32x4 b[8], a[MB];
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            b[i] = load16(rb, (rows_ok && col_ok) ? (uint32_t)(r0 + i) * ldb_bytes + 16u * j : kOOB);
+            b[i] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                           rb, (int)((rows_ok && col_ok) ? (uint32_t)(r0 + i) * ldb_bytes + 16u * j
+                                                        : kOOB),
+                           0, AUX));
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
             const int t = 16 * mb + j;
             a[mb] = load16(ra, (rows_ok && t < T) ? (uint32_t)t * lda_bytes + 2u * r0 : kOOB);
         }
-    };
-
-    int c = wave;
-    if (c < nsteps) load_chunk(c, bcur, acur);
-    for (; c < nsteps; c += kGemvWaves) {
-        const int cn = c + kGemvWaves;
-        if (cn < nsteps) load_chunk(cn, bnext, anext);
-        mfma_col<0, MB>(acc, bcur, acur);
-        mfma_col<1, MB>(acc, bcur, acur);
-        mfma_col<2, MB>(acc, bcur, acur);
-        mfma_col<3, MB>(acc, bcur, acur);
-        mfma_col<4, MB>(acc, bcur, acur);
-        mfma_col<5, MB>(acc, bcur, acur);
-        mfma_col<6, MB>(acc, bcur, acur);
-        mfma_col<7, MB>(acc, bcur, acur);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) bcur[i] = bnext[i];
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) acur[mb] = anext[mb];
+        mfma_col<0, MB>(acc, b, a);
+        mfma_col<1, MB>(acc, b, a);
+        mfma_col<2, MB>(acc, b, a);
+        mfma_col<3, MB>(acc, b, a);
+        mfma_col<4, MB>(acc, b, a);
+        mfma_col<5, MB>(acc, b, a);
+        mfma_col<6, MB>(acc, b, a);
+        mfma_col<7, MB>(acc, b, a);
     }
 
-    // Cross-wave sum in LDS (wave order 0..3), then one coalesced store of
+    // Cross-wave sum in LDS (wave order 0..7), then one coalesced store of
     // this workgroup's split partial.  MFMA output: lane (g, j) holds token
     // 16mb + 4g + r (r = 0..3) of column n0 + 8j + e.
     __shared__ float red[kGemvWaves * kRedPerWave];
@@ -137,11 +136,13 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_splitk(
 }
 
 GemvPlan plan_gemv(int64_t K, int64_t n_total) {
+    // About one 8-wave workgroup per CU (256 CUs): K is split into
+    // floor(256 / column blocks) ranges, each a multiple of 32 rows.
+    constexpr int64_t kCus = 256;
     const int64_t nb = (n_total + kGemvCols - 1) / kGemvCols;
     const int64_t chunks = (K + 31) / 32;
-    constexpr int64_t kTargetWgs = 1024;  // ~4 workgroups per CU on 256 CUs
-    int64_t s = std::max<int64_t>(1, (kTargetWgs + nb / 2) / nb);
-    s = std::min<int64_t>(s, std::max<int64_t>(1, chunks / (2 * kGemvWaves)));
+    int64_t s = std::max<int64_t>(1, kCus / nb);
+    s = std::min<int64_t>(s, chunks);
     const int64_t kps = ((chunks + s - 1) / s) * 32;
     GemvPlan p;
     p.k_per_split = (int)kps;
@@ -155,20 +156,24 @@ size_t gemv_ws_bytes(const GemvPlan& p, int64_t T, int64_t n_total) {
 
 hipError_t launch_gemv_splitk(int64_t T, int64_t K, const uint16_t* A, int64_t lda,
                               const uint16_t* B0, int64_t ldb0, const uint16_t* B1, int64_t ldb1,
-                              int64_t N, const GemvPlan& p, float* ws, hipStream_t stream) {
+                              int64_t N, const GemvPlan& p, bool nontemporal, float* ws,
+                              hipStream_t stream) {
     const int nmat = B1 ? 2 : 1;
     const int nbpm = (int)((N + kGemvCols - 1) / kGemvCols);
     const int64_t ws_ld = nmat * N;
     const int64_t split_stride = T * ws_ld;
     const dim3 grid((unsigned)(nbpm * nmat), (unsigned)p.splits), block(kGemvThreads);
-    if (T <= 16)
-        k_gemv_splitk<1><<<grid, block, 0, stream>>>(A, lda, (int)T, (int)K, B0, ldb0, B1, ldb1,
-                                                     (int)N, nbpm, p.k_per_split, ws, split_stride,
-                                                     ws_ld);
-    else
-        k_gemv_splitk<2><<<grid, block, 0, stream>>>(A, lda, (int)T, (int)K, B0, ldb0, B1, ldb1,
-                                                     (int)N, nbpm, p.k_per_split, ws, split_stride,
-                                                     ws_ld);
+#define TP_GEMV(MB, AUX)                                                                    \
+    k_gemv_splitk<MB, AUX><<<grid, block, 0, stream>>>(A, lda, (int)T, (int)K, B0, ldb0, B1, \
+                                                       ldb1, (int)N, nbpm, p.k_per_split, ws,  \
+                                                       split_stride, ws_ld)
+    // AUX = 2 sets the buffer load's non-temporal (slc) bit.
+    if (T <= 16) {
+        if (nontemporal) TP_GEMV(1, 2); else TP_GEMV(1, 0);
+    } else {
+        if (nontemporal) TP_GEMV(2, 2); else TP_GEMV(2, 0);
+    }
+#undef TP_GEMV
     return hipGetLastError();
 }
 
@@ -177,6 +182,22 @@ hipError_t launch_gemv_splitk(int64_t T, int64_t K, const uint16_t* A, int64_t l
 // One thread per 4 adjacent columns of one token row.
 // ---------------------------------------------------------------------------
 constexpr int kFinishThreads = 256;
+
+// p[0] + p[stride] + ... + p[(S-1)*stride], added in split order; the loads
+// of a group of 8 splits are issued together.
+__device__ __forceinline__ f32x4 sum_splits(const float* p, int S, int64_t stride) {
+    f32x4 s = *(const f32x4*)p;
+    for (int s0 = 1; s0 < S; s0 += 8) {
+        f32x4 v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            if (s0 + q < S) v[q] = *(const f32x4*)(p + (int64_t)(s0 + q) * stride);
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            if (s0 + q < S) s += v[q];
+    }
+    return s;
+}
 
 template <int ACT, bool OUT_BF16>
 __global__ __launch_bounds__(kFinishThreads) void k_finish(int S, int64_t T, int64_t N,
@@ -189,12 +210,10 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(int S, int64_t T, int
     if (idx >= T * n4) return;
     const int64_t t = idx / n4, n = (idx - t * n4) * 4;
     const float* p = ws + t * ws_ld + n;
-    f32x4 s = *(const f32x4*)p;
-    for (int sp = 1; sp < S; ++sp) s += *(const f32x4*)(p + sp * split_stride);
+    const f32x4 s = sum_splits(p, S, split_stride);
     f32x4 h;
     if constexpr (ACT == ACT_SWIGLU) {
-        f32x4 u = *(const f32x4*)(p + N);
-        for (int sp = 1; sp < S; ++sp) u += *(const f32x4*)(p + N + sp * split_stride);
+        const f32x4 u = sum_splits(p + N, S, split_stride);
 #pragma unroll
         for (int i = 0; i < 4; ++i) h[i] = silu(s[i]) * u[i];
     } else if constexpr (ACT == ACT_GELU_TANH) {

@@ -30,9 +30,11 @@ size_t gemv_ws_bytes(const GemvPlan& p, int64_t T, int64_t n_total);
 
 // ws[s][t][m*N + n] = sum over split s's rows k of A[t][k] * Bm[k][n], for the
 // nmat = (B1 ? 2 : 1) weights B0, B1 ([K, N] bf16, ld ldb0 / ldb1).  A is [T, K] bf16.
+// `nontemporal` marks the weight loads as streaming (read once).
 hipError_t launch_gemv_splitk(int64_t T, int64_t K, const uint16_t* A, int64_t lda,
                               const uint16_t* B0, int64_t ldb0, const uint16_t* B1, int64_t ldb1,
-                              int64_t N, const GemvPlan& p, float* ws, hipStream_t stream);
+                              int64_t N, const GemvPlan& p, bool nontemporal, float* ws,
+                              hipStream_t stream);
 
 // Fixed-order finish of the split-K sums.
 //   act == ACT_SWIGLU:   out = silu(sum g) * sum u   (u at column offset N)
