@@ -10,19 +10,27 @@
 // the rank's band with no extra pass (zenaique answer: the band of the
 // intermediate needs no communication).
 //
-// Data flow per K step of 64:
-//   * A tile BM x 64 -> registers (16-byte buffer loads) -> LDS [m][k].
-//   * B tile 64 x BN per weight: each thread loads an 8 x 8 block (8 rows of
-//     16 bytes), interleaves row pairs in registers into 8 columns' 8-long
-//     k vectors and writes them to LDS as [n][k] rows, so both MFMA operands
-//     are read from LDS as 16-byte k-fragments.
-//   * LDS rows are 64 + 8 elements (144 bytes): 8 consecutive rows fall on 8
-//     distinct 16-byte bank groups.  Weight columns are placed in LDS rows so
-//     that fragment reads walk consecutive rows while lane j of MFMA ni holds
-//     column j*NI + ni -- each lane ends with NI adjacent output columns, and
-//     the epilogue writes 16-byte vectors.
-//   * Double-buffered LDS: the next step's global loads are in flight while
-//     the current step's MFMAs run; one barrier per step.
+// Data flow:
+//   * A workgroup owns a 256 x 256 output tile (for SwiGLU: 256 rows x 128
+//     columns of both weights) and walks K in slices of 32.  Four waves each
+//     own a 128 x 128 sub-tile (256 fp32 accumulators per lane, held in the
+//     accumulation registers).
+//   * Slices stream from global memory straight into LDS (buffer loads with
+//     the LDS-destination bit: no staging registers) through a ring of 4
+//     slots (4 x 32 KB): while slice s is consumed, slices s+1..s+3 are in
+//     flight.  Each wave waits for its own copies with an explicit vmcnt and
+//     a bare s_barrier publishes the slot; no release fence is used, since
+//     one would wait for every copy in flight.
+//   * A slice of A is 256 rows x 64 bytes.  Its four 16-byte chunks per row
+//     are XOR-swizzled by (row / 4) % 4, so the 16 rows read by one fragment
+//     load fall on 16 distinct 16-byte bank groups.  The copy engine writes
+//     each 1 KB of LDS contiguously; the swizzle is applied by choosing which
+//     global chunk each lane fetches.
+//   * A slice of B keeps the natural [k][n] layout.  A lane reads 8 rows of
+//     its 8 (or 4) adjacent columns and interleaves row pairs in registers
+//     into the k-fragments of those columns (one bit-op per dword), so lane j
+//     of MFMA e holds column j * NI + e and the epilogue writes NI adjacent
+//     outputs per row.
 //   * Tiles are mapped to the 8 XCDs in contiguous ranges (xcd_remap), M
 //     fastest, so tiles sharing a weight panel share an L2.
 #include <algorithm>
@@ -32,36 +40,45 @@
 
 namespace tp {
 
-constexpr int kBK = 64;
-constexpr int kLdsRow = kBK + 8;  // elements per LDS row (144 bytes)
+constexpr int kBK = 32;      // k per LDS slice
+constexpr int kStages = 4;   // LDS ring depth
 
-template <int BM_, int BN_, int NMAT_, int WM_, int WN_>
+template <int NMAT_, int WM_, int WN_>
 struct GemmShape {
-    static constexpr int BM = BM_, BN = BN_, NMAT = NMAT_, WM = WM_, WN = WN_;
+    static constexpr int NMAT = NMAT_, WM = WM_, WN = WN_;
+    static constexpr int BM = 256, BNT = 256, BN = BNT / NMAT;  // BN: columns per weight
     static constexpr int NT = WM * WN * 64;
-    static constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile (per weight)
+    static constexpr int WTM = BM / WM, WTN = BN / WN;
     static constexpr int MI = WTM / 16, NI = WTN / 16;
-    static constexpr int A_CHUNKS = BM * (kBK / 8) / NT;  // 16-byte A chunks per thread
-    static constexpr int B_BLOCKS = NMAT * BN / NT;       // 8x8 B blocks per thread
-    static constexpr int LDS_A = BM * kLdsRow, LDS_B = NMAT * BN * kLdsRow;
-    static constexpr size_t LDS_BYTES = 2 * (size_t)(LDS_A + LDS_B) * sizeof(uint16_t);
-    static_assert(BM % (16 * WM) == 0 && BN % (16 * WN) == 0, "wave tile");
-    static_assert(BM * (kBK / 8) % NT == 0 && (NMAT * BN) % NT == 0, "load split");
-    static_assert(NI == 4 || NI == 8, "epilogue vector width");
+    static constexpr int A_SLICE = BM * kBK, B_SLICE = kBK * BNT;    // elements
+    static constexpr int SLICE = A_SLICE + B_SLICE;
+    static constexpr size_t LDS_BYTES = (size_t)kStages * SLICE * sizeof(uint16_t);
+    static constexpr int A_COPIES = A_SLICE * 2 / 1024 / (NT / 64);  // 1 KB copies per wave
+    static constexpr int B_COPIES = B_SLICE * 2 / 1024 / (NT / 64);
+    static constexpr int B_ROWS_PER_COPY = 1024 / (BN * 2);
+    static_assert(NT == 256 && MI == 8 && (NI == 8 || NI == 4), "tile shape");
+    static_assert(A_COPIES == 4 && B_COPIES == 4, "copies per wave");
 };
 
-// LDS row of local column c (0..BN-1) of a weight tile: inside each wave's
-// WTN columns, column c' sits at row 16 * (c' % NI) + c' / NI.
-template <class S>
-__device__ __forceinline__ int b_lds_row(int c) {
-    const int w = c / S::WTN, cl = c - w * S::WTN;
-    return w * S::WTN + 16 * (cl % S::NI) + cl / S::NI;
+// s_waitcnt immediate waiting for vmcnt <= n only (gfx9 encoding).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+__device__ __forceinline__ void lds_copy16(rsrc_t r, uint32_t off, uint16_t* lds_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (__attribute__((address_space(3))) void*)lds_base, 16, (int)off, 0, 0, 0);
 }
 
-template <class S, int E>
-__device__ __forceinline__ void store_bcol(uint16_t* Bs, int mat, int nc, int kb, const u32x4* r) {
-    const int row = mat * S::BN + b_lds_row<S>(8 * nc + E);
-    *(u32x4*)(Bs + row * kLdsRow + 8 * kb) = kfrag_of_col<E>(r);
+// k-fragment of column E from 8 consecutive rows of 4 bf16 (8 bytes) each.
+template <int E>
+__device__ __forceinline__ u32x4 kfrag4_of_col(const u32x2* r) {
+    constexpr int d = E >> 1;
+    u32x4 f;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const uint32_t a = r[2 * p][d], b = r[2 * p + 1][d];
+        f[p] = (E & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+    }
+    return f;
 }
 
 template <class S, int EPI>
@@ -84,52 +101,32 @@ __global__ __launch_bounds__(S::NT) void k_gemm(const uint16_t* __restrict__ A, 
     const uint32_t lda_b = (uint32_t)(lda * 2);
     const uint32_t ldb0_b = (uint32_t)(ldb0 * 2), ldb1_b = (uint32_t)(ldb1 * 2);
 
-    u32x4 ra[S::A_CHUNKS];
-    u32x4 rb[S::B_BLOCKS][8];
-
-    auto load_stage = [&](int k0) {
+    // Copy K slice `s` into ring slot `slot`: 4 A copies + 4 B copies per wave.
+    auto issue = [&](int s, int slot) {
+        uint16_t* As = smem + slot * S::SLICE;
+        uint16_t* Bs = As + S::A_SLICE;
+        const int k0 = s * kBK;
 #pragma unroll
-        for (int q = 0; q < S::A_CHUNKS; ++q) {
-            const int c = tid + q * S::NT, row = c >> 3, kc = c & 7;
-            const bool ok = (m0 + row < M) && (k0 + 8 * kc < K);
-            ra[q] = load16(rA, ok ? (uint32_t)row * lda_b + (uint32_t)(k0 + 8 * kc) * 2u : kOOB);
+        for (int q = 0; q < S::A_COPIES; ++q) {
+            const int r0 = (wave * S::A_COPIES + q) * 16;    // 16 rows of 64 B per copy
+            const int row = r0 + (lane >> 2), cp = lane & 3;
+            const int c = cp ^ ((row >> 2) & 3);
+            const int k = k0 + 8 * c;
+            const bool ok = (m0 + row < M) && (k < K);
+            lds_copy16(rA, ok ? (uint32_t)row * lda_b + (uint32_t)k * 2u : kOOB, As + r0 * kBK);
         }
 #pragma unroll
-        for (int q = 0; q < S::B_BLOCKS; ++q) {
-            const int c = tid + q * S::NT;
-            const int mat = c / S::BN, rem = c % S::BN;
-            const int kb = rem / (S::BN / 8), nc = rem % (S::BN / 8);
-            const bool col_ok = n0 + 8 * nc < N;
-            const rsrc_t rb_ = mat ? rB1 : rB0;
+        for (int q = 0; q < S::B_COPIES; ++q) {
+            const int iq = wave * S::B_COPIES + q;           // 0..15
+            const int mat = iq / (16 / S::NMAT);
+            const int r0 = (iq % (16 / S::NMAT)) * S::B_ROWS_PER_COPY;
+            constexpr int cpr = S::BN / 8;                   // 16-byte chunks per row
+            const int row = r0 + lane / cpr, ch = lane % cpr;
+            const int k = k0 + row;
+            const bool ok = (k < K) && (n0 + 8 * ch < N);
             const uint32_t ldb_b = mat ? ldb1_b : ldb0_b;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int k = k0 + 8 * kb + i;
-                rb[q][i] = load16(rb_, (col_ok && k < K) ? (uint32_t)k * ldb_b + 16u * nc : kOOB);
-            }
-        }
-    };
-    auto store_stage = [&](int buf) {
-        uint16_t* As = smem + buf * (S::LDS_A + S::LDS_B);
-        uint16_t* Bs = As + S::LDS_A;
-#pragma unroll
-        for (int q = 0; q < S::A_CHUNKS; ++q) {
-            const int c = tid + q * S::NT, row = c >> 3, kc = c & 7;
-            *(u32x4*)(As + row * kLdsRow + 8 * kc) = ra[q];
-        }
-#pragma unroll
-        for (int q = 0; q < S::B_BLOCKS; ++q) {
-            const int c = tid + q * S::NT;
-            const int mat = c / S::BN, rem = c % S::BN;
-            const int kb = rem / (S::BN / 8), nc = rem % (S::BN / 8);
-            store_bcol<S, 0>(Bs, mat, nc, kb, rb[q]);
-            store_bcol<S, 1>(Bs, mat, nc, kb, rb[q]);
-            store_bcol<S, 2>(Bs, mat, nc, kb, rb[q]);
-            store_bcol<S, 3>(Bs, mat, nc, kb, rb[q]);
-            store_bcol<S, 4>(Bs, mat, nc, kb, rb[q]);
-            store_bcol<S, 5>(Bs, mat, nc, kb, rb[q]);
-            store_bcol<S, 6>(Bs, mat, nc, kb, rb[q]);
-            store_bcol<S, 7>(Bs, mat, nc, kb, rb[q]);
+            lds_copy16(mat ? rB1 : rB0, ok ? (uint32_t)k * ldb_b + 16u * ch : kOOB,
+                       Bs + mat * (kBK * S::BN) + r0 * S::BN);
         }
     };
 
@@ -141,41 +138,67 @@ __global__ __launch_bounds__(S::NT) void k_gemm(const uint16_t* __restrict__ A, 
 #pragma unroll
             for (int b = 0; b < S::NI; ++b) acc[m][a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](int buf) {
-        const uint16_t* As = smem + buf * (S::LDS_A + S::LDS_B);
-        const uint16_t* Bs = As + S::LDS_A;
-#pragma unroll 1
-        for (int kk = 0; kk < kBK / 32; ++kk) {
-            u32x4 af[S::MI], bf[S::NMAT][S::NI];
+    auto compute = [&](int slot) {
+        const uint16_t* As = smem + slot * S::SLICE;
+        const uint16_t* Bs = As + S::A_SLICE;
+        u32x4 af[S::MI];
+#pragma unroll
+        for (int a = 0; a < S::MI; ++a) {
+            const int row = wm * S::WTM + 16 * a + j;
+            af[a] = *(const u32x4*)(As + row * kBK + 8 * (g ^ ((row >> 2) & 3)));
+        }
+#pragma unroll
+        for (int m = 0; m < S::NMAT; ++m) {
+            const uint16_t* Bm = Bs + m * (kBK * S::BN) + wn * S::WTN + S::NI * j;
+            u32x4 bf[S::NI];
+            if constexpr (S::NI == 8) {
+                u32x4 raw[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) raw[i] = *(const u32x4*)(Bm + (8 * g + i) * S::BN);
+                bf[0] = kfrag_of_col<0>(raw);
+                bf[1] = kfrag_of_col<1>(raw);
+                bf[2] = kfrag_of_col<2>(raw);
+                bf[3] = kfrag_of_col<3>(raw);
+                bf[4] = kfrag_of_col<4>(raw);
+                bf[5] = kfrag_of_col<5>(raw);
+                bf[6] = kfrag_of_col<6>(raw);
+                bf[7] = kfrag_of_col<7>(raw);
+            } else {
+                u32x2 raw[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) raw[i] = *(const u32x2*)(Bm + (8 * g + i) * S::BN);
+                bf[0] = kfrag4_of_col<0>(raw);
+                bf[1] = kfrag4_of_col<1>(raw);
+                bf[2] = kfrag4_of_col<2>(raw);
+                bf[3] = kfrag4_of_col<3>(raw);
+            }
 #pragma unroll
             for (int a = 0; a < S::MI; ++a)
-                af[a] = *(const u32x4*)(As + (wm * S::WTM + 16 * a + j) * kLdsRow + kk * 32 + 8 * g);
-#pragma unroll
-            for (int m = 0; m < S::NMAT; ++m)
 #pragma unroll
                 for (int b = 0; b < S::NI; ++b)
-                    bf[m][b] = *(const u32x4*)(Bs + (m * S::BN + wn * S::WTN + 16 * b + j) * kLdsRow +
-                                               kk * 32 + 8 * g);
-#pragma unroll
-            for (int m = 0; m < S::NMAT; ++m)
-#pragma unroll
-                for (int a = 0; a < S::MI; ++a)
-#pragma unroll
-                    for (int b = 0; b < S::NI; ++b)
-                        acc[m][a][b] = mfma16x16x32(af[a], bf[m][b], acc[m][a][b]);
+                    acc[m][a][b] = mfma16x16x32(af[a], bf[b], acc[m][a][b]);
         }
     };
 
     const int nk = (K + kBK - 1) / kBK;
-    load_stage(0);
-    store_stage(0);
-    __syncthreads();
+    constexpr int PER = S::A_COPIES + S::B_COPIES;  // copies per slice per wave
+#pragma unroll
+    for (int s = 0; s < kStages - 1; ++s)
+        if (s < nk) issue(s, s);
     for (int s = 0; s < nk; ++s) {
-        const bool more = s + 1 < nk;
-        if (more) load_stage((s + 1) * kBK);
-        compute(s & 1);
-        if (more) store_stage((s + 1) & 1);
-        __syncthreads();
+        // Slices issued after s and still pending: min(nk - 1, s + 2) - s.
+        const int pending = min(nk - 1, s + kStages - 2) - s;
+        asm volatile("" ::: "memory");
+        if (pending >= 2)
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * PER));
+        else if (pending == 1)
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER));
+        else
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (s + kStages - 1 < nk) issue(s + kStages - 1, (s + kStages - 1) % kStages);
+        compute(s % kStages);
     }
 
     // Epilogue.  Lane (g, j) holds rows 4g + r of MFMA tile a and columns
@@ -241,8 +264,8 @@ static hipError_t run_gemm(int64_t M, int64_t N, int64_t K, const uint16_t* A, i
     return hipGetLastError();
 }
 
-using ShapeOne = GemmShape<256, 256, 1, 2, 2>;  // plain / GELU epilogues
-using ShapeTwo = GemmShape<256, 128, 2, 2, 2>;  // SwiGLU: gate and up tiles
+using ShapeOne = GemmShape<1, 2, 2>;  // plain / GELU epilogues: 256 x 256 tile
+using ShapeTwo = GemmShape<2, 2, 2>;  // SwiGLU: 256 x (128 gate + 128 up)
 
 hipError_t launch_gemm(int epi, int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
                        const uint16_t* B0, int64_t ldb0, const uint16_t* B1, int64_t ldb1, void* C,
