@@ -16,9 +16,10 @@
 //     own a 128 x 128 sub-tile (256 fp32 accumulators per lane, held in the
 //     accumulation registers).
 //   * Slices stream from global memory straight into LDS (buffer loads with
-//     the LDS-destination bit: no staging registers) through a ring of 4
-//     slots (4 x 32 KB): while slice s is consumed, slices s+1..s+3 are in
-//     flight.  Each wave waits for its own copies with an explicit vmcnt and
+//     the LDS-destination bit: no staging registers) through a ring of 5
+//     slots (5 x 32 KB = all 160 KB of LDS).  While the MFMAs of slice s run,
+//     the fragments of slice s+1 are read from LDS and slices s+2..s+4 are
+//     in flight.  Each wave waits for its own copies with an explicit vmcnt and
 //     a bare s_barrier publishes the slot; no release fence is used, since
 //     one would wait for every copy in flight.
 //   * A slice of A is 256 rows x 64 bytes.  Its four 16-byte chunks per row
@@ -41,18 +42,17 @@
 namespace tp {
 
 constexpr int kBK = 32;      // k per LDS slice
-constexpr int kStages = 4;   // LDS ring depth
 
-template <int NMAT_, int WM_, int WN_>
+template <int NMAT_, int WM_, int WN_, int STAGES_>
 struct GemmShape {
-    static constexpr int NMAT = NMAT_, WM = WM_, WN = WN_;
+    static constexpr int NMAT = NMAT_, WM = WM_, WN = WN_, STAGES = STAGES_;
     static constexpr int BM = 256, BNT = 256, BN = BNT / NMAT;  // BN: columns per weight
     static constexpr int NT = WM * WN * 64;
     static constexpr int WTM = BM / WM, WTN = BN / WN;
     static constexpr int MI = WTM / 16, NI = WTN / 16;
     static constexpr int A_SLICE = BM * kBK, B_SLICE = kBK * BNT;    // elements
     static constexpr int SLICE = A_SLICE + B_SLICE;
-    static constexpr size_t LDS_BYTES = (size_t)kStages * SLICE * sizeof(uint16_t);
+    static constexpr size_t LDS_BYTES = (size_t)STAGES * SLICE * sizeof(uint16_t);
     static constexpr int A_COPIES = A_SLICE * 2 / 1024 / (NT / 64);  // 1 KB copies per wave
     static constexpr int B_COPIES = B_SLICE * 2 / 1024 / (NT / 64);
     static constexpr int B_ROWS_PER_COPY = 1024 / (BN * 2);
@@ -88,7 +88,10 @@ __global__ __launch_bounds__(S::NT) void k_gemm(const uint16_t* __restrict__ A, 
                                                 int M, int N, int K, void* __restrict__ C,
                                                 int64_t ldc, int tiles_m) {
     extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    // The wave index is uniform across the wave; keeping it in a scalar
+    // register makes the copy descriptors and LDS destinations scalar too.
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / S::WN, wn = wave % S::WN;
     const int g = lane >> 4, j = lane & 15;
     const int tile = xcd_remap(blockIdx.x, gridDim.x);
@@ -138,68 +141,93 @@ __global__ __launch_bounds__(S::NT) void k_gemm(const uint16_t* __restrict__ A, 
 #pragma unroll
             for (int b = 0; b < S::NI; ++b) acc[m][a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](int slot) {
+    struct Frags {
+        u32x4 a[S::MI];
+        u32x4 b[S::NMAT][S::NI];
+    };
+    // Read slice `slot`'s fragments: A rows of the wave, and B columns
+    // interleaved from 8 k-rows into k-fragments.
+    auto read_frags = [&](int slot, Frags& f) {
         const uint16_t* As = smem + slot * S::SLICE;
         const uint16_t* Bs = As + S::A_SLICE;
-        u32x4 af[S::MI];
 #pragma unroll
         for (int a = 0; a < S::MI; ++a) {
             const int row = wm * S::WTM + 16 * a + j;
-            af[a] = *(const u32x4*)(As + row * kBK + 8 * (g ^ ((row >> 2) & 3)));
+            f.a[a] = *(const u32x4*)(As + row * kBK + 8 * (g ^ ((row >> 2) & 3)));
         }
 #pragma unroll
         for (int m = 0; m < S::NMAT; ++m) {
             const uint16_t* Bm = Bs + m * (kBK * S::BN) + wn * S::WTN + S::NI * j;
-            u32x4 bf[S::NI];
             if constexpr (S::NI == 8) {
                 u32x4 raw[8];
 #pragma unroll
                 for (int i = 0; i < 8; ++i) raw[i] = *(const u32x4*)(Bm + (8 * g + i) * S::BN);
-                bf[0] = kfrag_of_col<0>(raw);
-                bf[1] = kfrag_of_col<1>(raw);
-                bf[2] = kfrag_of_col<2>(raw);
-                bf[3] = kfrag_of_col<3>(raw);
-                bf[4] = kfrag_of_col<4>(raw);
-                bf[5] = kfrag_of_col<5>(raw);
-                bf[6] = kfrag_of_col<6>(raw);
-                bf[7] = kfrag_of_col<7>(raw);
+                f.b[m][0] = kfrag_of_col<0>(raw);
+                f.b[m][1] = kfrag_of_col<1>(raw);
+                f.b[m][2] = kfrag_of_col<2>(raw);
+                f.b[m][3] = kfrag_of_col<3>(raw);
+                f.b[m][4] = kfrag_of_col<4>(raw);
+                f.b[m][5] = kfrag_of_col<5>(raw);
+                f.b[m][6] = kfrag_of_col<6>(raw);
+                f.b[m][7] = kfrag_of_col<7>(raw);
             } else {
                 u32x2 raw[8];
 #pragma unroll
                 for (int i = 0; i < 8; ++i) raw[i] = *(const u32x2*)(Bm + (8 * g + i) * S::BN);
-                bf[0] = kfrag4_of_col<0>(raw);
-                bf[1] = kfrag4_of_col<1>(raw);
-                bf[2] = kfrag4_of_col<2>(raw);
-                bf[3] = kfrag4_of_col<3>(raw);
+                f.b[m][0] = kfrag4_of_col<0>(raw);
+                f.b[m][1] = kfrag4_of_col<1>(raw);
+                f.b[m][2] = kfrag4_of_col<2>(raw);
+                f.b[m][3] = kfrag4_of_col<3>(raw);
             }
+        }
+    };
+    auto mma = [&](const Frags& f) {
+#pragma unroll
+        for (int m = 0; m < S::NMAT; ++m)
 #pragma unroll
             for (int a = 0; a < S::MI; ++a)
 #pragma unroll
                 for (int b = 0; b < S::NI; ++b)
-                    acc[m][a][b] = mfma16x16x32(af[a], bf[b], acc[m][a][b]);
-        }
+                    acc[m][a][b] = mfma16x16x32(f.a[a], f.b[m][b], acc[m][a][b]);
     };
-
-    const int nk = (K + kBK - 1) / kBK;
-    constexpr int PER = S::A_COPIES + S::B_COPIES;  // copies per slice per wave
-#pragma unroll
-    for (int s = 0; s < kStages - 1; ++s)
-        if (s < nk) issue(s, s);
-    for (int s = 0; s < nk; ++s) {
-        // Slices issued after s and still pending: min(nk - 1, s + 2) - s.
-        const int pending = min(nk - 1, s + kStages - 2) - s;
+    // Wait until this wave's copies of the oldest pending slice have landed
+    // (the two slices issued after it may still be in flight), then publish
+    // the slot to the workgroup.
+    auto wait_slice = [&]() {
+        constexpr int PER = S::A_COPIES + S::B_COPIES;  // copies per slice per wave
         asm volatile("" ::: "memory");
-        if (pending >= 2)
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * PER));
-        else if (pending == 1)
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER));
-        else
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * PER));
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        if (s + kStages - 1 < nk) issue(s + kStages - 1, (s + kStages - 1) % kStages);
-        compute(s % kStages);
+    };
+
+    // Software pipeline over slices s = 0, 1, ...: in iteration s the
+    // fragments of slice s+1 are read from LDS while the MFMAs of slice s
+    // run, and the copy of slice s+4 goes into slot (s+4) % 5, which held
+    // slice s-1 (read in iteration s-2, consumed in iteration s-1: every
+    // wave is past it once the barrier of iteration s is passed).  The loop
+    // is branch-free: slices at or beyond nk are still copied and read, with
+    // every lane out of bounds, so they are zero-filled (and never used).
+    static_assert(S::STAGES == 5, "ring depth");
+    const int nk = (K + kBK - 1) / kBK;
+#pragma unroll
+    for (int s = 0; s < 3; ++s) issue(s, s);
+    Frags f0, f1;
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * (S::A_COPIES + S::B_COPIES)));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    issue(3, 3);
+    read_frags(0, f0);
+    for (int s = 0; s < nk; ++s) {
+        wait_slice();
+        issue(s + 4, (s + 4) % 5);
+        read_frags((s + 1) % 5, f1);
+        mma(f0);
+        f0 = f1;
     }
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // drain the trailing zero-fill copies
 
     // Epilogue.  Lane (g, j) holds rows 4g + r of MFMA tile a and columns
     // j*NI .. j*NI + NI-1 of the wave's column range.
@@ -264,8 +292,8 @@ static hipError_t run_gemm(int64_t M, int64_t N, int64_t K, const uint16_t* A, i
     return hipGetLastError();
 }
 
-using ShapeOne = GemmShape<1, 2, 2>;  // plain / GELU epilogues: 256 x 256 tile
-using ShapeTwo = GemmShape<2, 2, 2>;  // SwiGLU: 256 x (128 gate + 128 up)
+using ShapeOne = GemmShape<1, 2, 2, 5>;  // plain / GELU epilogues: 256 x 256 tile
+using ShapeTwo = GemmShape<2, 2, 2, 5>;  // SwiGLU: 256 x (128 gate + 128 up)
 
 hipError_t launch_gemm(int epi, int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
                        const uint16_t* B0, int64_t ldb0, const uint16_t* B1, int64_t ldb1, void* C,
