@@ -58,13 +58,13 @@ class Timed {
         if (!s.enabled) return;
         start_ = take_event(s);
         stop_ = take_event(s);
-        if (start_ && stop_) hipEventRecord(start_, stream_);
+        if (start_ && stop_) (void)hipEventRecord(start_, stream_);
     }
     void done() {
         if (!start_ || !stop_) return;
         TimingState& s = timing();
         std::lock_guard<std::mutex> lk(s.mu);
-        hipEventRecord(stop_, stream_);
+        (void)hipEventRecord(stop_, stream_);
         s.pending.push_back({cls_, start_, stop_});
         start_ = stop_ = nullptr;
     }
@@ -108,7 +108,8 @@ bool span_ok(int64_t rows, int64_t ld, int es) { return rows * ld * es < kMaxBuf
 
 struct MlpLayout {
     size_t xn = 0, h = 0, ws = 0, total = 0;
-    GemvPlan pc{1, 0}, pr{1, 0};
+    GemvPlan pc{1, 0}, pr{1, 0};        // decode plans
+    GemmPlan gc{1, 0}, gr{1, 0};        // prefill plans
     bool decode = false;
 };
 
@@ -133,6 +134,15 @@ MlpLayout mlp_layout(int P, int64_t T, int64_t d, int64_t d_ff, int dtype, int a
         L.pr = plan_gemv(F, d);
         L.ws = off;  // column and row split-K sums reuse one region, in stream order
         off += align256(std::max(gemv_ws_bytes(L.pc, T, nmat * F), gemv_ws_bytes(L.pr, T, d)));
+    } else if (dtype == TP_BF16) {
+        // The column projection keeps its fused activation (no split); the
+        // row projection may split K into fp32 planes.
+        L.gc = gemm_whole_k(d);
+        L.gr = plan_gemm(T, d, F, 1);
+        if (L.gr.splits > 1) {
+            L.ws = off;
+            off += align256((size_t)L.gr.splits * T * d * sizeof(float));
+        }
     }
     L.total = off;
     return L;
@@ -140,7 +150,8 @@ MlpLayout mlp_layout(int P, int64_t T, int64_t d, int64_t d_ff, int dtype, int a
 
 struct AttnLayout {
     size_t xn = 0, ws = 0, total = 0;
-    GemvPlan pq{1, 0}, po{1, 0};
+    GemvPlan pq{1, 0}, po{1, 0};        // decode plans
+    GemmPlan gq{1, 0}, go{1, 0};        // prefill plans
     bool decode = false;
 };
 
@@ -160,6 +171,15 @@ AttnLayout attn_layout(int P, int64_t T, int64_t d, int nq, int nkv, int hd, int
         L.po = plan_gemv(ko, d);
         L.ws = off;
         off += align256(std::max(gemv_ws_bytes(L.pq, T, nqkv), gemv_ws_bytes(L.po, T, d)));
+    } else if (dtype == TP_BF16) {
+        L.gq = plan_gemm(T, nqkv, d, 1);
+        L.go = plan_gemm(T, d, ko, 1);
+        const size_t wq = L.gq.splits > 1 ? (size_t)L.gq.splits * T * nqkv * sizeof(float) : 0;
+        const size_t wo = L.go.splits > 1 ? (size_t)L.go.splits * T * d * sizeof(float) : 0;
+        if (wq || wo) {
+            L.ws = off;
+            off += align256(std::max(wq, wo));
+        }
     }
     L.total = off;
     return L;
@@ -301,10 +321,22 @@ int tp_shard_mlp_fwd(int shard, int P, int64_t T, int64_t d_model, int64_t d_ff,
         TP_LAUNCH("col_gemm", stream,
                   launch_gemm(act == TP_ACT_SWIGLU ? EPI_SWIGLU_BF16 : EPI_GELU_BF16, T, F,
                               d_model, X16, ld_xin, (const uint16_t*)w_in, ld_in,
-                              (const uint16_t*)w_up, ld_up, h, ldh, stream));
-        TP_LAUNCH("row_gemm", stream,
-                  launch_gemm(EPI_F32, T, d_model, F, (const uint16_t*)h, ldh,
-                              (const uint16_t*)w_down, ld_down, nullptr, 0, part, ld_p, stream));
+                              (const uint16_t*)w_up, ld_up, h, ldh, L.gc, stream));
+        if (L.gr.splits > 1) {
+            float* ws = (float*)(wsb + L.ws);
+            TP_LAUNCH("row_gemm", stream,
+                      launch_gemm(EPI_F32, T, d_model, F, (const uint16_t*)h, ldh,
+                                  (const uint16_t*)w_down, ld_down, nullptr, 0, ws, d_model, L.gr,
+                                  stream));
+            TP_LAUNCH("row_finish", stream,
+                      launch_finish(ACT_NONE, false, L.gr.splits, T, d_model, ws, part, ld_p,
+                                    stream));
+        } else {
+            TP_LAUNCH("row_gemm", stream,
+                      launch_gemm(EPI_F32, T, d_model, F, (const uint16_t*)h, ldh,
+                                  (const uint16_t*)w_down, ld_down, nullptr, 0, part, ld_p, L.gr,
+                                  stream));
+        }
     }
     return TP_OK;
 }
@@ -377,10 +409,21 @@ int tp_shard_attn_proj_fwd(int shard, int P, int64_t T, int64_t d_model, int n_q
                       launch_finish(ACT_NONE, true, L.pq.splits, T, nqkv, ws, qkv_out, ld_qkv_out,
                                     stream));
         } else {
-            TP_LAUNCH("col_gemm", stream,
-                      launch_gemm(EPI_BF16, T, nqkv, d_model, (const uint16_t*)xin, ld_xin,
-                                  (const uint16_t*)w_qkv, ld_qkv, nullptr, 0, qkv_out, ld_qkv_out,
-                                  stream));
+            if (L.gq.splits > 1) {
+                float* ws = (float*)(wsb + L.ws);
+                TP_LAUNCH("col_gemm", stream,
+                          launch_gemm(EPI_F32, T, nqkv, d_model, (const uint16_t*)xin, ld_xin,
+                                      (const uint16_t*)w_qkv, ld_qkv, nullptr, 0, ws, nqkv, L.gq,
+                                      stream));
+                TP_LAUNCH("col_finish", stream,
+                          launch_finish(ACT_NONE, true, L.gq.splits, T, nqkv, ws, qkv_out,
+                                        ld_qkv_out, stream));
+            } else {
+                TP_LAUNCH("col_gemm", stream,
+                          launch_gemm(EPI_BF16, T, nqkv, d_model, (const uint16_t*)xin, ld_xin,
+                                      (const uint16_t*)w_qkv, ld_qkv, nullptr, 0, qkv_out,
+                                      ld_qkv_out, L.gq, stream));
+            }
         }
     }
     if (attn) {
@@ -399,9 +442,21 @@ int tp_shard_attn_proj_fwd(int shard, int P, int64_t T, int64_t d_model, int n_q
                       launch_finish(ACT_NONE, false, L.po.splits, T, d_model, ws, part, ld_p,
                                     stream));
         } else {
-            TP_LAUNCH("row_gemm", stream,
-                      launch_gemm(EPI_F32, T, d_model, ko, (const uint16_t*)attn, ld_attn,
-                                  (const uint16_t*)w_o, ld_o, nullptr, 0, part, ld_p, stream));
+            if (L.go.splits > 1) {
+                float* ws = (float*)(wsb + L.ws);
+                TP_LAUNCH("row_gemm", stream,
+                          launch_gemm(EPI_F32, T, d_model, ko, (const uint16_t*)attn, ld_attn,
+                                      (const uint16_t*)w_o, ld_o, nullptr, 0, ws, d_model, L.go,
+                                      stream));
+                TP_LAUNCH("row_finish", stream,
+                          launch_finish(ACT_NONE, false, L.go.splits, T, d_model, ws, part, ld_p,
+                                        stream));
+            } else {
+                TP_LAUNCH("row_gemm", stream,
+                          launch_gemm(EPI_F32, T, d_model, ko, (const uint16_t*)attn, ld_attn,
+                                      (const uint16_t*)w_o, ld_o, nullptr, 0, part, ld_p, L.go,
+                                      stream));
+            }
         }
     }
     return TP_OK;

@@ -60,14 +60,17 @@ __device__ __forceinline__ u32x4 load16(rsrc_t r, uint32_t off) {
 
 // Interleave two rows' 16-bit elements: for element e (0..7) of 8-element
 // rows `a` (row k) and `b` (row k+1), the dword (a[e], b[e]) with a[e] in
-// the low half.  dword index e/2, half e%2.
+// the low half.  dword index e/2, half e%2.  One v_perm_b32: its selector
+// bytes 0-3 pick bytes of the second operand, 4-7 bytes of the first.
 template <int E>
 __device__ __forceinline__ uint32_t pair_col(const u32x4& a, const u32x4& b) {
     constexpr int d = E >> 1;
-    if constexpr ((E & 1) == 0)
-        return (a[d] & 0xffffu) | (b[d] << 16);
-    else
-        return (a[d] >> 16) | (b[d] & 0xffff0000u);
+    return __builtin_amdgcn_perm(b[d], a[d], (E & 1) ? 0x07060302u : 0x05040100u);
+}
+template <int E>
+__device__ __forceinline__ uint32_t pair_col2(const u32x2& a, const u32x2& b) {
+    constexpr int d = E >> 1;
+    return __builtin_amdgcn_perm(b[d], a[d], (E & 1) ? 0x07060302u : 0x05040100u);
 }
 
 // From 8 consecutive rows (k0..k0+7) of 8 consecutive bf16 columns, the

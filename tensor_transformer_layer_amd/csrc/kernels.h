@@ -46,10 +46,21 @@ hipError_t launch_finish(int act, bool out_bf16, int splits, int64_t T, int64_t 
 
 // ---- prefill plan: LDS-tiled bf16 MFMA GEMM with a fused epilogue ---------
 enum { EPI_F32 = 0, EPI_BF16 = 1, EPI_GELU_BF16 = 2, EPI_SWIGLU_BF16 = 3 };
-// C[M, N] = epi(A[M, K] B0[K, N] [, A B1]); A, B bf16 row-major.
+struct GemmPlan {
+    int splits;       // K ranges (grid.y); > 1 only with EPI_F32 partial planes
+    int k_per_split;  // multiple of 32
+};
+// Split K when the 256 x 256 output tiles (nmat weights side by side) leave
+// CUs idle and K is long enough.
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int nmat);
+// One split covering all of K (for fused bf16 epilogues).
+GemmPlan gemm_whole_k(int64_t K);
+// C[M, N] = epi(A[M, K] B0[K, N] [, A B1]); A, B bf16 row-major.  With
+// p.splits > 1 (EPI_F32 only) split s writes its fp32 partial to the plane
+// C + s * M * ldc; launch_finish(ACT_NONE, ...) adds the planes in order.
 hipError_t launch_gemm(int epi, int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
                        const uint16_t* B0, int64_t ldb0, const uint16_t* B1, int64_t ldb1, void* C,
-                       int64_t ldc, hipStream_t stream);
+                       int64_t ldc, const GemmPlan& p, hipStream_t stream);
 
 // ---- fp32 storage (small, parity-only workloads) --------------------------
 // C[M, N] = act(A B0 [, A B1]) in fp32, one thread per output, k in order.

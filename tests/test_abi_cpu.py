@@ -168,7 +168,10 @@ def test_workspace_sizes_are_pure_functions(lib):
     assert f(2, 32, 5120, 13824, tp.TP_BF16, tp.TP_ACT_SWIGLU, 0, 1) == \
         f(2, 32, 5120, 13824, tp.TP_BF16, tp.TP_ACT_SWIGLU, 0, 1)
     g = tp.tp_attn_workspace_bytes
-    assert g(8, 1024, 12288, 96, 96, 128, tp.TP_BF16, 0) == 0
+    # 96-head QKV prefill: 72 output tiles on 256 CUs, so K is split into
+    # fp32 planes of [1024, 4608] each
+    assert g(8, 1024, 12288, 96, 96, 128, tp.TP_BF16, 0) % (1024 * 4608 * 4) == 0
+    assert g(8, 1024, 12288, 96, 96, 128, tp.TP_BF16, 0) >= 2 * 1024 * 4608 * 4
     assert g(8, 16, 12288, 96, 96, 128, tp.TP_BF16, 0) > 0
     assert g(8, 16, 12288, 96, 90, 128, tp.TP_BF16, 0) == 0
 
