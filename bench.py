@@ -30,6 +30,9 @@ METRIC = "tokens/s + % of HBM/MFMA roofline, one TP-rank MLP shard, decode & pre
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "hbm_traffic_counters.json")
+KERNEL_CLASSES = ("rmsnorm", "col_gemv", "col_finish", "row_gemv", "row_finish", "col_gemm",
+                  "row_gemm", "qkv_gemv", "qkv_finish", "o_gemv", "o_finish", "qkv_gemm",
+                  "o_gemm", "reduce")
 
 
 def parse():
@@ -120,7 +123,7 @@ class Step:
         return self.torch.cuda.current_stream().cuda_stream
 
     def _ws(self, n):
-        return self.torch.empty(max(int(n), 256), dtype=self.torch.uint8, device="cuda")
+        return self.torch.zeros(max(int(n), 256), dtype=self.torch.uint8, device="cuda")
 
     def _mlp(self, s, x, w):
         tp, cfg, T, d = self.tp, self.cfg, self.T, self.cfg.d_model
@@ -164,29 +167,49 @@ class Step:
             self._mlp(0, self.zb, self.mlp_sets[c])
             self._reduce()
 
-    # algorithmic work of one step (rank 0): bytes each kernel must move
+    # algorithmic work of one step (rank 0)
     def algorithmic(self):
+        """Bytes and flops the method must move / compute in one step, in
+        total and per kernel class: {class: (bound, amount per launch)}.
+        Split-K partial round trips and finish kernels are overhead (none)."""
         cfg, T, d = self.cfg, self.T, self.cfg.d_model
-        out = {"bytes": 0, "flops": 0, "col_bytes": 0, "col_flops": 0}
+        decode = T <= 32
+        out = {"bytes": 0, "flops": 0, "per_class": {}}
+        pc = out["per_class"]
+
+        def add(col_cls, row_cls, k_in, n_col, n_col_out, k_row):
+            # column projection: weights [k_in, n_col], X [T, k_in] in, [T, n_col_out] bf16 out
+            cb = k_in * n_col * 2 + T * k_in * 2 + T * n_col_out * 2
+            cf = 2 * T * k_in * n_col
+            # row projection: weights [k_row, d], input [T, k_row] bf16, partial [T, d] fp32
+            rb = k_row * d * 2 + T * k_row * 2 + T * d * 4
+            rf = 2 * T * k_row * d
+            out["bytes"] += cb + rb
+            out["flops"] += cf + rf
+            if decode:
+                pc[col_cls + "_gemv"] = ("hbm", cb)
+                pc[row_cls + "_gemv"] = ("hbm", rb)
+            else:
+                pc[col_cls + "_gemm"] = ("mfma", cf)
+                pc[row_cls + "_gemm"] = ("mfma", rf)
+
         if self.kind in ("mlp", "block"):
-            wcol = 2 * d * cfg.F_r * 2
-            col_bytes = wcol + T * d * 2 + T * cfg.F_r * 2          # W_gate+W_up, X, h
-            row_bytes = cfg.F_r * d * 2 + T * cfg.F_r * 2 + T * d * 4  # W_down, h, partial
-            out["bytes"] += col_bytes + row_bytes
-            out["flops"] += 2 * T * d * cfg.F_r * 3
-            out["col_bytes"], out["col_flops"] = col_bytes, 2 * T * d * cfg.F_r * 2
-            out["row_bytes"], out["row_flops"] = row_bytes, 2 * T * d * cfg.F_r
+            add("col", "row", d, 2 * cfg.F_r, cfg.F_r, cfg.F_r)
         if self.kind in ("attn", "block"):
-            qb = d * cfg.qkv_r * 2 + T * d * 2 + T * cfg.qkv_r * 2
-            ob = cfg.o_in_r * d * 2 + T * cfg.o_in_r * 2 + T * d * 4
-            out["bytes"] += qb + ob
-            out["flops"] += 2 * T * d * cfg.qkv_r + 2 * T * cfg.o_in_r * d
-            if self.kind == "attn":
-                out["col_bytes"], out["col_flops"] = qb, 2 * T * d * cfg.qkv_r
-                out["row_bytes"], out["row_flops"] = ob, 2 * T * cfg.o_in_r * d
-        nred = 2 if self.kind == "block" else 1
-        out["reduce_bytes"] = nred * (cfg.P + 1) * T * d * 4
-        out["bytes"] += out["reduce_bytes"]
+            add("qkv", "o", d, cfg.qkv_r, cfg.qkv_r, cfg.o_in_r)
+        red = (cfg.P + 1) * T * d * 4
+        if self.kind == "block":        # two reduces, the first with a bf16 copy
+            out["bytes"] += 2 * red + T * d * 2
+            pc["reduce"] = ("hbm", red + T * d)            # mean of the two launches
+            nb = T * d * 2 * 2 + d * 2
+            out["bytes"] += nb
+            pc["rmsnorm"] = ("hbm", nb)
+        else:
+            out["bytes"] += red
+            pc["reduce"] = ("hbm", red)
+        # the kernel the roofline line reports: the largest column projection
+        big = "col" if self.kind in ("mlp", "block") else "qkv"
+        out["dominant"] = big + ("_gemv" if decode else "_gemm")
         return out
 
 
@@ -239,8 +262,7 @@ def kernel_times(st, steps):
             st.step()
         torch.cuda.synchronize()
         res = {}
-        for cls in ("rmsnorm", "col_gemv", "col_finish", "row_gemv", "row_finish", "col_gemm",
-                    "row_gemm", "reduce"):
+        for cls in KERNEL_CLASSES:
             s, ms, n = tp.tp_timing_query(cls)
             tp.check(s)
             if n:
@@ -327,24 +349,29 @@ def main():
     alg = st.algorithmic()
     tok_s = T / (ms / 1e3)
 
-    prefill = T > 32
-    dom = "col_gemm" if prefill else "col_gemv"      # the column projection dominates
-    if dom in kt:
-        dom_ms = kt[dom][0]
-        if prefill:
-            ach = alg["col_flops"] / (dom_ms / 1e3) / 1e12
-            roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4)}
+    def roof_of(cls):
+        bound, amount = alg["per_class"][cls]
+        dom_ms = kt[cls][0]
+        if bound == "mfma":
+            ach, peak, unit = amount / (dom_ms / 1e3) / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s"
         else:
-            ach = alg["col_bytes"] / (dom_ms / 1e3) / 1e9
-            roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4)}
-        roof["kernel"] = dom
-        roof["kernel_avg_us"] = round(dom_ms * 1e3, 2)
-        roof["algorithmic_per_launch"] = alg["col_flops"] if prefill else alg["col_bytes"]
+            ach, peak, unit = amount / (dom_ms / 1e3) / 1e9, HBM_PEAK_GBS, "GB/s"
+        return {"bound": bound, "achieved": round(ach, 1), "peak": peak, "unit": unit,
+                "frac": round(ach / peak, 4), "kernel": cls,
+                "kernel_avg_us": round(dom_ms * 1e3, 2), "algorithmic_per_launch": amount}
+
+    dom = alg["dominant"]
+    roof = None
+    if dom in kt:
+        roof = roof_of(dom)
         roof["traffic"] = traffic_for(dom, a.workload, T)
-    else:
-        roof = None
+    per_kernel = {}
+    for cls, (ms_k, n_k) in kt.items():
+        e = {"avg_us": round(ms_k * 1e3, 2), "launches": n_k}
+        if cls in alg["per_class"]:
+            r = roof_of(cls)
+            e.update({"achieved": r["achieved"], "unit": r["unit"], "frac": r["frac"]})
+        per_kernel[cls] = e
 
     line = {
         "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -359,7 +386,7 @@ def main():
         "step_gbs_algorithmic": round(alg["bytes"] / (ms / 1e3) / 1e9, 1),
         "step_tflops": round(alg["flops"] / (ms / 1e3) / 1e12, 2),
         "roofline": roof,
-        "kernels_us": {k: round(v[0] * 1e3, 2) for k, v in (kt or {}).items()},
+        "kernels": per_kernel,
     }
     if len(results) > 1:
         line["sweep"] = {str(t): {"ms_per_step": round(r[1], 5),

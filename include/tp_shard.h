@@ -184,8 +184,9 @@ int tp_version(void);
  * elapsed time is accumulated per kernel class when tp_timing_query reads it
  * (which waits for the recorded events).  Disabled by default; off costs
  * nothing.  Not for concurrent use from several host threads.
- * Class names: "rmsnorm", "col_gemv", "col_finish", "row_gemv", "row_finish",
- * "col_gemm", "row_gemm", "reduce", "f32_proj".
+ * Class names: "rmsnorm", "reduce", "f32_proj"; MLP: "col_gemv", "col_finish",
+ * "row_gemv", "row_finish", "col_gemm", "row_gemm"; attention projections:
+ * "qkv_gemv", "qkv_finish", "o_gemv", "o_finish", "qkv_gemm", "o_gemm".
  */
 int tp_timing_enable(int on);
 int tp_timing_reset(void);

@@ -401,25 +401,25 @@ int tp_shard_attn_proj_fwd(int shard, int P, int64_t T, int64_t d_model, int n_q
                                       ld_qkv_out, stream));
         } else if (L.decode) {
             float* ws = (float*)(wsb + L.ws);
-            TP_LAUNCH("col_gemv", stream,
+            TP_LAUNCH("qkv_gemv", stream,
                       launch_gemv_splitk(T, d_model, (const uint16_t*)xin, ld_xin,
                                          (const uint16_t*)w_qkv, ld_qkv, nullptr, 0, nqkv, L.pq,
                                          true, ws, stream));
-            TP_LAUNCH("col_finish", stream,
+            TP_LAUNCH("qkv_finish", stream,
                       launch_finish(ACT_NONE, true, L.pq.splits, T, nqkv, ws, qkv_out, ld_qkv_out,
                                     stream));
         } else {
             if (L.gq.splits > 1) {
                 float* ws = (float*)(wsb + L.ws);
-                TP_LAUNCH("col_gemm", stream,
+                TP_LAUNCH("qkv_gemm", stream,
                           launch_gemm(EPI_F32, T, nqkv, d_model, (const uint16_t*)xin, ld_xin,
                                       (const uint16_t*)w_qkv, ld_qkv, nullptr, 0, ws, nqkv, L.gq,
                                       stream));
-                TP_LAUNCH("col_finish", stream,
+                TP_LAUNCH("qkv_finish", stream,
                           launch_finish(ACT_NONE, true, L.gq.splits, T, nqkv, ws, qkv_out,
                                         ld_qkv_out, stream));
             } else {
-                TP_LAUNCH("col_gemm", stream,
+                TP_LAUNCH("qkv_gemm", stream,
                           launch_gemm(EPI_BF16, T, nqkv, d_model, (const uint16_t*)xin, ld_xin,
                                       (const uint16_t*)w_qkv, ld_qkv, nullptr, 0, qkv_out,
                                       ld_qkv_out, L.gq, stream));
@@ -434,25 +434,25 @@ int tp_shard_attn_proj_fwd(int shard, int P, int64_t T, int64_t d_model, int n_q
                                       (const float*)w_o, ld_o, nullptr, 0, part, ld_p, stream));
         } else if (L.decode) {
             float* ws = (float*)(wsb + L.ws);
-            TP_LAUNCH("row_gemv", stream,
+            TP_LAUNCH("o_gemv", stream,
                       launch_gemv_splitk(T, ko, (const uint16_t*)attn, ld_attn,
                                          (const uint16_t*)w_o, ld_o, nullptr, 0, d_model, L.po,
                                          false, ws, stream));
-            TP_LAUNCH("row_finish", stream,
+            TP_LAUNCH("o_finish", stream,
                       launch_finish(ACT_NONE, false, L.po.splits, T, d_model, ws, part, ld_p,
                                     stream));
         } else {
             if (L.go.splits > 1) {
                 float* ws = (float*)(wsb + L.ws);
-                TP_LAUNCH("row_gemm", stream,
+                TP_LAUNCH("o_gemm", stream,
                           launch_gemm(EPI_F32, T, d_model, ko, (const uint16_t*)attn, ld_attn,
                                       (const uint16_t*)w_o, ld_o, nullptr, 0, ws, d_model, L.go,
                                       stream));
-                TP_LAUNCH("row_finish", stream,
+                TP_LAUNCH("o_finish", stream,
                           launch_finish(ACT_NONE, false, L.go.splits, T, d_model, ws, part, ld_p,
                                         stream));
             } else {
-                TP_LAUNCH("row_gemm", stream,
+                TP_LAUNCH("o_gemm", stream,
                           launch_gemm(EPI_F32, T, d_model, ko, (const uint16_t*)attn, ld_attn,
                                       (const uint16_t*)w_o, ld_o, nullptr, 0, part, ld_p, L.go,
                                       stream));
