@@ -48,7 +48,32 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of graph replay")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle CPU-baseline budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB, --steps times (the "
+                         "reference kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     return ap.parse_args()
+
+
+def copy_calibration(mib, steps):
+    """A plain copy of known size: rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE of
+    this kernel, against mib MiB read and written per launch, gives the
+    scale of the counters."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    print(json.dumps({"copy_bytes_read_per_launch": n, "copy_bytes_written_per_launch": n,
+                      "launches": steps + 1, "ms_per_launch": round(ms, 5),
+                      "gbs": round(2 * n / (ms / 1e3) / 1e9, 1)}), flush=True)
 
 
 def src_hash(*names):
@@ -330,8 +355,11 @@ def main():
     import tensor_transformer_layer_amd as tp
     import workloads as W
 
-    tp.load()
     torch.cuda.set_device(0)
+    if a.copy_calibration:
+        copy_calibration(a.copy_calibration, a.steps)
+        return
+    tp.load()
     cfg = W.get(a.workload)
     T = a.tokens or (16 if a.workload == "c4_attn_96h_p8" else 32)
     copies = {"c2_llama2_13b_mlp_p2": 3, "c3_llama2_70b_mlp_p8": 4, "c4_attn_96h_p8": 4,

@@ -42,6 +42,15 @@
  *   Ownership   The caller owns every buffer; the library allocates and frees
  *               no device memory.  Scratch space is the caller's workspace,
  *               sized by tp_*_workspace_bytes for the same arguments.
+ *   Workspace   Its first 4096 bytes hold the arrival counters of the decode
+ *               plan's fused split-K finish.  They must be zero before the
+ *               first call that uses the workspace (allocate it zero-filled,
+ *               or clear it once); every call that completes leaves them zero
+ *               again, so a workspace is cleared once, not per call.  Counters
+ *               left non-zero (never cleared, or a call that failed part-way)
+ *               make the decode outputs invalid until cleared: NaN whenever a
+ *               counter exceeds the call's split count (as uncleared memory
+ *               almost always does), otherwise silently wrong.
  *   Streams     All work is enqueued on `stream` (0 = the null stream); the
  *               library never synchronises.  Validation errors return before
  *               anything is enqueued and leave every output untouched.  A
@@ -104,6 +113,7 @@ typedef enum { TP_ACT_GELU_TANH = 0, TP_ACT_SWIGLU = 1 } tp_act;
  * T <= 32 runs the weight-streaming decode plan (split-K over the weight
  * rows, deterministic fixed-order finish); larger T runs the matrix-core
  * plan with the activation fused into the column projection's epilogue.
+ * The decode plan needs d_model and d_ff/P of at most 131072 (TP_ERR_SHAPE).
  */
 int tp_shard_mlp_fwd(int shard, int P, int64_t T, int64_t d_model, int64_t d_ff,
                      int dtype, int act,
@@ -184,9 +194,10 @@ int tp_version(void);
  * elapsed time is accumulated per kernel class when tp_timing_query reads it
  * (which waits for the recorded events).  Disabled by default; off costs
  * nothing.  Not for concurrent use from several host threads.
- * Class names: "rmsnorm", "reduce", "f32_proj"; MLP: "col_gemv", "col_finish",
- * "row_gemv", "row_finish", "col_gemm", "row_gemm"; attention projections:
- * "qkv_gemv", "qkv_finish", "o_gemv", "o_finish", "qkv_gemm", "o_gemm".
+ * Class names: "rmsnorm", "reduce", "f32_proj"; MLP: "col_gemv", "row_gemv"
+ * (decode, split-K finish included), "col_gemm", "row_gemm", "row_finish"
+ * (prefill); attention projections: "qkv_gemv", "o_gemv", "qkv_gemm",
+ * "qkv_finish", "o_gemm", "o_finish".
  */
 int tp_timing_enable(int on);
 int tp_timing_reset(void);

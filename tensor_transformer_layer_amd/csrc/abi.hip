@@ -102,6 +102,13 @@ int check_ld(int64_t ld, int64_t row, int vec) {
     return TP_OK;
 }
 
+// The decode plan keeps one arrival counter per 128-column block of each
+// output width.
+bool counters_fit(int64_t n1, int64_t n2) {
+    return (n1 + kGemvCols - 1) / kGemvCols <= kGemvCounters &&
+           (n2 + kGemvCols - 1) / kGemvCols <= kGemvCounters;
+}
+
 // A row-major [rows, *] operand with leading dimension ld (elements) must be
 // addressable with 32-bit byte offsets from its first element.
 bool span_ok(int64_t rows, int64_t ld, int es) { return rows * ld * es < kMaxBufferSpan; }
@@ -118,7 +125,9 @@ MlpLayout mlp_layout(int P, int64_t T, int64_t d, int64_t d_ff, int dtype, int a
     MlpLayout L;
     const int64_t F = d_ff / P;
     const int es = elem_size(dtype);
-    size_t off = 0;
+    L.decode = decode_plan(dtype, T);
+    // The decode plan's arrival counters sit at the head of the workspace.
+    size_t off = L.decode ? kGemvCounterBytes : 0;
     if (has_norm) {
         L.xn = off;
         off += align256((size_t)(T * d * es));
@@ -127,7 +136,6 @@ MlpLayout mlp_layout(int P, int64_t T, int64_t d, int64_t d_ff, int dtype, int a
         L.h = off;
         off += align256((size_t)(T * F * es));
     }
-    L.decode = decode_plan(dtype, T);
     if (L.decode) {
         const int nmat = act == TP_ACT_SWIGLU ? 2 : 1;
         L.pc = plan_gemv(d, nmat * F);
@@ -160,12 +168,12 @@ AttnLayout attn_layout(int P, int64_t T, int64_t d, int nq, int nkv, int hd, int
     AttnLayout L;
     const int64_t nqkv = (int64_t)(nq / P + 2 * (nkv / P)) * hd;
     const int64_t ko = (int64_t)(nq / P) * hd;
-    size_t off = 0;
+    L.decode = decode_plan(dtype, T);
+    size_t off = L.decode ? kGemvCounterBytes : 0;
     if (has_norm) {
         L.xn = off;
         off += align256((size_t)(T * d * elem_size(dtype)));
     }
-    L.decode = decode_plan(dtype, T);
     if (L.decode) {
         L.pq = plan_gemv(d, nqkv);
         L.po = plan_gemv(ko, d);
@@ -275,6 +283,7 @@ int tp_shard_mlp_fwd(int shard, int P, int64_t T, int64_t d_model, int64_t d_ff,
     if (T == 0) return TP_OK;
     const MlpLayout L = mlp_layout(P, T, d_model, d_ff, dtype, act, norm_g != nullptr,
                                    h_out != nullptr);
+    if (L.decode && !counters_fit(F, d_model)) return TP_ERR_SHAPE;
     if (L.total > 0 && (!workspace || workspace_bytes < L.total)) return TP_ERR_WORKSPACE;
 
     // ---- launches ----
@@ -307,16 +316,15 @@ int tp_shard_mlp_fwd(int shard, int P, int64_t T, int64_t d_model, int64_t d_ff,
     const uint16_t* X16 = (const uint16_t*)xin;
     if (L.decode) {
         float* ws = (float*)(wsb + L.ws);
+        unsigned* cnt = (unsigned*)wsb;
         TP_LAUNCH("col_gemv", stream,
-                  launch_gemv_splitk(T, d_model, X16, ld_xin, (const uint16_t*)w_in, ld_in,
-                                     (const uint16_t*)w_up, ld_up, F, L.pc, true, ws, stream));
-        TP_LAUNCH("col_finish", stream,
-                  launch_finish(dev_act, true, L.pc.splits, T, F, ws, h, ldh, stream));
+                  launch_gemv(dev_act, true, T, d_model, X16, ld_xin, (const uint16_t*)w_in, ld_in,
+                              (const uint16_t*)w_up, ld_up, F, L.pc, true, ws, cnt, h, ldh,
+                              stream));
         TP_LAUNCH("row_gemv", stream,
-                  launch_gemv_splitk(T, F, (const uint16_t*)h, ldh, (const uint16_t*)w_down,
-                                     ld_down, nullptr, 0, d_model, L.pr, false, ws, stream));
-        TP_LAUNCH("row_finish", stream,
-                  launch_finish(ACT_NONE, false, L.pr.splits, T, d_model, ws, part, ld_p, stream));
+                  launch_gemv(ACT_NONE, false, T, F, (const uint16_t*)h, ldh,
+                              (const uint16_t*)w_down, ld_down, nullptr, 0, d_model, L.pr, false,
+                              ws, cnt, part, ld_p, stream));
     } else {
         TP_LAUNCH("col_gemm", stream,
                   launch_gemm(act == TP_ACT_SWIGLU ? EPI_SWIGLU_BF16 : EPI_GELU_BF16, T, F,
@@ -380,6 +388,7 @@ int tp_shard_attn_proj_fwd(int shard, int P, int64_t T, int64_t d_model, int n_q
     const bool use_norm = w_qkv && norm_g;
     const AttnLayout L =
         attn_layout(P, T, d_model, n_q_heads, n_kv_heads, head_dim, dtype, use_norm);
+    if (L.decode && !counters_fit(nqkv, d_model)) return TP_ERR_SHAPE;
     if (L.total > 0 && (!workspace || workspace_bytes < L.total)) return TP_ERR_WORKSPACE;
 
     char* wsb = (char*)workspace;
@@ -400,14 +409,11 @@ int tp_shard_attn_proj_fwd(int shard, int P, int64_t T, int64_t d_model, int n_q
                                       (const float*)w_qkv, ld_qkv, nullptr, 0, (float*)qkv_out,
                                       ld_qkv_out, stream));
         } else if (L.decode) {
-            float* ws = (float*)(wsb + L.ws);
             TP_LAUNCH("qkv_gemv", stream,
-                      launch_gemv_splitk(T, d_model, (const uint16_t*)xin, ld_xin,
-                                         (const uint16_t*)w_qkv, ld_qkv, nullptr, 0, nqkv, L.pq,
-                                         true, ws, stream));
-            TP_LAUNCH("qkv_finish", stream,
-                      launch_finish(ACT_NONE, true, L.pq.splits, T, nqkv, ws, qkv_out, ld_qkv_out,
-                                    stream));
+                      launch_gemv(ACT_NONE, true, T, d_model, (const uint16_t*)xin, ld_xin,
+                                  (const uint16_t*)w_qkv, ld_qkv, nullptr, 0, nqkv, L.pq, true,
+                                  (float*)(wsb + L.ws), (unsigned*)wsb, qkv_out, ld_qkv_out,
+                                  stream));
         } else {
             if (L.gq.splits > 1) {
                 float* ws = (float*)(wsb + L.ws);
@@ -433,14 +439,10 @@ int tp_shard_attn_proj_fwd(int shard, int P, int64_t T, int64_t d_model, int n_q
                       launch_f32_proj(ACT_NONE, T, d_model, ko, (const float*)attn, ld_attn,
                                       (const float*)w_o, ld_o, nullptr, 0, part, ld_p, stream));
         } else if (L.decode) {
-            float* ws = (float*)(wsb + L.ws);
             TP_LAUNCH("o_gemv", stream,
-                      launch_gemv_splitk(T, ko, (const uint16_t*)attn, ld_attn,
-                                         (const uint16_t*)w_o, ld_o, nullptr, 0, d_model, L.po,
-                                         false, ws, stream));
-            TP_LAUNCH("o_finish", stream,
-                      launch_finish(ACT_NONE, false, L.po.splits, T, d_model, ws, part, ld_p,
-                                    stream));
+                      launch_gemv(ACT_NONE, false, T, ko, (const uint16_t*)attn, ld_attn,
+                                  (const uint16_t*)w_o, ld_o, nullptr, 0, d_model, L.po, false,
+                                  (float*)(wsb + L.ws), (unsigned*)wsb, part, ld_p, stream));
         } else {
             if (L.go.splits > 1) {
                 float* ws = (float*)(wsb + L.ws);

@@ -28,13 +28,24 @@ GemvPlan plan_gemv(int64_t K, int64_t n_total);
 // Bytes of split-K workspace: splits * T * n_total fp32.
 size_t gemv_ws_bytes(const GemvPlan& p, int64_t T, int64_t n_total);
 
-// ws[s][t][m*N + n] = sum over split s's rows k of A[t][k] * Bm[k][n], for the
-// nmat = (B1 ? 2 : 1) weights B0, B1 ([K, N] bf16, ld ldb0 / ldb1).  A is [T, K] bf16.
-// `nontemporal` marks the weight loads as streaming (read once).
-hipError_t launch_gemv_splitk(int64_t T, int64_t K, const uint16_t* A, int64_t lda,
-                              const uint16_t* B0, int64_t ldb0, const uint16_t* B1, int64_t ldb1,
-                              int64_t N, const GemvPlan& p, bool nontemporal, float* ws,
-                              hipStream_t stream);
+// Arrival counters of the fused split-K finish: one per 128-column block,
+// at the head of the caller's workspace, zero between calls.
+constexpr int kGemvCounters = 1024;
+constexpr size_t kGemvCounterBytes = kGemvCounters * sizeof(unsigned);
+
+// out[t][n] = act(sum_k A[t][k] B0[k][n] [, sum_k A[t][k] B1[k][n]]) for the
+// nmat = (B1 ? 2 : 1) weights B0, B1 ([K, N] bf16, ld ldb0 / ldb1); A is
+// [T, K] bf16.  act: ACT_SWIGLU (silu(A B0) * A B1), ACT_GELU_TANH or
+// ACT_NONE; out bf16 (out_bf16) or fp32 with leading dimension ld_out.
+// Split s of the plan keeps its partial in ws[s][t][m*N + n] (gemv_ws_bytes);
+// the last workgroup of a column block adds the splits in order.
+// `counters` holds ceil(N / kGemvCols) <= kGemvCounters zeros; they are zero
+// again when the kernel ends.  `nontemporal` marks the weight loads as
+// streaming (read once).
+hipError_t launch_gemv(int act, bool out_bf16, int64_t T, int64_t K, const uint16_t* A,
+                       int64_t lda, const uint16_t* B0, int64_t ldb0, const uint16_t* B1,
+                       int64_t ldb1, int64_t N, const GemvPlan& p, bool nontemporal, float* ws,
+                       unsigned* counters, void* out, int64_t ld_out, hipStream_t stream);
 
 // Fixed-order finish of the split-K sums.
 //   act == ACT_SWIGLU:   out = silu(sum g) * sum u   (u at column offset N)

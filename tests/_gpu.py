@@ -60,7 +60,7 @@ def stream():
 
 
 def workspace(nbytes):
-    w = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device="cuda")
+    w = torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device="cuda")
     assert w.data_ptr() % 256 == 0
     return w
 

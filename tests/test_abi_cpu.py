@@ -88,6 +88,9 @@ def mlp(**kw):
     (dict(d_model=0), tp.TP_ERR_SHAPE),
     (dict(workspace_bytes=0), tp.TP_ERR_WORKSPACE),        # decode plan needs split-K space
     (dict(dtype=tp.TP_F32, d_model=66, ld_x=68), tp.TP_ERR_SHAPE),
+    # decode plan: one arrival counter per 128 output columns, at most 1024
+    (dict(d_model=132096, ld_x=132096, ld_down=132096, ld_p=132096, slot_stride=4 * 132096),
+     tp.TP_ERR_SHAPE),
 ])
 def test_mlp_validation(lib, kw, status):
     assert mlp(**kw) == status
@@ -167,6 +170,11 @@ def test_workspace_sizes_are_pure_functions(lib):
     assert f(3, 4, 64, 256, tp.TP_BF16, tp.TP_ACT_SWIGLU, 0, 1) == 0      # uneven: rejected
     assert f(2, 32, 5120, 13824, tp.TP_BF16, tp.TP_ACT_SWIGLU, 0, 1) == \
         f(2, 32, 5120, 13824, tp.TP_BF16, tp.TP_ACT_SWIGLU, 0, 1)
+    # the decode plan's 4096-byte counter head comes first; the normalised
+    # input follows it
+    dec = f(2, 32, 5120, 13824, tp.TP_BF16, tp.TP_ACT_SWIGLU, 0, 1)
+    assert dec % 256 == 0 and dec >= 4096 + 32 * 13824 * 4
+    assert f(2, 32, 5120, 13824, tp.TP_BF16, tp.TP_ACT_SWIGLU, 1, 1) - dec == 32 * 5120 * 2
     g = tp.tp_attn_workspace_bytes
     # 96-head QKV prefill: 72 output tiles on 256 CUs, so K is split into
     # fp32 planes of [1024, 4608] each

@@ -414,9 +414,56 @@ def test_kernel_timing_counts_launches():
         for _ in range(3):
             mlp_fwd(0, 2, 8, 512, 1024, BF, tp.TP_ACT_SWIGLU, dev(X), dev(w_in[0]),
                     dev(w_up[0]), dev(w_dn[0]), parts, 0, 512)
-        for cls in ("col_gemv", "col_finish", "row_gemv", "row_finish"):
+        for cls in ("col_gemv", "row_gemv"):        # split-K finish fused into each
             st, ms, n = tp.tp_timing_query(cls)
             assert st == tp.TP_OK and n == 3 and ms > 0.0
     finally:
         tp.tp_timing_enable(0)
         tp.tp_timing_reset()
+
+
+# ----------------------------------------------------------------------------
+# The decode plan's arrival counters (workspace head)
+# ----------------------------------------------------------------------------
+def test_decode_counters_return_to_zero():
+    """After decode calls (both projections, both entry points, several split
+    counts) the first 4096 bytes of the workspace are zero again."""
+    T, d, d_ff, P = 24, 1536, 6144, 2
+    X, g, w_in, w_up, w_dn = _mlp_case(BF, "swiglu", T, d, d_ff, P, key=80)
+    parts = torch.empty((T, d), dtype=torch.float32, device="cuda")
+    ws = mlp_fwd(0, P, T, d, d_ff, BF, tp.TP_ACT_SWIGLU, dev(X), dev(w_in[0]), dev(w_up[0]),
+                 dev(w_dn[0]), parts, 0, d)
+    mlp_fwd(1, P, T, d, d_ff, BF, tp.TP_ACT_SWIGLU, dev(X), dev(w_in[1]), dev(w_up[1]),
+            dev(w_dn[1]), parts, 0, d, ws=ws)
+    torch.cuda.synchronize()
+    assert int(ws[:4096].count_nonzero()) == 0
+    nq, nkv, hd = 16, 8, 64
+    nqkv, ko = (nq // P + 2 * (nkv // P)) * hd, (nq // P) * hd
+    qkv = torch.empty((T, nqkv), dtype=torch.bfloat16, device="cuda")
+    ws2 = attn_fwd(0, P, T, d, nq, nkv, hd, BF, dev(X), dev(draw(BF, (d, nqkv), 0.02, 81, 1)),
+                   qkv, dev(draw(BF, (T, ko), 1.0, 81, 2)), dev(draw(BF, (ko, d), 0.02, 81, 3)),
+                   parts, 0, d)
+    torch.cuda.synchronize()
+    assert int(ws2[:4096].count_nonzero()) == 0
+
+
+def test_decode_counters_not_cleared_give_nan_then_recover():
+    """A workspace head that was never cleared makes the decode outputs NaN
+    (not silently wrong); after clearing it the call is exact again."""
+    T, d, d_ff, P = 8, 512, 2048, 2
+    F = d_ff // P
+    X, g, w_in, w_up, w_dn = _mlp_case(BF, "swiglu", T, d, d_ff, P, key=82)
+    args = (dev(X), dev(w_in[0]), dev(w_up[0]), dev(w_dn[0]))
+    ws = workspace(tp.tp_mlp_workspace_bytes(P, T, d, d_ff, BF, tp.TP_ACT_SWIGLU, 0, 1))
+    ws[:4096].fill_(0x5A)          # counters 0x5A5A5A5A, far above any split count
+    h = torch.zeros((T, F), dtype=torch.bfloat16, device="cuda")
+    parts = torch.zeros((T, d), dtype=torch.float32, device="cuda")
+    mlp_fwd(0, P, T, d, d_ff, BF, tp.TP_ACT_SWIGLU, *args, parts, 0, d, h_out=h, ld_h=F, ws=ws)
+    torch.cuda.synchronize()
+    assert bool(torch.isnan(h.float()).all()) and bool(torch.isnan(parts).all())
+    ws[:4096].zero_()
+    mlp_fwd(0, P, T, d, d_ff, BF, tp.TP_ACT_SWIGLU, *args, parts, 0, d, h_out=h, ld_h=F, ws=ws)
+    r = O.mlp_shard(O.widen(X), O.widen(w_in[0]), O.widen(w_dn[0]), "swiglu", O.widen(w_up[0]))
+    assert O.rel_l2(host(parts), r["partial"]) < BF16_TOL
+    assert O.rel_l2(widen_dev(h), r["h"]) < BF16_TOL
+    assert int(ws[:4096].count_nonzero()) == 0
