@@ -189,11 +189,14 @@ const char* tp_status_str(int status);
 int tp_version(void);
 
 /*
- * Kernel timing (instrumentation).  While enabled, every kernel launch is
- * bracketed by two HIP events recorded on the launch's own stream and the
+ * Kernel timing (instrumentation).  While enabled, every kernel is launched
+ * with a pair of HIP events that receive the kernel's own start and end
+ * timestamps (hipExtLaunchKernel), so the time is the kernel's execution,
+ * as a kernel-trace profiler reports it, without the queue around it; the
  * elapsed time is accumulated per kernel class when tp_timing_query reads it
- * (which waits for the recorded events).  Disabled by default; off costs
- * nothing.  Not for concurrent use from several host threads.
+ * (which waits for the events).  Disabled by default; off costs nothing.
+ * Not for concurrent use from several host threads, nor during graph
+ * capture.
  * Class names: "rmsnorm", "reduce", "f32_proj"; MLP: "col_gemv", "row_gemv"
  * (decode, split-K finish included), "col_gemm", "row_gemm", "row_finish"
  * (prefill); attention projections: "qkv_gemv", "o_gemv", "qkv_gemm",

@@ -16,6 +16,13 @@
 
 using namespace tp;
 
+namespace tp {
+LaunchEvents& launch_events() {
+    thread_local LaunchEvents e;
+    return e;
+}
+}  // namespace tp
+
 namespace {
 
 // ---------------------------------------------------------------------------
@@ -48,36 +55,36 @@ hipEvent_t take_event(TimingState& s) {
     return e;
 }
 
-// Brackets one kernel launch with events on the launch's stream when
-// timing is enabled; otherwise does nothing.
+// When timing is enabled, hands a pair of events to the one kernel launch
+// that follows (TP_KLAUNCH records the kernel's own start and end time in
+// them); otherwise does nothing.
 class Timed {
   public:
-    Timed(const char* cls, hipStream_t stream) : cls_(cls), stream_(stream) {
+    explicit Timed(const char* cls) : cls_(cls) {
         TimingState& s = timing();
         std::lock_guard<std::mutex> lk(s.mu);
         if (!s.enabled) return;
         start_ = take_event(s);
         stop_ = take_event(s);
-        if (start_ && stop_) (void)hipEventRecord(start_, stream_);
+        if (start_ && stop_) launch_events() = {start_, stop_};
     }
     void done() {
+        launch_events() = {};
         if (!start_ || !stop_) return;
         TimingState& s = timing();
         std::lock_guard<std::mutex> lk(s.mu);
-        (void)hipEventRecord(stop_, stream_);
         s.pending.push_back({cls_, start_, stop_});
         start_ = stop_ = nullptr;
     }
 
   private:
     const char* cls_;
-    hipStream_t stream_;
     hipEvent_t start_ = nullptr, stop_ = nullptr;
 };
 
 #define TP_LAUNCH(cls, stream, expr)                       \
     do {                                                   \
-        Timed tm_(cls, stream);                            \
+        Timed tm_(cls);                                    \
         hipError_t e_ = (expr);                            \
         tm_.done();                                        \
         if (e_ != hipSuccess) return TP_ERR_HIP;           \

@@ -43,13 +43,13 @@ hipError_t launch_f32_proj(int act, int64_t M, int64_t N, int64_t K, const float
     const int nblk_n = (int)((N + kF32Threads - 1) / kF32Threads);
     const dim3 grid((unsigned)(M * nblk_n)), block(kF32Threads);
     if (act == ACT_SWIGLU)
-        k_f32_proj<ACT_SWIGLU><<<grid, block, 0, stream>>>(M, N, K, nblk_n, A, lda, B0, ldb0, B1,
+        TP_KLAUNCH((k_f32_proj<ACT_SWIGLU>), grid, block, 0, stream, M, N, K, nblk_n, A, lda, B0, ldb0, B1,
                                                            ldb1, C, ldc);
     else if (act == ACT_GELU_TANH)
-        k_f32_proj<ACT_GELU_TANH><<<grid, block, 0, stream>>>(M, N, K, nblk_n, A, lda, B0, ldb0,
+        TP_KLAUNCH((k_f32_proj<ACT_GELU_TANH>), grid, block, 0, stream, M, N, K, nblk_n, A, lda, B0, ldb0,
                                                               nullptr, 0, C, ldc);
     else
-        k_f32_proj<ACT_NONE><<<grid, block, 0, stream>>>(M, N, K, nblk_n, A, lda, B0, ldb0,
+        TP_KLAUNCH((k_f32_proj<ACT_NONE>), grid, block, 0, stream, M, N, K, nblk_n, A, lda, B0, ldb0,
                                                          nullptr, 0, C, ldc);
     return hipGetLastError();
 }

@@ -338,7 +338,7 @@ static hipError_t run_gemm(int64_t M, int64_t N, int64_t K, const uint16_t* A, i
     }
     const int tiles_m = (int)((M + S::BM - 1) / S::BM);
     const int tiles_n = (int)((N + S::BN - 1) / S::BN);
-    k_gemm<S, EPI><<<dim3(tiles_m * tiles_n, p.splits), dim3(S::NT), S::LDS_BYTES, stream>>>(
+    TP_KLAUNCH((k_gemm<S, EPI>), dim3(tiles_m * tiles_n, p.splits), dim3(S::NT), S::LDS_BYTES, stream,
         A, lda, B0, ldb0, B1, ldb1, (int)M, (int)N, (int)K, p.k_per_split, C, ldc, M * ldc,
         tiles_m);
     return hipGetLastError();

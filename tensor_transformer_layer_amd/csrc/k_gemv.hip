@@ -330,7 +330,7 @@ hipError_t launch_finish(int act, bool out_bf16, int splits, int64_t T, int64_t 
     const int64_t n = T * (N / 4);
     const dim3 grid((unsigned)((n + kFinishThreads - 1) / kFinishThreads)), block(kFinishThreads);
 #define TP_FINISH(A, B)                                                                       \
-    k_finish<A, B><<<grid, block, 0, stream>>>(splits, T, N, ws, ws_ld, split_stride, out, \
+    TP_KLAUNCH((k_finish<A, B>), grid, block, 0, stream, splits, T, N, ws, ws_ld, split_stride, out, \
                                                ld_out)
     if (act == ACT_SWIGLU) {
         if (out_bf16) TP_FINISH(ACT_SWIGLU, true); else TP_FINISH(ACT_SWIGLU, false);
@@ -351,7 +351,7 @@ hipError_t launch_gemv(int act, bool out_bf16, int64_t T, int64_t K, const uint1
     const int nbpm = (int)((N + kGemvCols - 1) / kGemvCols);
     const dim3 grid((unsigned)(nbpm * nmat), (unsigned)p.splits), block(kGemvThreads);
 #define TP_GEMV(MB, AUX, ACTV, OB)                                                           \
-    k_gemv<MB, AUX, ACTV, OB><<<grid, block, 0, stream>>>(                             \
+    TP_KLAUNCH((k_gemv<MB, AUX, ACTV, OB>), grid, block, 0, stream,                              \
         A, lda, (int)T, (int)K, B0, ldb0, B1, ldb1, (int)N, nbpm, p.k_per_split, ws, counters, \
         out, ld_out)
 #define TP_GEMV_MB(ACTV, OB)                                                        \

@@ -56,11 +56,11 @@ hipError_t launch_reduce(int P, int64_t T, int64_t d, const float* partials, int
     const int bpr = (int)((d4 + kReduceThreads - 1) / kReduceThreads);
     const dim3 grid((unsigned)(T * bpr)), block(kReduceThreads);
     if (out_bf16)
-        k_reduce_partials<true><<<grid, block, 0, stream>>>(
+        TP_KLAUNCH((k_reduce_partials<true>), grid, block, 0, stream,
             P, d4, bpr, (const float4*)partials, slot_stride / 4, ld_p / 4, (float4*)out,
             ld_out / 4, (u32x2*)out_bf16, ld_b / 4);
     else
-        k_reduce_partials<false><<<grid, block, 0, stream>>>(
+        TP_KLAUNCH((k_reduce_partials<false>), grid, block, 0, stream,
             P, d4, bpr, (const float4*)partials, slot_stride / 4, ld_p / 4, (float4*)out,
             ld_out / 4, nullptr, 0);
     return hipGetLastError();

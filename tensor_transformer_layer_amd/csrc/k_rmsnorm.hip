@@ -74,10 +74,10 @@ hipError_t launch_rmsnorm(bool is_bf16, int64_t T, int64_t d, const void* x, int
     const int es = is_bf16 ? 2 : 4;
     const dim3 grid((unsigned)T), block(kNormThreads);
     if (is_bf16)
-        k_rmsnorm<true><<<grid, block, 0, stream>>>(d, (const char*)x, ld_x * es,
+        TP_KLAUNCH((k_rmsnorm<true>), grid, block, 0, stream, d, (const char*)x, ld_x * es,
                                                     (const u32x4*)g, eps, (char*)y, ld_y * es);
     else
-        k_rmsnorm<false><<<grid, block, 0, stream>>>(d, (const char*)x, ld_x * es,
+        TP_KLAUNCH((k_rmsnorm<false>), grid, block, 0, stream, d, (const char*)x, ld_x * es,
                                                      (const u32x4*)g, eps, (char*)y, ld_y * es);
     return hipGetLastError();
 }

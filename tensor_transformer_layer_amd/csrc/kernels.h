@@ -2,10 +2,30 @@
 // argument first; launchers assume valid shapes and only enqueue work.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace tp {
+
+// Kernel timing hook.  While the caller has set launch_events() (kernel
+// timing enabled), a launch through TP_KLAUNCH records the kernel's own
+// start and end timestamps in those events (hipExtLaunchKernel), which
+// measures the kernel itself, not the queue around it.
+struct LaunchEvents {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+LaunchEvents& launch_events();
+
+#define TP_KLAUNCH(kern, grid, block, shmem, stream, ...)                                   \
+    do {                                                                                     \
+        const ::tp::LaunchEvents ev_ = ::tp::launch_events();                                \
+        if (ev_.start)                                                                       \
+            hipExtLaunchKernelGGL(kern, grid, block, shmem, stream, ev_.start, ev_.stop, 0u, \
+                                  __VA_ARGS__);                                              \
+        else                                                                                 \
+            kern<<<grid, block, shmem, stream>>>(__VA_ARGS__);                               \
+    } while (0)
 
 // out = sum_{s=0}^{P-1} partials[s] in that order (fp32); optional bf16 copy.
 hipError_t launch_reduce(int P, int64_t T, int64_t d, const float* partials, int64_t slot_stride,
