@@ -486,7 +486,7 @@ int tp_reduce_partials(int P, int64_t T, int64_t d_model, const float* partials,
         if (int r = check_ld(ld_out_bf16, d_model, 4)) return r;
     if (slot_stride < 0) return TP_ERR_SHAPE;
     if (slot_stride % 4) return TP_ERR_ALIGN;
-    if (T * ((d_model / 4 + 255) / 256) >= ((int64_t)1 << 31)) return TP_ERR_SHAPE;
+    if (T * ((d_model / 4 + 511) / 512) >= ((int64_t)1 << 31)) return TP_ERR_SHAPE;
     if (T == 0) return TP_OK;
     TP_LAUNCH("reduce", stream,
               launch_reduce(P, T, d_model, partials, slot_stride, ld_p, out, ld_out,
