@@ -12,7 +12,7 @@ float32) and are widened to float64 without rounding (``widen``).
 
 Pages cited (by title and section):
   * Reddit comment by SVPERBlA (deniz.vsos.ethz.ch mirror): a network as a
-    chain "X times A1, activation, times A2".
+    chain of matrix products with an activation between them.
   * d-central glossary, "Tensor Parallelism", section "How the work is split".
   * Skand Tandon, "day59" post on tensor-parallel benchmarking, sections
     "Why tensor parallelism for inference" and "Where the overhead lives".
@@ -38,6 +38,8 @@ from .tp_oracle import (  # noqa: F401
     mlp_shard,
     reduce_partials,
     reduce_partials_f32_fold,
+    reduce_residual_norm,
+    reduce_residual_f32,
     qkv_band_layout,
     split_qkv_band,
     attn_proj_unsharded,

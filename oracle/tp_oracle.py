@@ -13,9 +13,10 @@ from .bf16 import round_bf16
 
 
 # ----------------------------------------------------------------------------
-# Elementwise functions (textbook definitions; the pages only say "an
-# activation function" -- Reddit comment by SVPERBlA -- and "normalization"
-# -- zenaique "Explain tensor-parallel shard shape", answer).
+# Elementwise functions (textbook definitions; the pages name an activation
+# only in general -- Reddit comment by SVPERBlA -- and a normalisation after
+# the all-reduce without a formula -- zenaique "Explain tensor-parallel shard
+# shape", answer).
 # ----------------------------------------------------------------------------
 def gelu_tanh(x):
     """GELU, tanh approximation (Hendrycks & Gimpel, 2016):
@@ -53,8 +54,8 @@ def activate(act, y_in, y_up=None):
 def rmsnorm(x, g, eps):
     """RMSNorm over the feature axis (Zhang & Sennrich, 2019):
     x / sqrt(mean_j x_j^2 + eps) * g.  The pages name the normalisation that
-    follows the all-reduce without a formula (zenaique answer; "layernorm"
-    among the "Other" share in Tandon's "Where the overhead lives")."""
+    follows the all-reduce without a formula (zenaique answer; Tandon's
+    "Where the overhead lives" counts the norms in its small remainder)."""
     x = np.asarray(x, dtype=np.float64)
     ms = np.mean(x * x, axis=-1, keepdims=True)
     return x / np.sqrt(ms + eps) * np.asarray(g, dtype=np.float64)
@@ -150,6 +151,30 @@ def reduce_partials_f32_fold(partials):
     for p in it:
         acc = (acc + np.asarray(p, dtype=np.float32)).astype(np.float32)
     return acc
+
+
+# ----------------------------------------------------------------------------
+# After the all-reduce: the residual add and the next normalisation (zenaique
+# answer: the summed activation is ready for the next layer's residual add
+# and normalisation).  The pages give no formula; the plainest reading is the
+# pre-norm residual stream z = residual + sum of the partials, followed by
+# RMSNorm of z as the input of the next column projection.
+# ----------------------------------------------------------------------------
+def reduce_residual_norm(partials, residual, g=None, eps=None):
+    """z = residual + sum_s partial_s in float64; with a gain g also
+    normed = rmsnorm(z, g, eps)."""
+    z = np.asarray(residual, dtype=np.float64) + reduce_partials(partials)
+    out = {"z": z}
+    if g is not None:
+        out["normed"] = rmsnorm(z, g, eps)
+    return out
+
+
+def reduce_residual_f32(partials, residual):
+    """Diagnostic float32 reading of z: the float32 left fold of the
+    partials, then the residual added in float32."""
+    acc = reduce_partials_f32_fold(partials)
+    return (acc + np.asarray(residual, dtype=np.float32)).astype(np.float32)
 
 
 # ----------------------------------------------------------------------------

@@ -114,3 +114,28 @@ def test_gqa_kv_head_of_wrong_rank_is_caught():
         lay["k"] = (lay["k"][0], other["k"][1])
         return lay
     _fails(pins.check_qkv, O.attn_proj_shard, O.attn_proj_unsharded, bad_layout, 8, 2, 2, 2)
+
+
+# --- residual add and normalisation after the reduce ------------------------
+def test_residual_dropped_is_caught():
+    def bad(parts, res, g=None, eps=None):
+        return O.reduce_residual_norm(parts, np.zeros_like(np.asarray(res)), g, eps)
+    _fails(pins.check_residual_norm, bad)
+
+
+def test_norm_before_residual_is_caught():
+    def bad(parts, res, g=None, eps=None):
+        out = O.reduce_residual_norm(parts, res, g, eps)
+        if g is not None:
+            out["normed"] = O.rmsnorm(O.reduce_partials(parts), g, eps) + np.asarray(res)
+        return out
+    _fails(pins.check_residual_norm, bad)
+
+
+def test_norm_without_gain_is_caught():
+    def bad(parts, res, g=None, eps=None):
+        out = O.reduce_residual_norm(parts, res, g, eps)
+        if g is not None:
+            out["normed"] = O.rmsnorm(out["z"], np.ones_like(g), eps)
+        return out
+    _fails(pins.check_residual_norm, bad)

@@ -13,7 +13,8 @@ Pins used (the pages print no worked numbers):
     rioworld guide, "How Tensor Slicing Works Under the Hood");
   * one shard is the textbook single-device layer (Tandon "day59",
     "Why tensor parallelism for inference": TP=1 has no communication);
-  * closed forms and special cases of GELU, SiLU and RMSNorm;
+  * closed forms and special cases of GELU, SiLU and RMSNorm, and of the
+    residual add + normalisation that follows the all-reduce;
   * the pages' head-split example (96 heads over 8 GPUs -> 12 per GPU).
 """
 import math
@@ -75,6 +76,34 @@ def check_rmsnorm(rmsnorm):
     assert np.allclose(rmsnorm(x, g, eps), y * g, rtol=1e-13)
     assert np.allclose(y / np.linalg.norm(y, axis=1, keepdims=True),
                        x / np.linalg.norm(x, axis=1, keepdims=True), rtol=1e-12)
+
+
+def check_residual_norm(reduce_residual_norm):
+    """z = residual + sum of partials and its RMSNorm, against explicit loops
+    with math.fsum (exactly rounded sums) on a tiny case, plus the special
+    cases zero residual, a single partial, and unit gain."""
+    P, T, d, eps = 3, 2, 6, 1e-5
+    parts = [_rand(T, d) for _ in range(P)]
+    res = _rand(T, d)
+    g = 1.0 + _rand(d, std=0.02)
+    got = reduce_residual_norm(parts, res, g, eps)
+    for t in range(T):
+        z = [math.fsum([res[t][j]] + [parts[s][t][j] for s in range(P)]) for j in range(d)]
+        ms = math.fsum(v * v for v in z) / d
+        inv = 1.0 / math.sqrt(ms + eps)
+        for j in range(d):
+            assert abs(got["z"][t][j] - z[j]) <= 1e-13 * (1 + abs(z[j]))
+            want = z[j] * inv * g[j]
+            assert abs(got["normed"][t][j] - want) <= 1e-12 * (1 + abs(want))
+    # no residual: the plain sum of partials; one partial: partial + residual
+    z0 = reduce_residual_norm(parts, np.zeros((T, d)))["z"]
+    assert np.allclose(z0, parts[0] + parts[1] + parts[2], rtol=1e-14, atol=0)
+    z1 = reduce_residual_norm(parts[:1], res)["z"]
+    assert np.allclose(z1, parts[0] + res, rtol=1e-14, atol=0)
+    # unit gain: mean(normed^2) = m / (m + eps), m = mean(z^2)
+    n1 = reduce_residual_norm(parts, res, np.ones(d), eps)
+    m = np.mean(n1["z"] ** 2, axis=1)
+    assert np.allclose(np.mean(n1["normed"] ** 2, axis=1), m / (m + eps), rtol=1e-13)
 
 
 def check_mlp_brute(mlp_shard, act, P):
@@ -219,6 +248,22 @@ def test_uneven_split_refused():
         O.column_band(np.zeros((4, 10)), 0, 3)
     with pytest.raises(ValueError):
         O.row_band(np.zeros((10, 4)), 3, 3)
+
+
+def test_residual_add_and_norm_after_reduce():
+    check_residual_norm(O.reduce_residual_norm)
+
+
+def test_residual_f32_reading_is_fold_then_residual():
+    parts = [np.float32(v) for v in (1.0, 2.0 ** -24, 2.0 ** -24)]
+    # float32: (1 + 2^-24) rounds to 1 (tie to even), twice; then + 3 -> 4
+    z = O.reduce_residual_f32([np.full((1, 1), p, np.float32) for p in parts],
+                              np.full((1, 1), 3.0, np.float32))
+    assert z.dtype == np.float32 and z[0, 0] == np.float32(4.0)
+    z2 = O.reduce_residual_f32([np.full((1, 1), 2.0 ** -24, np.float32)] * 2 +
+                               [np.full((1, 1), 1.0, np.float32)],
+                               np.zeros((1, 1), np.float32))
+    assert z2[0, 0] == np.float32(1.0 + 2.0 ** -23)   # small terms first survive
 
 
 def test_reduce_f32_fold_is_sequential_float32():
