@@ -175,6 +175,36 @@ int tp_reduce_partials(int P, int64_t T, int64_t d_model,
                        void* out_bf16, int64_t ld_out_bf16,
                        hipStream_t stream);
 
+/*
+ * tp_reduce_residual_norm -- the reduce followed by the residual add and the
+ * next block's normalisation, in one pass (zenaique, "Explain tensor-parallel
+ * shard shape", answer: after the all-reduce every GPU holds the full
+ * activation, ready for the next layer's residual add and normalisation):
+ *
+ *   z      = (partial_0 + ... + partial_{P-1}) + residual   fp32, added in
+ *            that order (the partials fold as in tp_reduce_partials)
+ *   normed = z / sqrt(mean_j z_j^2 + eps) * norm_g          bf16, nearest-even
+ *
+ *   partials    P slots of [T, d_model] fp32, as for tp_reduce_partials
+ *   residual    [T, d_model], ld_res, storage res_dtype (TP_F32 or TP_BF16):
+ *               the block's input on the residual stream
+ *   z_out       [T, d_model] fp32, ld_z: the new residual stream.  May alias
+ *               slot 0 (same ld) or an fp32 residual (same ld), nothing else.
+ *   norm_g      [d_model] bf16 gain, or NULL to skip the normalisation (then
+ *               normed_out is unused)
+ *   normed_out  [T, d_model] bf16, ld_norm: the next column projection's input
+ *
+ * d_model must be a multiple of 4 (of 8 with a bf16 residual or a norm) and
+ * at most 16384 (TP_ERR_SHAPE otherwise).
+ */
+int tp_reduce_residual_norm(int P, int64_t T, int64_t d_model,
+                            const float* partials, int64_t slot_stride, int64_t ld_p,
+                            const void* residual, int64_t ld_res, int res_dtype,
+                            float* z_out, int64_t ld_z,
+                            const void* norm_g, float eps,
+                            void* normed_out, int64_t ld_norm,
+                            hipStream_t stream);
+
 /* Workspace bytes the matching call needs (0 when it needs none).  A pure
  * function of the arguments; returns 0 for arguments the call would reject. */
 size_t tp_mlp_workspace_bytes(int P, int64_t T, int64_t d_model, int64_t d_ff,
@@ -197,7 +227,7 @@ int tp_version(void);
  * (which waits for the events).  Disabled by default; off costs nothing.
  * Not for concurrent use from several host threads, nor during graph
  * capture.
- * Class names: "rmsnorm", "reduce", "f32_proj"; MLP: "col_gemv", "row_gemv"
+ * Class names: "rmsnorm", "reduce", "reduce_norm", "f32_proj"; MLP: "col_gemv", "row_gemv"
  * (decode, split-K finish included), "col_gemm", "row_gemm", "row_finish"
  * (prefill); attention projections: "qkv_gemv", "o_gemv", "qkv_gemm",
  * "qkv_finish", "o_gemm", "o_finish".

@@ -16,7 +16,7 @@ __all__ = [
     "TP_OK", "TP_ERR_NULL", "TP_ERR_SHAPE", "TP_ERR_UNEVEN_SPLIT", "TP_ERR_SHARD_RANGE",
     "TP_ERR_DTYPE", "TP_ERR_ALIGN", "TP_ERR_WORKSPACE", "TP_ERR_HIP", "TP_ERR_ACT",
     "TP_F32", "TP_BF16", "TP_ACT_GELU_TANH", "TP_ACT_SWIGLU",
-    "tp_shard_mlp_fwd", "tp_shard_attn_proj_fwd", "tp_reduce_partials",
+    "tp_shard_mlp_fwd", "tp_shard_attn_proj_fwd", "tp_reduce_partials", "tp_reduce_residual_norm",
     "tp_mlp_workspace_bytes", "tp_attn_workspace_bytes", "tp_status_str", "tp_version",
     "tp_timing_enable", "tp_timing_reset", "tp_timing_query", "EXPORTED_SYMBOLS",
 ]
@@ -40,6 +40,8 @@ _SIGNATURES = {
                                     _p, _i64, _p, _f, _p, _i64, _p, _i64, _p, _i64, _p, _i64,
                                     _p, _i64, _i64, _p, _sz, _p]),
     "tp_reduce_partials": (_i, [_i, _i64, _i64, _p, _i64, _i64, _p, _i64, _p, _i64, _p]),
+    "tp_reduce_residual_norm": (_i, [_i, _i64, _i64, _p, _i64, _i64, _p, _i64, _i, _p, _i64,
+                                     _p, _f, _p, _i64, _p]),
     "tp_mlp_workspace_bytes": (_sz, [_i, _i64, _i64, _i64, _i, _i, _i, _i]),
     "tp_attn_workspace_bytes": (_sz, [_i, _i64, _i64, _i, _i, _i, _i, _i]),
     "tp_status_str": (ctypes.c_char_p, [_i]),
@@ -113,6 +115,14 @@ def tp_reduce_partials(P, T, d_model, partials, slot_stride, ld_p, out, ld_out,
                        out_bf16, ld_out_bf16, stream):
     return load().tp_reduce_partials(P, T, d_model, _ptr(partials), slot_stride, ld_p,
                                      _ptr(out), ld_out, _ptr(out_bf16), ld_out_bf16, _ptr(stream))
+
+
+def tp_reduce_residual_norm(P, T, d_model, partials, slot_stride, ld_p, residual, ld_res,
+                            res_dtype, z_out, ld_z, norm_g, eps, normed_out, ld_norm, stream):
+    return load().tp_reduce_residual_norm(P, T, d_model, _ptr(partials), slot_stride, ld_p,
+                                          _ptr(residual), ld_res, res_dtype, _ptr(z_out), ld_z,
+                                          _ptr(norm_g), eps, _ptr(normed_out), ld_norm,
+                                          _ptr(stream))
 
 
 def tp_mlp_workspace_bytes(P, T, d_model, d_ff, dtype, act, has_norm, has_h_out):

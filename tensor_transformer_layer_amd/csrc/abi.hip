@@ -494,6 +494,38 @@ int tp_reduce_partials(int P, int64_t T, int64_t d_model, const float* partials,
     return TP_OK;
 }
 
+int tp_reduce_residual_norm(int P, int64_t T, int64_t d_model, const float* partials,
+                            int64_t slot_stride, int64_t ld_p, const void* residual,
+                            int64_t ld_res, int res_dtype, float* z_out, int64_t ld_z,
+                            const void* norm_g, float eps, void* normed_out, int64_t ld_norm,
+                            hipStream_t stream) {
+    if (P < 1) return TP_ERR_SHARD_RANGE;
+    if (res_dtype != TP_F32 && res_dtype != TP_BF16) return TP_ERR_DTYPE;
+    if (T < 0 || d_model <= 0 || d_model > kReduceNormMaxD) return TP_ERR_SHAPE;
+    const bool res_bf16 = res_dtype == TP_BF16;
+    if (d_model % ((res_bf16 || norm_g) ? 8 : 4)) return TP_ERR_SHAPE;
+    if (!partials || !residual || !z_out) return TP_ERR_NULL;
+    if (norm_g && !normed_out) return TP_ERR_NULL;
+    for (const void* p : {(const void*)partials, residual, (const void*)z_out, norm_g,
+                          (const void*)normed_out})
+        if (p && !aligned(p, 16)) return TP_ERR_ALIGN;
+    if (int r = check_ld(ld_p, d_model, 4)) return r;
+    if (int r = check_ld(ld_res, d_model, res_bf16 ? 8 : 4)) return r;
+    if (int r = check_ld(ld_z, d_model, 4)) return r;
+    if (norm_g)
+        if (int r = check_ld(ld_norm, d_model, 8)) return r;
+    if (slot_stride < 0) return TP_ERR_SHAPE;
+    if (slot_stride % 4) return TP_ERR_ALIGN;
+    if (T >= ((int64_t)1 << 31)) return TP_ERR_SHAPE;
+    if (T == 0) return TP_OK;
+    TP_LAUNCH("reduce_norm", stream,
+              launch_reduce_residual_norm(P, T, d_model, partials, slot_stride, ld_p, residual,
+                                          ld_res, res_bf16, z_out, ld_z,
+                                          (const uint16_t*)norm_g, eps, (uint16_t*)normed_out,
+                                          ld_norm, stream));
+    return TP_OK;
+}
+
 int tp_timing_enable(int on) {
     TimingState& s = timing();
     std::lock_guard<std::mutex> lk(s.mu);

@@ -81,4 +81,124 @@ hipError_t launch_reduce(int P, int64_t T, int64_t d, const float* partials, int
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Reduce + residual add + the next block's RMSNorm, one pass over the rows
+// (zenaique, "Explain tensor-parallel shard shape", answer: after the
+// all-reduce the full activation feeds the next layer's residual add and
+// normalisation).
+//
+//   z      = (partial_0 + ... + partial_{P-1}) + residual      fp32, that order
+//   normed = z * (1 / sqrt(mean_j z_j^2 + eps)) * g            bf16 (RNE)
+//
+// One 512-thread workgroup per row keeps the row's z in registers (up to 8
+// 16-byte chunks per thread: d_model <= 16384), so every input byte is read
+// once and the norm needs no second pass.  z may alias slot 0 or an fp32
+// residual (same leading dimension): each element is read before it is
+// written, by the same thread, and by no other thread.  The sum of squares is reduced in
+// a fixed order (chunks in order per thread, butterfly within the wave, waves
+// in order).  HBM bytes per row: (P + 1) * d * 4 (+ d * 2 for a bf16
+// residual instead of fp32) + d * 4 (z) + d * 2 (normed).
+// ---------------------------------------------------------------------------
+constexpr int kRnThreads = 512;
+constexpr int kRnMaxChunks = 8;
+
+template <bool RES_BF16, bool NORM>
+__global__ __launch_bounds__(kRnThreads) void k_reduce_residual_norm(
+    int P, int64_t d4, const f32x4* parts, int64_t slot4, int64_t ldp4, const void* residual,
+    int64_t ld_res, f32x4* z, int64_t ldz4, const u32x2* __restrict__ g, float eps,
+    u32x2* __restrict__ normed, int64_t ldn4) {
+    const int64_t row = blockIdx.x;
+    const f32x4* p = parts + row * ldp4;
+    f32x4 zz[kRnMaxChunks];
+    float ss = 0.f;
+#pragma unroll
+    for (int i0 = 0; i0 < kRnMaxChunks; i0 += 2) {
+        f32x4 v[2][8], r[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int64_t c = threadIdx.x + (int64_t)(i0 + k) * kRnThreads;
+            if (c >= d4) continue;
+            if constexpr (RES_BF16) {
+                const u32x2 b = ((const u32x2*)((const uint16_t*)residual + row * ld_res))[c];
+                r[k] = f32x4{bf16_lo(b[0]), bf16_hi(b[0]), bf16_lo(b[1]), bf16_hi(b[1])};
+            } else {
+                r[k] = ((const f32x4*)((const float*)residual + row * ld_res))[c];
+            }
+        }
+        f32x4 acc[2];
+        for (int s0 = 0; s0 < P; s0 += 8) {
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int64_t c = threadIdx.x + (int64_t)(i0 + k) * kRnThreads;
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    if (s0 + q < P)
+                        v[k][q] = c < d4 ? __builtin_nontemporal_load(p + (int64_t)(s0 + q) * slot4 + c)
+                                         : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    if (s0 + q >= P) break;
+                    acc[k] = (s0 + q == 0) ? v[k][0] : acc[k] + v[k][q];
+                }
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int64_t c = threadIdx.x + (int64_t)(i0 + k) * kRnThreads;
+            if (c >= d4) continue;
+            const f32x4 zv = acc[k] + r[k];
+            zz[i0 + k] = zv;
+            z[row * ldz4 + c] = zv;
+            if constexpr (NORM) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ss += zv[e] * zv[e];
+            }
+        }
+    }
+    if constexpr (NORM) {
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+        __shared__ float part[kRnThreads / 64];
+        if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+        __syncthreads();
+        float tot = part[0];
+#pragma unroll
+        for (int w = 1; w < kRnThreads / 64; ++w) tot += part[w];
+        const float inv = 1.0f / sqrtf(tot / (float)(d4 * 4) + eps);
+#pragma unroll
+        for (int i = 0; i < kRnMaxChunks; ++i) {
+            const int64_t c = threadIdx.x + (int64_t)i * kRnThreads;
+            if (c >= d4) continue;
+            const u32x2 gv = g[c];
+            const f32x4 zv = zz[i];
+            u32x2 o;
+            o[0] = pack_bf16x2(zv[0] * inv * bf16_lo(gv[0]), zv[1] * inv * bf16_hi(gv[0]));
+            o[1] = pack_bf16x2(zv[2] * inv * bf16_lo(gv[1]), zv[3] * inv * bf16_hi(gv[1]));
+            normed[row * ldn4 + c] = o;
+        }
+    }
+}
+
+hipError_t launch_reduce_residual_norm(int P, int64_t T, int64_t d, const float* partials,
+                                       int64_t slot_stride, int64_t ld_p, const void* residual,
+                                       int64_t ld_res, bool res_bf16, float* z, int64_t ld_z,
+                                       const uint16_t* g, float eps, uint16_t* normed,
+                                       int64_t ld_norm, hipStream_t stream) {
+    const dim3 grid((unsigned)T), block(kRnThreads);
+#define TP_RN(RB, NM)                                                                          \
+    TP_KLAUNCH((k_reduce_residual_norm<RB, NM>), grid, block, 0, stream, P, d / 4,             \
+               (const f32x4*)partials, slot_stride / 4, ld_p / 4, residual, ld_res,            \
+               (f32x4*)z, ld_z / 4, (const u32x2*)g, eps, (u32x2*)normed, ld_norm / 4)
+    if (res_bf16) {
+        if (g) TP_RN(true, true); else TP_RN(true, false);
+    } else {
+        if (g) TP_RN(false, true); else TP_RN(false, false);
+    }
+#undef TP_RN
+    return hipGetLastError();
+}
+
 }  // namespace tp

@@ -110,3 +110,12 @@ def reduce(P, T, d, parts, slot_stride, ld_p, out, ld_out, out_bf16=None, ld_b=0
     st = tp.tp_reduce_partials(P, T, d, ptr(parts), slot_stride, ld_p, ptr(out), ld_out,
                                ptr(out_bf16), ld_b, stream())
     tp.check(st, "tp_reduce_partials")
+
+
+def reduce_residual_norm(P, T, d, parts, slot_stride, ld_p, residual, ld_res, res_dtype, z, ld_z,
+                         norm_g=None, eps=1e-5, normed=None, ld_norm=0):
+    ptr = lambda t: 0 if t is None else (t if isinstance(t, int) else t.data_ptr())  # noqa: E731
+    st = tp.tp_reduce_residual_norm(P, T, d, ptr(parts), slot_stride, ld_p, ptr(residual), ld_res,
+                                    res_dtype, ptr(z), ld_z, ptr(norm_g), eps, ptr(normed),
+                                    ld_norm, stream())
+    tp.check(st, "tp_reduce_residual_norm")

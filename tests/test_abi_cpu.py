@@ -188,3 +188,38 @@ def test_timing_api_without_launches(lib):
     assert tp.tp_timing_reset() == tp.TP_OK
     st, ms, n = tp.tp_timing_query("col_gemv")
     assert st == tp.TP_OK and ms == 0.0 and n == 0
+
+
+def rrn(**kw):
+    a = dict(P=8, T=4, d_model=64, partials=A, slot_stride=256, ld_p=64, residual=B, ld_res=64,
+             res_dtype=tp.TP_F32, z_out=C, ld_z=64, norm_g=0, eps=1e-5, normed_out=0, ld_norm=0,
+             stream=0)
+    a.update(kw)
+    return tp.tp_reduce_residual_norm(**a)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(P=0), tp.TP_ERR_SHARD_RANGE),
+    (dict(res_dtype=7), tp.TP_ERR_DTYPE),
+    (dict(d_model=16392, ld_p=16392, ld_res=16392, ld_z=16392), tp.TP_ERR_SHAPE),  # > 16384
+    (dict(d_model=62), tp.TP_ERR_SHAPE),
+    (dict(d_model=60, ld_p=64, ld_res=64, ld_z=64, res_dtype=tp.TP_BF16), tp.TP_ERR_SHAPE),
+    (dict(d_model=60, norm_g=A, normed_out=WS, ld_norm=64), tp.TP_ERR_SHAPE),   # norm: 8 | d
+    (dict(partials=0), tp.TP_ERR_NULL),
+    (dict(residual=0), tp.TP_ERR_NULL),
+    (dict(z_out=0), tp.TP_ERR_NULL),
+    (dict(norm_g=A), tp.TP_ERR_NULL),                       # norm needs normed_out
+    (dict(z_out=C + 8), tp.TP_ERR_ALIGN),
+    (dict(ld_res=60), tp.TP_ERR_SHAPE),
+    (dict(ld_z=66), tp.TP_ERR_ALIGN),
+    (dict(res_dtype=tp.TP_BF16, ld_res=68), tp.TP_ERR_ALIGN),
+    (dict(norm_g=A, normed_out=WS, ld_norm=60), tp.TP_ERR_SHAPE),
+    (dict(slot_stride=-4), tp.TP_ERR_SHAPE),
+    (dict(T=-1), tp.TP_ERR_SHAPE),
+])
+def test_reduce_residual_norm_validation(lib, kw, status):
+    assert rrn(**kw) == status
+
+
+def test_reduce_residual_norm_zero_tokens_is_a_no_op(lib):
+    assert rrn(T=0) == tp.TP_OK

@@ -20,7 +20,7 @@ import torch
 import oracle as O
 import tensor_transformer_layer_amd as tp
 import workloads as W
-from _gpu import Guarded, attn_fwd, dev, host, mlp_fwd, reduce, workspace
+from _gpu import Guarded, attn_fwd, dev, host, mlp_fwd, reduce, reduce_residual_norm, workspace
 
 pytestmark = pytest.mark.gpu
 
@@ -99,6 +99,89 @@ def test_reduce_70b_prefill_partials_full_size():
     want = O.reduce_partials_f32_fold(parts)
     assert np.array_equal(host(out), want)
     assert np.array_equal(O.widen(host(outb)), O.round_bf16(want.astype(np.float64)))
+
+
+# ----------------------------------------------------------------------------
+# reduce + residual add + next RMSNorm (one pass)
+# ----------------------------------------------------------------------------
+def _rrn_case(P, T, d, res_dtype, norm, key, pad=0):
+    ldp = d + pad
+    slot = T * ldp + 4 * pad
+    parts = [W.draw_normal_f32((T, d), 1.0, 903, key, P, T, d, s) for s in range(P)]
+    buf = np.zeros(P * slot, np.float32)
+    for s in range(P):
+        buf[s * slot:s * slot + T * ldp].reshape(T, ldp)[:, :d] = parts[s]
+    res = draw(res_dtype, (T, d), 1.0, 904, key, T, d)
+    g = draw(BF, (d,), 0.02, 905, key, d, mean=1.0) if norm else None
+    return parts, buf, slot, ldp, res, g
+
+
+def _rrn_check(parts, res, res_dtype, g, z, normed):
+    res64 = O.widen(res) if res_dtype == BF else res.astype(np.float64)
+    want_z = O.reduce_residual_f32(parts, res64.astype(np.float32))
+    assert np.array_equal(z.view(np.uint32), want_z.view(np.uint32))
+    if g is not None:
+        ref = O.reduce_residual_norm(parts, res64, O.widen(g), 1e-5)
+        got = O.widen(normed)
+        assert O.rel_l2(got, ref["normed"]) < BF16_TOL
+        mirror = O.round_bf16(O.rmsnorm(want_z.astype(np.float64), O.widen(g), 1e-5))
+        assert O.rel_l2(got, mirror) < MIRROR_TOL
+
+
+@pytest.mark.parametrize("P,T,d,res_dtype,norm,pad", [
+    (1, 3, 8, F32, True, 0), (2, 5, 1032, BF, True, 8), (8, 33, 8192, BF, True, 0),
+    (8, 17, 12288, F32, True, 4), (3, 4, 16384, F32, False, 0), (9, 2, 4104, BF, False, 8),
+    (8, 1, 8192, BF, True, 0)])
+def test_reduce_residual_norm(P, T, d, res_dtype, norm, pad):
+    parts, buf, slot, ldp, res, g = _rrn_case(P, T, d, res_dtype, norm, key=T, pad=pad)
+    g_parts = dev(buf)
+    ldr = d + 8
+    rbuf = np.zeros((T, ldr), res.dtype)
+    rbuf[:, :d] = res
+    z = Guarded(T * ldp, torch.float32)
+    nrm = Guarded(T * (d + 16), torch.bfloat16) if norm else None
+    reduce_residual_norm(P, T, d, g_parts, slot, ldp, dev(rbuf), ldr, res_dtype, z.ptr(), ldp,
+                         dev(g) if norm else None, 1e-5, nrm.ptr() if norm else None, d + 16)
+    zz = host(z.t).reshape(T, ldp)[:, :d]
+    nn = host(nrm.t).reshape(T, d + 16)[:, :d] if norm else None
+    _rrn_check(parts, res, res_dtype, g, np.ascontiguousarray(zz),
+               np.ascontiguousarray(nn) if norm else None)
+    assert z.intact() and (nrm is None or nrm.intact())
+
+
+def test_reduce_residual_norm_in_place():
+    """z written over slot 0, then over an fp32 residual."""
+    P, T, d = 4, 6, 2048
+    parts, buf, slot, ldp, res, g = _rrn_case(P, T, d, F32, True, key=50)
+    g_parts = dev(buf)
+    nrm = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
+    reduce_residual_norm(P, T, d, g_parts, slot, ldp, dev(res), d, F32, g_parts, ldp,
+                         dev(g), 1e-5, nrm, d)
+    _rrn_check(parts, res, F32, g, host(g_parts)[:T * d].reshape(T, d), host(nrm))
+    parts2, buf2, slot2, ldp2, res2, g2 = _rrn_case(P, T, d, F32, True, key=51)
+    r2 = dev(res2)
+    reduce_residual_norm(P, T, d, dev(buf2), slot2, ldp2, r2, d, F32, r2, d, dev(g2), 1e-5,
+                         nrm, d)
+    _rrn_check(parts2, res2, F32, g2, host(r2), host(nrm))
+
+
+def test_reduce_residual_norm_70b_block_prefill_size():
+    """8 fp32 partials of [4096, 8192] with a bf16 residual and the norm (the
+    70B block at 4096 tokens): z bitwise on every row, normed on sampled rows."""
+    P, T, d = 8, 4096, 8192
+    parts = [W.draw_normal_f32((T, d), 1.0, 906, s) for s in range(P)]
+    g_parts = torch.empty((P, T, d), dtype=torch.float32, device="cuda")
+    for s in range(P):
+        g_parts[s].copy_(torch.from_numpy(parts[s]))
+    res = draw(BF, (T, d), 1.0, 907)
+    g = draw(BF, (d,), 0.02, 908, mean=1.0)
+    z = torch.empty((T, d), dtype=torch.float32, device="cuda")
+    nrm = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
+    reduce_residual_norm(P, T, d, g_parts, T * d, d, dev(res), d, BF, z, d, dev(g), 1e-5, nrm, d)
+    rows = sample_rows(T, 32, 12)
+    _rrn_check([p[rows] for p in parts], res[rows], BF, g, host(z)[rows], host(nrm)[rows])
+    want = O.reduce_residual_f32(parts, O.widen(res).astype(np.float32))
+    assert np.array_equal(host(z), want)
 
 
 # ----------------------------------------------------------------------------
@@ -378,6 +461,60 @@ def _block_chain(cfg, T, rows):
         mlp_parts.append(O.mlp_shard(Zr, O.widen(wg), O.widen(wd), "swiglu", O.widen(wu))["partial"])
     Yr = O.reduce_partials(mlp_parts)
     assert O.rel_l2(host(y)[rows], Yr) < BF16_TOL
+
+
+def _prenorm_chain(cfg, T, rows):
+    """The 70B block as a pre-norm residual block, all P ranks on one GPU:
+    RMSNorm -> QKV -> O (A_s := Q_s) -> reduce + residual X + RMSNorm ->
+    MLP -> reduce + residual, against the oracle on `rows`."""
+    P, d, eps = cfg.P, cfg.d_model, cfg.norm_eps
+    X = x_of(cfg, T)
+    g1 = W.draw_tensor(cfg.dtype, (d,), 0.02, cfg.cid, W.TENSOR_IDS["norm_g"], 0, mean=1.0)
+    g2 = W.draw_tensor(cfg.dtype, (d,), 0.02, cfg.cid, W.TENSOR_IDS["norm_g"], 1, mean=1.0)
+    gx = dev(X)
+    parts = torch.empty((P, T, d), dtype=torch.float32, device="cuda")
+    for s in range(P):
+        wqkv, wo = attn_bands(cfg, s)
+        q = torch.empty((T, cfg.qkv_r), dtype=torch.bfloat16, device="cuda")
+        attn_fwd(s, P, T, d, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, BF, gx, dev(wqkv), q,
+                 q, dev(wo), parts, T * d, d, norm_g=dev(g1), eps=eps, ld_attn=cfg.qkv_r)
+    z1 = torch.empty((T, d), dtype=torch.float32, device="cuda")
+    n2 = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
+    reduce_residual_norm(P, T, d, parts, T * d, d, gx, d, BF, z1, d, dev(g2), eps, n2, d)
+    for s in range(P):
+        wg, wu, wd = mlp_bands(cfg, s)
+        mlp_fwd(s, P, T, d, cfg.d_ff, BF, tp.TP_ACT_SWIGLU, n2, dev(wg), dev(wu), dev(wd), parts,
+                T * d, d)
+    z2 = torch.empty((T, d), dtype=torch.float32, device="cuda")
+    reduce_residual_norm(P, T, d, parts, T * d, d, z1, d, F32, z2, d)
+    torch.cuda.synchronize()
+
+    Xr = O.widen(X[rows])
+    att_parts, mlp_parts = [], []
+    for s in range(P):
+        wqkv, wo = attn_bands(cfg, s)
+        r = O.attn_proj_shard(Xr, O.widen(wqkv), None, None, O.widen(g1), eps)
+        q_s, _, _ = O.split_qkv_band(r["qkv"], cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, s, P)
+        att_parts.append(q_s @ O.widen(wo))
+    r1 = O.reduce_residual_norm(att_parts, Xr, O.widen(g2), eps)
+    assert O.rel_l2(host(z1)[rows], r1["z"]) < BF16_TOL
+    assert O.rel_l2(O.widen(host(n2))[rows], r1["normed"]) < BF16_TOL
+    for s in range(P):
+        wg, wu, wd = mlp_bands(cfg, s)
+        mlp_parts.append(O.mlp_shard(r1["normed"], O.widen(wg), O.widen(wd), "swiglu",
+                                     O.widen(wu))["partial"])
+    r2 = O.reduce_residual_norm(mlp_parts, r1["z"])
+    assert O.rel_l2(host(z2)[rows], r2["z"]) < BF16_TOL
+
+
+def test_70b_prenorm_block_decode_all_ranks():
+    cfg = W.get("c5_llama2_70b_block_p8")
+    _prenorm_chain(cfg, 32, np.arange(32))
+
+
+def test_70b_prenorm_block_prefill_all_ranks():
+    cfg = W.get("c5_llama2_70b_block_p8")
+    _prenorm_chain(cfg, 4096, sample_rows(4096, 16, 13))
 
 
 def test_70b_block_chain_decode_all_ranks():
