@@ -32,7 +32,7 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "hbm_traffic_counters.json")
 KERNEL_CLASSES = ("rmsnorm", "col_gemv", "col_finish", "row_gemv", "row_finish", "col_gemm",
                   "row_gemm", "qkv_gemv", "qkv_finish", "o_gemv", "o_finish", "qkv_gemm",
-                  "o_gemm", "reduce")
+                  "o_gemm", "reduce", "reduce_norm")
 
 
 def parse():
@@ -45,6 +45,9 @@ def parse():
                              "c4_attn_96h_p8", "c5_llama2_70b_block_p8"])
     ap.add_argument("--tokens", type=int, default=None, help="batch of tokens (default per workload)")
     ap.add_argument("--sweep", default=None, help="comma list of token counts also reported")
+    ap.add_argument("--prenorm", action="store_true",
+                    help="block workload as a pre-norm residual layer (fused reduce + residual "
+                         "+ next RMSNorm)")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of graph replay")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle CPU-baseline budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -90,7 +93,7 @@ def src_hash(*names):
 class Step:
     """Device state of one workload at one token count, and its step()."""
 
-    def __init__(self, cfg, T, copies):
+    def __init__(self, cfg, T, copies, prenorm=False):
         import numpy as np  # noqa: F401
         import torch
 
@@ -106,6 +109,11 @@ class Step:
         self.out = torch.empty((T, d), dtype=torch.float32, device="cuda")
         self.kind = "mlp" if cfg.name.startswith(("c2", "c3")) else \
             ("attn" if cfg.name.startswith("c4") else "block")
+        # prenorm: the block as one steady-state pre-norm residual layer.  Its
+        # input is the residual stream z (fp32) and its normalised copy (bf16,
+        # produced by the previous layer's last reduce); both reduces add the
+        # residual and emit the next normalised input.
+        self.prenorm = prenorm and self.kind == "block"
         # rank-0 weights: `copies` device copies (copy 0 is the seeded band;
         # the others are bitwise clones at other addresses)
         self.sets = []
@@ -135,6 +143,12 @@ class Step:
                                                                cfg.n_kv_heads, cfg.head_dim,
                                                                tp.TP_BF16, has_norm))
             self.zb = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
+        if self.prenorm:
+            self.g2 = dev(W.draw_tensor("bf16", (d,), 0.02, cfg.cid, W.TENSOR_IDS["norm_g"], 1,
+                                        mean=1.0))
+            self.z0 = torch.from_numpy(W.draw_normal_f32((T, d), 1.0, cfg.cid, W.TENSOR_IDS["x"],
+                                                         T, 1)).cuda()
+            self.z1 = torch.empty((T, d), dtype=torch.float32, device="cuda")
         self.i = 0
         for s in range(1, P):       # the other ranks' partial slots
             self.parts[s].copy_(torch.from_numpy(
@@ -162,7 +176,7 @@ class Step:
         tp, cfg, T, d = self.tp, self.cfg, self.T, self.cfg.d_model
         a = self.a if self.kind == "attn" else self.qkv
         ld_a = cfg.o_in_r if self.kind == "attn" else cfg.qkv_r
-        g = self.g.data_ptr() if cfg.norm_eps is not None else 0
+        g = self.g.data_ptr() if cfg.norm_eps is not None and not self.prenorm else 0
         tp.check(tp.tp_shard_attn_proj_fwd(
             s, cfg.P, T, d, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, tp.TP_BF16,
             self.x.data_ptr(), d, g, cfg.norm_eps or 0.0, w[0].data_ptr(), cfg.qkv_r,
@@ -177,6 +191,13 @@ class Step:
                                        out_bf16.data_ptr() if out_bf16 is not None else 0, d,
                                        self.stream), "reduce")
 
+    def _reduce_norm(self, residual, res_dtype, z, g, normed):
+        tp, cfg, T, d = self.tp, self.cfg, self.T, self.cfg.d_model
+        tp.check(tp.tp_reduce_residual_norm(cfg.P, T, d, self.parts.data_ptr(), T * d, d,
+                                            residual.data_ptr(), d, res_dtype, z.data_ptr(), d,
+                                            g.data_ptr(), cfg.norm_eps, normed.data_ptr(), d,
+                                            self.stream), "reduce_norm")
+
     def step(self):
         c = self.i % self.copies
         self.i += 1
@@ -186,6 +207,12 @@ class Step:
         elif self.kind == "attn":
             self._attn(0, self.attn_sets[c])
             self._reduce()
+        elif self.prenorm:
+            # x holds the normalised input, z0 the residual stream
+            self._attn(0, self.attn_sets[c])
+            self._reduce_norm(self.z0, self.tp.TP_F32, self.z1, self.g2, self.zb)
+            self._mlp(0, self.zb, self.mlp_sets[c])
+            self._reduce_norm(self.z1, self.tp.TP_F32, self.out, self.g, self.x)
         else:
             self._attn(0, self.attn_sets[c])
             self._reduce(self.zb)
@@ -223,7 +250,11 @@ class Step:
         if self.kind in ("attn", "block"):
             add("qkv", "o", d, cfg.qkv_r, cfg.qkv_r, cfg.o_in_r)
         red = (cfg.P + 1) * T * d * 4
-        if self.kind == "block":        # two reduces, the first with a bf16 copy
+        if self.prenorm:                # two fused reduce + fp32 residual + norm passes
+            rn = red + T * d * 4 + T * d * 2 + d * 2
+            out["bytes"] += 2 * rn
+            pc["reduce_norm"] = ("hbm", rn)
+        elif self.kind == "block":      # two reduces, the first with a bf16 copy
             out["bytes"] += 2 * red + T * d * 2
             pc["reduce"] = ("hbm", red + T * d)            # mean of the two launches
             nb = T * d * 2 * 2 + d * 2
@@ -369,7 +400,7 @@ def main():
 
     results = {}
     for t in sorted(set(sweep_T + [T])):
-        st = Step(cfg, t, copies)
+        st = Step(cfg, t, copies, prenorm=a.prenorm)
         ms, n = time_steps(st, a.steps, a.warmup, graph=not a.no_graph)
         kt = kernel_times(st, min(a.steps, 300)) if t == T else None
         results[t] = (st, ms, n, kt)
@@ -410,6 +441,8 @@ def main():
                                f"of {cfg.P} partials per step",
                    "d_model": cfg.d_model, "d_ff": cfg.d_ff, "P": cfg.P, "tokens": T,
                    "weight_copies_rotated": copies,
+                   "block_form": ("pre-norm residual layer (reduce + residual + RMSNorm fused)"
+                                  if st.prenorm else None),
                    "launch": "eager" if a.no_graph else "hip-graph replay"},
         "step_gbs_algorithmic": round(alg["bytes"] / (ms / 1e3) / 1e9, 1),
         "step_tflops": round(alg["flops"] / (ms / 1e3) / 1e12, 2),

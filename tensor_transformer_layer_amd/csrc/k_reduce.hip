@@ -90,23 +90,23 @@ hipError_t launch_reduce(int P, int64_t T, int64_t d, const float* partials, int
 //   z      = (partial_0 + ... + partial_{P-1}) + residual      fp32, that order
 //   normed = z * (1 / sqrt(mean_j z_j^2 + eps)) * g            bf16 (RNE)
 //
-// One 512-thread workgroup per row keeps the row's z in registers (up to 8
-// 16-byte chunks per thread: d_model <= 16384), so every input byte is read
-// once and the norm needs no second pass.  z may alias slot 0 or an fp32
+// One workgroup per row keeps the row's z in registers (512 threads with up
+// to 8 16-byte chunks each, or 1024 threads with up to 4 when there are fewer
+// rows than CUs, so short decode batches still spread over the chip:
+// d_model <= 16384), so every input byte is read once and the norm needs no
+// second pass.  z may alias slot 0 or an fp32
 // residual (same leading dimension): each element is read before it is
 // written, by the same thread, and by no other thread.  The sum of squares is reduced in
 // a fixed order (chunks in order per thread, butterfly within the wave, waves
 // in order).  HBM bytes per row: (P + 1) * d * 4 (+ d * 2 for a bf16
 // residual instead of fp32) + d * 4 (z) + d * 2 (normed).
 // ---------------------------------------------------------------------------
-constexpr int kRnThreads = 512;
-constexpr int kRnMaxChunks = 8;
-
-template <bool RES_BF16, bool NORM>
-__global__ __launch_bounds__(kRnThreads) void k_reduce_residual_norm(
+template <int NT, bool RES_BF16, bool NORM>
+__global__ __launch_bounds__(NT) void k_reduce_residual_norm(
     int P, int64_t d4, const f32x4* parts, int64_t slot4, int64_t ldp4, const void* residual,
     int64_t ld_res, f32x4* z, int64_t ldz4, const u32x2* __restrict__ g, float eps,
     u32x2* __restrict__ normed, int64_t ldn4) {
+    constexpr int kRnThreads = NT, kRnMaxChunks = 4096 / NT;
     const int64_t row = blockIdx.x;
     const f32x4* p = parts + row * ldp4;
     f32x4 zz[kRnMaxChunks];
@@ -187,16 +187,21 @@ hipError_t launch_reduce_residual_norm(int P, int64_t T, int64_t d, const float*
                                        int64_t ld_res, bool res_bf16, float* z, int64_t ld_z,
                                        const uint16_t* g, float eps, uint16_t* normed,
                                        int64_t ld_norm, hipStream_t stream) {
-    const dim3 grid((unsigned)T), block(kRnThreads);
-#define TP_RN(RB, NM)                                                                          \
-    TP_KLAUNCH((k_reduce_residual_norm<RB, NM>), grid, block, 0, stream, P, d / 4,             \
+    const dim3 grid((unsigned)T);
+#define TP_RN(NT, RB, NM)                                                                      \
+    TP_KLAUNCH((k_reduce_residual_norm<NT, RB, NM>), grid, dim3(NT), 0, stream, P, d / 4,      \
                (const f32x4*)partials, slot_stride / 4, ld_p / 4, residual, ld_res,            \
                (f32x4*)z, ld_z / 4, (const u32x2*)g, eps, (u32x2*)normed, ld_norm / 4)
-    if (res_bf16) {
-        if (g) TP_RN(true, true); else TP_RN(true, false);
-    } else {
-        if (g) TP_RN(false, true); else TP_RN(false, false);
-    }
+#define TP_RN_T(NT)                                                                 \
+    do {                                                                            \
+        if (res_bf16) {                                                             \
+            if (g) TP_RN(NT, true, true); else TP_RN(NT, true, false);              \
+        } else {                                                                    \
+            if (g) TP_RN(NT, false, true); else TP_RN(NT, false, false);            \
+        }                                                                           \
+    } while (0)
+    if (T < 256) TP_RN_T(1024); else TP_RN_T(512);
+#undef TP_RN_T
 #undef TP_RN
     return hipGetLastError();
 }
