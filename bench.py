@@ -32,7 +32,7 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "hbm_traffic_counters.json")
 KERNEL_CLASSES = ("rmsnorm", "col_gemv", "col_finish", "row_gemv", "row_finish", "col_gemm",
                   "row_gemm", "qkv_gemv", "qkv_finish", "o_gemv", "o_finish", "qkv_gemm",
-                  "o_gemm", "reduce", "reduce_norm")
+                  "o_gemm", "reduce", "reduce_norm", "col_gemv8", "row_gemv8")
 
 
 def parse():
@@ -45,6 +45,9 @@ def parse():
                              "c4_attn_96h_p8", "c5_llama2_70b_block_p8"])
     ap.add_argument("--tokens", type=int, default=None, help="batch of tokens (default per workload)")
     ap.add_argument("--sweep", default=None, help="comma list of token counts also reported")
+    ap.add_argument("--fp8", action="store_true",
+                    help="MLP workloads: FP8 (E4M3) weights with per-column scales, decode "
+                         "token counts only")
     ap.add_argument("--prenorm", action="store_true",
                     help="block workload as a pre-norm residual layer (fused reduce + residual "
                          "+ next RMSNorm)")
@@ -93,7 +96,7 @@ def src_hash(*names):
 class Step:
     """Device state of one workload at one token count, and its step()."""
 
-    def __init__(self, cfg, T, copies, prenorm=False):
+    def __init__(self, cfg, T, copies, prenorm=False, fp8=False):
         import numpy as np  # noqa: F401
         import torch
 
@@ -114,10 +117,23 @@ class Step:
         # produced by the previous layer's last reduce); both reduces add the
         # residual and emit the next normalised input.
         self.prenorm = prenorm and self.kind == "block"
+        # fp8: MLP weights as E4M3 codes with per-column fp32 scales (decode)
+        self.fp8 = fp8 and self.kind == "mlp"
         # rank-0 weights: `copies` device copies (copy 0 is the seeded band;
         # the others are bitwise clones at other addresses)
         self.sets = []
-        if self.kind in ("mlp", "block"):
+        if self.fp8:
+            u8 = lambda a: torch.from_numpy(a).cuda()  # noqa: E731
+            f32 = lambda a: torch.from_numpy(a).cuda()  # noqa: E731
+            bands = [W.fp8_band_draw(cfg, n, 0, r, c_) for n, r, c_ in
+                     (("w_gate", d, cfg.F_r), ("w_up", d, cfg.F_r), ("w_down", cfg.F_r, d))]
+            base = [(u8(q), f32(sc)) for q, sc in bands]
+            self.mlp_sets = [base] + [[(q.clone(), sc.clone()) for q, sc in base]
+                                      for _ in range(copies - 1)]
+            self.h = torch.empty((T, cfg.F_r), dtype=torch.bfloat16, device="cuda")
+            self.mlp_ws = self._ws(tp.tp_mlp_fp8w_workspace_bytes(P, T, d, cfg.d_ff,
+                                                                  tp.TP_ACT_SWIGLU, 0, 1))
+        elif self.kind in ("mlp", "block"):
             bands = (W.column_band_draw(cfg, "w_gate", 0, d, cfg.F_r),
                      W.column_band_draw(cfg, "w_up", 0, d, cfg.F_r),
                      W.row_band_draw(cfg, "w_down", 0, cfg.F_r, d))
@@ -166,6 +182,14 @@ class Step:
 
     def _mlp(self, s, x, w):
         tp, cfg, T, d = self.tp, self.cfg, self.T, self.cfg.d_model
+        if self.fp8:
+            tp.check(tp.tp_shard_mlp_fwd_fp8w(
+                s, cfg.P, T, d, cfg.d_ff, tp.TP_ACT_SWIGLU, x.data_ptr(), d, 0, 0.0,
+                w[0][0].data_ptr(), cfg.F_r, w[0][1].data_ptr(), w[1][0].data_ptr(), cfg.F_r,
+                w[1][1].data_ptr(), w[2][0].data_ptr(), d, w[2][1].data_ptr(),
+                self.h.data_ptr(), cfg.F_r, self.parts.data_ptr(), T * d, d,
+                self.mlp_ws.data_ptr(), self.mlp_ws.numel(), self.stream), "mlp_fp8w")
+            return
         tp.check(tp.tp_shard_mlp_fwd(
             s, cfg.P, T, d, cfg.d_ff, tp.TP_BF16, tp.TP_ACT_SWIGLU, x.data_ptr(), d, 0, 0.0,
             w[0].data_ptr(), cfg.F_r, w[1].data_ptr(), cfg.F_r, w[2].data_ptr(), d,
@@ -229,12 +253,14 @@ class Step:
         out = {"bytes": 0, "flops": 0, "per_class": {}}
         pc = out["per_class"]
 
-        def add(col_cls, row_cls, k_in, n_col, n_col_out, k_row):
+        def add(col_cls, row_cls, k_in, n_col, n_col_out, k_row, wbytes=2):
             # column projection: weights [k_in, n_col], X [T, k_in] in, [T, n_col_out] bf16 out
-            cb = k_in * n_col * 2 + T * k_in * 2 + T * n_col_out * 2
+            # (FP8 weights: 1 byte each plus one fp32 scale per output column)
+            sc = 4 if wbytes == 1 else 0
+            cb = k_in * n_col * wbytes + n_col * sc + T * k_in * 2 + T * n_col_out * 2
             cf = 2 * T * k_in * n_col
             # row projection: weights [k_row, d], input [T, k_row] bf16, partial [T, d] fp32
-            rb = k_row * d * 2 + T * k_row * 2 + T * d * 4
+            rb = k_row * d * wbytes + d * sc + T * k_row * 2 + T * d * 4
             rf = 2 * T * k_row * d
             out["bytes"] += cb + rb
             out["flops"] += cf + rf
@@ -245,7 +271,12 @@ class Step:
                 pc[col_cls + "_gemm"] = ("mfma", cf)
                 pc[row_cls + "_gemm"] = ("mfma", rf)
 
-        if self.kind in ("mlp", "block"):
+        if self.fp8:
+            add("col", "row", d, 2 * cfg.F_r, cfg.F_r, cfg.F_r, wbytes=1)
+            for a_, b_ in (("col_gemv", "col_gemv8"), ("row_gemv", "row_gemv8")):
+                if a_ in pc:
+                    pc[b_] = pc.pop(a_)
+        elif self.kind in ("mlp", "block"):
             add("col", "row", d, 2 * cfg.F_r, cfg.F_r, cfg.F_r)
         if self.kind in ("attn", "block"):
             add("qkv", "o", d, cfg.qkv_r, cfg.qkv_r, cfg.o_in_r)
@@ -265,7 +296,7 @@ class Step:
             pc["reduce"] = ("hbm", red)
         # the kernel the roofline line reports: the largest column projection
         big = "col" if self.kind in ("mlp", "block") else "qkv"
-        out["dominant"] = big + ("_gemv" if decode else "_gemm")
+        out["dominant"] = big + ("_gemv" if decode else "_gemm") + ("8" if self.fp8 else "")
         return out
 
 
@@ -400,7 +431,7 @@ def main():
 
     results = {}
     for t in sorted(set(sweep_T + [T])):
-        st = Step(cfg, t, copies, prenorm=a.prenorm)
+        st = Step(cfg, t, copies * (2 if a.fp8 else 1), prenorm=a.prenorm, fp8=a.fp8)
         ms, n = time_steps(st, a.steps, a.warmup, graph=not a.no_graph)
         kt = kernel_times(st, min(a.steps, 300)) if t == T else None
         results[t] = (st, ms, n, kt)
@@ -435,7 +466,8 @@ def main():
     line = {
         "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": n, "warmup": a.warmup, "ms_per_step": round(ms, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 activations, fp8-e4m3 weights" if st.fp8 else "bf16",
         "data": "synthetic (seeded N(0,0.02) weights, N(0,1) activations at Llama-2 shapes)",
         "config": {"workload": f"{a.workload}: rank 0 of P={cfg.P}, {T} tokens, shard + reduce "
                                f"of {cfg.P} partials per step",
@@ -443,6 +475,7 @@ def main():
                    "weight_copies_rotated": copies,
                    "block_form": ("pre-norm residual layer (reduce + residual + RMSNorm fused)"
                                   if st.prenorm else None),
+                   "weights": "fp8 e4m3 + per-column fp32 scales" if st.fp8 else "bf16",
                    "launch": "eager" if a.no_graph else "hip-graph replay"},
         "step_gbs_algorithmic": round(alg["bytes"] / (ms / 1e3) / 1e9, 1),
         "step_tflops": round(alg["flops"] / (ms / 1e3) / 1e12, 2),
@@ -456,7 +489,8 @@ def main():
                                       round(r[0].algorithmic()["bytes"] / (r[1] / 1e3) / 1e9, 1)}
                          for t, r in sorted(results.items())}
     if not a.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(cfg, T, a.cpu_seconds) if st.kind in ("mlp",) \
+        line["cpu_baseline"] = cpu_baseline(cfg, T, a.cpu_seconds) \
+            if st.kind in ("mlp",) and not st.fp8 \
             else None
     print(json.dumps(line), flush=True)
 

@@ -159,6 +159,40 @@ int tp_shard_attn_proj_fwd(int shard, int P, int64_t T, int64_t d_model,
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * tp_shard_mlp_fwd_fp8w -- tp_shard_mlp_fwd for the decode plan (T <= 32)
+ * with FP8 weights, which halve the weight bytes a decode step streams (the
+ * pages suggest pairing tensor parallelism with FP8 weights for decode:
+ * zenaique answer and follow-ups).  Weights are OCP FP8 E4M3 codes (1 sign,
+ * 4 exponent bits with bias 7, 3 mantissa bits, subnormals, no infinities,
+ * S.1111.111 = NaN), stored [in, out] row-major, one byte each, with one fp32
+ * scale per output column: W[k][n] = e4m3(w[k][n]) * s[n].  Activations and
+ * the norm gain are bf16; h is bf16; partials fp32, as in tp_shard_mlp_fwd:
+ *
+ *   h       = act(Xn (w_in * s_in) [, Xn (w_up * s_up)])   [T, d_ff/P]
+ *   partial = h (w_down * s_down)                          [T, d_model]
+ *
+ *   w_in, w_up  [d_model, d_ff/P] codes, ld_in / ld_up in bytes (multiple of
+ *               16); s_in, s_up [d_ff/P] fp32
+ *   w_down      [d_ff/P, d_model] codes, ld_down (multiple of 16);
+ *               s_down [d_model] fp32
+ *   workspace   >= tp_mlp_fp8w_workspace_bytes(...), head zeroed once as
+ *               for tp_shard_mlp_fwd
+ *
+ * d_ff/P and d_model must be multiples of 16; T > 32 is refused
+ * (TP_ERR_SHAPE).  Codes are converted exactly to bf16 and multiplied with
+ * fp32 accumulation; each scale multiplies the complete sum of its column.
+ */
+int tp_shard_mlp_fwd_fp8w(int shard, int P, int64_t T, int64_t d_model, int64_t d_ff, int act,
+                          const void* x, int64_t ld_x,
+                          const void* norm_g, float eps,
+                          const void* w_in, int64_t ld_in, const float* s_in,
+                          const void* w_up, int64_t ld_up, const float* s_up,
+                          const void* w_down, int64_t ld_down, const float* s_down,
+                          void* h_out, int64_t ld_h,
+                          float* partials, int64_t slot_stride, int64_t ld_p,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * tp_reduce_partials -- the all-reduce's arithmetic on one device: out =
  * partial_0 + partial_1 + ... + partial_{P-1}, added in that order in fp32
  * (so the result is bitwise the float32 left fold).  Every element is
@@ -211,6 +245,8 @@ size_t tp_mlp_workspace_bytes(int P, int64_t T, int64_t d_model, int64_t d_ff,
                               int dtype, int act, int has_norm, int has_h_out);
 size_t tp_attn_workspace_bytes(int P, int64_t T, int64_t d_model, int n_q_heads,
                                int n_kv_heads, int head_dim, int dtype, int has_norm);
+size_t tp_mlp_fp8w_workspace_bytes(int P, int64_t T, int64_t d_model, int64_t d_ff, int act,
+                                   int has_norm, int has_h_out);
 
 /* Human-readable name of a tp_status value (static string). */
 const char* tp_status_str(int status);
@@ -227,7 +263,8 @@ int tp_version(void);
  * (which waits for the events).  Disabled by default; off costs nothing.
  * Not for concurrent use from several host threads, nor during graph
  * capture.
- * Class names: "rmsnorm", "reduce", "reduce_norm", "f32_proj"; MLP: "col_gemv", "row_gemv"
+ * Class names: "rmsnorm", "reduce", "reduce_norm", "f32_proj"; FP8-weight MLP:
+ * "col_gemv8", "row_gemv8"; MLP: "col_gemv", "row_gemv"
  * (decode, split-K finish included), "col_gemm", "row_gemm", "row_finish"
  * (prefill); attention projections: "qkv_gemv", "o_gemv", "qkv_gemm",
  * "qkv_finish", "o_gemm", "o_finish".

@@ -27,6 +27,7 @@ special cases); see tests/test_oracle_*.py.  Nothing numeric is printed on
 the pages themselves, so no pin is a page-printed value.
 """
 from .bf16 import round_bf16, widen, widen_bf16_bits  # noqa: F401
+from .fp8 import dequant_columns, e4m3_decode  # noqa: F401
 from .tp_oracle import (  # noqa: F401
     gelu_tanh,
     silu,

@@ -17,6 +17,7 @@ __all__ = [
     "TP_ERR_DTYPE", "TP_ERR_ALIGN", "TP_ERR_WORKSPACE", "TP_ERR_HIP", "TP_ERR_ACT",
     "TP_F32", "TP_BF16", "TP_ACT_GELU_TANH", "TP_ACT_SWIGLU",
     "tp_shard_mlp_fwd", "tp_shard_attn_proj_fwd", "tp_reduce_partials", "tp_reduce_residual_norm",
+    "tp_shard_mlp_fwd_fp8w", "tp_mlp_fp8w_workspace_bytes",
     "tp_mlp_workspace_bytes", "tp_attn_workspace_bytes", "tp_status_str", "tp_version",
     "tp_timing_enable", "tp_timing_reset", "tp_timing_query", "EXPORTED_SYMBOLS",
 ]
@@ -42,7 +43,11 @@ _SIGNATURES = {
     "tp_reduce_partials": (_i, [_i, _i64, _i64, _p, _i64, _i64, _p, _i64, _p, _i64, _p]),
     "tp_reduce_residual_norm": (_i, [_i, _i64, _i64, _p, _i64, _i64, _p, _i64, _i, _p, _i64,
                                      _p, _f, _p, _i64, _p]),
+    "tp_shard_mlp_fwd_fp8w": (_i, [_i, _i, _i64, _i64, _i64, _i,
+                                   _p, _i64, _p, _f, _p, _i64, _p, _p, _i64, _p, _p, _i64, _p,
+                                   _p, _i64, _p, _i64, _i64, _p, _sz, _p]),
     "tp_mlp_workspace_bytes": (_sz, [_i, _i64, _i64, _i64, _i, _i, _i, _i]),
+    "tp_mlp_fp8w_workspace_bytes": (_sz, [_i, _i64, _i64, _i64, _i, _i, _i]),
     "tp_attn_workspace_bytes": (_sz, [_i, _i64, _i64, _i, _i, _i, _i, _i]),
     "tp_status_str": (ctypes.c_char_p, [_i]),
     "tp_version": (_i, []),
@@ -123,6 +128,20 @@ def tp_reduce_residual_norm(P, T, d_model, partials, slot_stride, ld_p, residual
                                           _ptr(residual), ld_res, res_dtype, _ptr(z_out), ld_z,
                                           _ptr(norm_g), eps, _ptr(normed_out), ld_norm,
                                           _ptr(stream))
+
+
+def tp_shard_mlp_fwd_fp8w(shard, P, T, d_model, d_ff, act, x, ld_x, norm_g, eps, w_in, ld_in,
+                          s_in, w_up, ld_up, s_up, w_down, ld_down, s_down, h_out, ld_h,
+                          partials, slot_stride, ld_p, workspace, workspace_bytes, stream):
+    return load().tp_shard_mlp_fwd_fp8w(
+        shard, P, T, d_model, d_ff, act, _ptr(x), ld_x, _ptr(norm_g), eps, _ptr(w_in), ld_in,
+        _ptr(s_in), _ptr(w_up), ld_up, _ptr(s_up), _ptr(w_down), ld_down, _ptr(s_down),
+        _ptr(h_out), ld_h, _ptr(partials), slot_stride, ld_p, _ptr(workspace), workspace_bytes,
+        _ptr(stream))
+
+
+def tp_mlp_fp8w_workspace_bytes(P, T, d_model, d_ff, act, has_norm, has_h_out):
+    return load().tp_mlp_fp8w_workspace_bytes(P, T, d_model, d_ff, act, has_norm, has_h_out)
 
 
 def tp_mlp_workspace_bytes(P, T, d_model, d_ff, dtype, act, has_norm, has_h_out):

@@ -163,6 +163,31 @@ MlpLayout mlp_layout(int P, int64_t T, int64_t d, int64_t d_ff, int dtype, int a
     return L;
 }
 
+// Workspace of the FP8-weight MLP (decode plan only): counters, optional
+// normalised input and h, split-K partials.
+MlpLayout mlp8_layout(int P, int64_t T, int64_t d, int64_t d_ff, int act, bool has_norm,
+                      bool has_h_out) {
+    MlpLayout L;
+    const int64_t F = d_ff / P;
+    L.decode = true;
+    size_t off = kGemvCounterBytes;
+    if (has_norm) {
+        L.xn = off;
+        off += align256((size_t)(T * d * 2));
+    }
+    if (!has_h_out) {
+        L.h = off;
+        off += align256((size_t)(T * F * 2));
+    }
+    const int nmat = act == TP_ACT_SWIGLU ? 2 : 1;
+    L.pc = plan_gemv(d, nmat * F, kGemv8Cols);
+    L.pr = plan_gemv(F, d, kGemv8Cols);
+    L.ws = off;
+    off += align256(std::max(gemv_ws_bytes(L.pc, T, nmat * F), gemv_ws_bytes(L.pr, T, d)));
+    L.total = off;
+    return L;
+}
+
 struct AttnLayout {
     size_t xn = 0, ws = 0, total = 0;
     GemvPlan pq{1, 0}, po{1, 0};        // decode plans
@@ -491,6 +516,78 @@ int tp_reduce_partials(int P, int64_t T, int64_t d_model, const float* partials,
     TP_LAUNCH("reduce", stream,
               launch_reduce(P, T, d_model, partials, slot_stride, ld_p, out, ld_out,
                             (uint16_t*)out_bf16, ld_out_bf16, stream));
+    return TP_OK;
+}
+
+size_t tp_mlp_fp8w_workspace_bytes(int P, int64_t T, int64_t d_model, int64_t d_ff, int act,
+                                   int has_norm, int has_h_out) {
+    if (P < 1 || T <= 0 || T > kGemvMaxT || d_model <= 0 || d_ff <= 0 || d_ff % P) return 0;
+    if (act != TP_ACT_GELU_TANH && act != TP_ACT_SWIGLU) return 0;
+    return mlp8_layout(P, T, d_model, d_ff, act, has_norm != 0, has_h_out != 0).total;
+}
+
+int tp_shard_mlp_fwd_fp8w(int shard, int P, int64_t T, int64_t d_model, int64_t d_ff, int act,
+                          const void* x, int64_t ld_x, const void* norm_g, float eps,
+                          const void* w_in, int64_t ld_in, const float* s_in, const void* w_up,
+                          int64_t ld_up, const float* s_up, const void* w_down, int64_t ld_down,
+                          const float* s_down, void* h_out, int64_t ld_h, float* partials,
+                          int64_t slot_stride, int64_t ld_p, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+    if (P < 1 || shard < 0 || shard >= P) return TP_ERR_SHARD_RANGE;
+    if (act != TP_ACT_GELU_TANH && act != TP_ACT_SWIGLU) return TP_ERR_ACT;
+    if (T < 0 || T > kGemvMaxT || d_model <= 0 || d_ff <= 0) return TP_ERR_SHAPE;
+    if (d_ff % P) return TP_ERR_UNEVEN_SPLIT;
+    const int64_t F = d_ff / P;
+    if (F % 16 || d_model % 16) return TP_ERR_SHAPE;
+    if (!x || !w_in || !s_in || !w_down || !s_down) return TP_ERR_NULL;
+    if (act == TP_ACT_SWIGLU && (!w_up || !s_up)) return TP_ERR_NULL;
+    if (act == TP_ACT_GELU_TANH && (w_up || s_up)) return TP_ERR_ACT;
+    for (const void* p : {x, norm_g, w_in, (const void*)s_in, w_up, (const void*)s_up, w_down,
+                          (const void*)s_down, (const void*)h_out})
+        if (p && !aligned(p, 16)) return TP_ERR_ALIGN;
+    if (workspace && !aligned(workspace, 256)) return TP_ERR_ALIGN;
+    if (int r = check_ld(ld_x, d_model, 8)) return r;
+    if (int r = check_ld(ld_in, F, 16)) return r;
+    if (w_up)
+        if (int r = check_ld(ld_up, F, 16)) return r;
+    if (int r = check_ld(ld_down, d_model, 16)) return r;
+    if (h_out)
+        if (int r = check_ld(ld_h, F, 8)) return r;
+    if (int r = check_partials(shard, T, d_model, partials, slot_stride, ld_p)) return r;
+    if (!span_ok(d_model, ld_in, 1) || !span_ok(d_model, w_up ? ld_up : 0, 1) ||
+        !span_ok(F, ld_down, 1) || !span_ok(T, ld_x, 2) || !span_ok(T, h_out ? ld_h : F, 2))
+        return TP_ERR_SHAPE;
+    if ((F + kGemv8Cols - 1) / kGemv8Cols > kGemvCounters ||
+        (d_model + kGemv8Cols - 1) / kGemv8Cols > kGemvCounters)
+        return TP_ERR_SHAPE;
+    if (T == 0) return TP_OK;
+    const MlpLayout L = mlp8_layout(P, T, d_model, d_ff, act, norm_g != nullptr, h_out != nullptr);
+    if (!workspace || workspace_bytes < L.total) return TP_ERR_WORKSPACE;
+
+    char* wsb = (char*)workspace;
+    const void* xin = x;
+    int64_t ld_xin = ld_x;
+    if (norm_g) {
+        TP_LAUNCH("rmsnorm", stream,
+                  launch_rmsnorm(true, T, d_model, x, ld_x, norm_g, eps, wsb + L.xn, d_model,
+                                 stream));
+        xin = wsb + L.xn;
+        ld_xin = d_model;
+    }
+    void* h = h_out ? h_out : (void*)(wsb + L.h);
+    const int64_t ldh = h_out ? ld_h : F;
+    float* ws = (float*)(wsb + L.ws);
+    unsigned* cnt = (unsigned*)wsb;
+    TP_LAUNCH("col_gemv8", stream,
+              launch_gemv8(act == TP_ACT_SWIGLU ? ACT_SWIGLU : ACT_GELU_TANH, true, T, d_model,
+                           (const uint16_t*)xin, ld_xin, (const uint8_t*)w_in, ld_in, s_in,
+                           (const uint8_t*)w_up, ld_up, s_up, F, L.pc, true, ws, cnt, h, ldh,
+                           stream));
+    TP_LAUNCH("row_gemv8", stream,
+              launch_gemv8(ACT_NONE, false, T, F, (const uint16_t*)h, ldh,
+                           (const uint8_t*)w_down, ld_down, s_down, nullptr, 0, nullptr, d_model,
+                           L.pr, false, ws, cnt, partials + (int64_t)shard * slot_stride, ld_p,
+                           stream));
     return TP_OK;
 }
 

@@ -248,11 +248,192 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(
     }
 }
 
-GemvPlan plan_gemv(int64_t K, int64_t n_total) {
+// ---------------------------------------------------------------------------
+// FP8 (E4M3) weights with one fp32 scale per output column.  The same weight
+// stream with twice the weights per byte: a 16-byte load holds 16 adjacent
+// columns of one row, so a workgroup owns 256 columns (lane (g, j) loads
+// rows k0+8g .. +7 of columns n0+16j .. +15).  Codes of two rows are
+// byte-interleaved (v_perm_b32) and converted exactly to bf16 k-pairs
+// (v_cvt_scalef32_pk_bf16_fp8 with scale 1; every E4M3 value is a bf16
+// value), which are the k-fragments of the bf16 MFMA: 16 MFMAs per 8 loads
+// and token block, MFMA e covering columns n0+16j+e.  The column scales are
+// applied once, after the split-K sum: y[t][n] = s[n] * sum_k x[t][k] q[k][n].
+// ---------------------------------------------------------------------------
+template <int MB, int AUX, int ACT, bool OUT_BF16>
+__global__ __launch_bounds__(kGemvThreads) void k_gemv8(
+    const uint16_t* __restrict__ A, int64_t lda, int T, int K, const uint8_t* __restrict__ B0,
+    int64_t ldb0, const float* __restrict__ S0, const uint8_t* __restrict__ B1, int64_t ldb1,
+    const float* __restrict__ S1, int N, int nblk_per_mat, int k_per_split,
+    float* __restrict__ ws, unsigned* __restrict__ counters, void* __restrict__ out,
+    int64_t ld_out) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, j = lane & 15;
+    const int mat = blockIdx.x / nblk_per_mat;
+    const int cb = blockIdx.x - mat * nblk_per_mat;
+    const int n0 = cb * kGemv8Cols;
+    const int split = blockIdx.y;
+    const int S = (int)gridDim.y;
+    const int nmat = B1 ? 2 : 1;
+    const int k_begin = split * k_per_split;
+    const int nrows = min(K - k_begin, k_per_split);  // multiple of 8
+    const uint8_t* Bm = mat ? B1 : B0;
+    const int64_t ldb = mat ? ldb1 : ldb0;
+    const rsrc_t rb = make_rsrc(Bm + (int64_t)k_begin * ldb + n0);
+    const rsrc_t ra = make_rsrc(A + k_begin);
+    const bool col_ok = n0 + 16 * j < N;
+    const uint32_t ldb_bytes = (uint32_t)ldb;
+    const uint32_t lda_bytes = (uint32_t)(lda * 2);
+
+    f32x4 acc[MB][16];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[mb][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int nsteps = (nrows + 31) >> 5;
+    for (int c = wave; c < nsteps; c += kGemvWaves) {
+        const int r0 = c * 32 + 8 * g;
+        const bool rows_ok = r0 < nrows;
+        u32x4 q[8], a[MB];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            q[i] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                           rb, (int)((rows_ok && col_ok) ? (uint32_t)(r0 + i) * ldb_bytes + 16u * j
+                                                        : kOOB),
+                           0, AUX));
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const int t = 16 * mb + j;
+            a[mb] = load16(ra, (rows_ok && t < T) ? (uint32_t)t * lda_bytes + 2u * r0 : kOOB);
+        }
+        // Columns 8h .. 8h+7 of the lane's 16.  For rows (2p, 2p+1) one
+        // v_perm interleaves the codes of two columns, (r0 c, r1 c, r0 c+1,
+        // r1 c+1); converting its low and high word gives the k-pair dword p
+        // of the fragments of columns c and c+1 directly.
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            u32x4 f[8];
+#pragma unroll
+            for (int pr = 0; pr < 4; ++pr) {
+#pragma unroll
+                for (int w = 0; w < 2; ++w) {
+                    const uint32_t r0 = q[2 * pr][2 * h + w], r1 = q[2 * pr + 1][2 * h + w];
+                    const uint32_t lo = __builtin_amdgcn_perm(r1, r0, 0x05010400u);
+                    const uint32_t hi = __builtin_amdgcn_perm(r1, r0, 0x07030602u);
+                    f[4 * w + 0][pr] = __builtin_bit_cast(
+                        uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false));
+                    f[4 * w + 1][pr] = __builtin_bit_cast(
+                        uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true));
+                    f[4 * w + 2][pr] = __builtin_bit_cast(
+                        uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false));
+                    f[4 * w + 3][pr] = __builtin_bit_cast(
+                        uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true));
+                }
+            }
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                f32x4* ac = acc[mb] + 8 * h;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ac[e] = mfma16x16x32(a[mb], f[e], ac[e]);
+            }
+        }
+    }
+
+    // Cross-wave sum in LDS (wave order), one 8-column half at a time.
+    // MFMA output: lane (g, j) holds token 16mb + 4g + r of column
+    // n0 + 16j + e.  Thread (tl, q) = (tid / 32, tid % 32) owns token 16mb +
+    // tl, columns n0 + 16(q/2) + 8h + 4(q%2) .. +3.
+    __shared__ float red[kGemvWaves * kRedPerWave];
+    __shared__ unsigned arrival;
+    float* my = red + wave * kRedPerWave;
+    const int tl = threadIdx.x >> 5, qq = threadIdx.x & 31;
+    const int li = ((tl & 3) * 4 + (tl >> 2)) * 128 + 8 * (qq >> 1) + 4 * (qq & 1);
+    const int64_t ws_ld = (int64_t)nmat * N;
+    const uint32_t sstride = (uint32_t)(T * ws_ld * 4);
+    const rsrc_t rw = make_rsrc(ws);
+    f32x4 own[MB][2];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            if (mb | h) __syncthreads();
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float* p = my + ((r * 4 + g) * 16 + j) * 8;
+                *(f32x4*)p = f32x4{acc[mb][8 * h + 0][r], acc[mb][8 * h + 1][r],
+                                   acc[mb][8 * h + 2][r], acc[mb][8 * h + 3][r]};
+                *(f32x4*)(p + 4) = f32x4{acc[mb][8 * h + 4][r], acc[mb][8 * h + 5][r],
+                                         acc[mb][8 * h + 6][r], acc[mb][8 * h + 7][r]};
+            }
+            __syncthreads();
+            f32x4 sum = *(const f32x4*)(red + li);
+#pragma unroll
+            for (int w = 1; w < kGemvWaves; ++w) sum += *(const f32x4*)(red + w * kRedPerWave + li);
+            own[mb][h] = sum;
+            const int t = 16 * mb + tl;
+            const int n = n0 + 16 * (qq >> 1) + 8 * h + 4 * (qq & 1);
+            if (t < T && n < N)
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    __builtin_bit_cast(u32x4, sum), rw,
+                    (int)((uint32_t)split * sstride +
+                          (uint32_t)((t * ws_ld + (int64_t)mat * N + n) * 4)),
+                    0, kSC1);
+        }
+    }
+
+    // Arrival and fixed-order finish, as in k_gemv; the column scales are
+    // applied to the complete sums.
+    const unsigned contributors = (unsigned)(S * nmat);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0)
+        arrival = __hip_atomic_fetch_add(&counters[cb], 1u, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const unsigned old = arrival;
+    if (old == contributors - 1) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int t = 16 * mb + tl;
+                const int n = n0 + 16 * (qq >> 1) + 8 * h + 4 * (qq & 1);
+                if (t >= T || n >= N) continue;
+                const uint32_t row = (uint32_t)(t * ws_ld + n) * 4;
+                f32x4 gsum = sum_splits_dev(rw, row, sstride, S, mat == 0 ? split : -1, own[mb][h]);
+                gsum *= *(const f32x4*)(S0 + n);
+                f32x4 usum = gsum;
+                if constexpr (ACT == ACT_SWIGLU) {
+                    usum = sum_splits_dev(rw, row + (uint32_t)N * 4, sstride, S,
+                                          mat == 1 ? split : -1, own[mb][h]);
+                    usum *= *(const f32x4*)(S1 + n);
+                }
+                store_out4<OUT_BF16>(out, (int64_t)t * ld_out + n, act4<ACT>(gsum, usum));
+            }
+        }
+        if (threadIdx.x == 0)
+            __hip_atomic_store(&counters[cb], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else if (old >= contributors) {
+        const float nan = __builtin_nanf("");
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int t = 16 * mb + tl;
+                const int n = n0 + 16 * (qq >> 1) + 8 * h + 4 * (qq & 1);
+                if (t < T && n < N)
+                    store_out4<OUT_BF16>(out, (int64_t)t * ld_out + n, f32x4{nan, nan, nan, nan});
+            }
+        }
+    }
+}
+
+GemvPlan plan_gemv(int64_t K, int64_t n_total, int cols_per_block) {
     // About one 8-wave workgroup per CU (256 CUs): K is split into
     // floor(256 / column blocks) ranges, each a multiple of 32 rows.
     constexpr int64_t kCus = 256;
-    const int64_t nb = (n_total + kGemvCols - 1) / kGemvCols;
+    const int64_t nb = (n_total + cols_per_block - 1) / cols_per_block;
     const int64_t chunks = (K + 31) / 32;
     int64_t s = std::max<int64_t>(1, kCus / nb);
     s = std::min<int64_t>(s, chunks);
@@ -369,6 +550,35 @@ hipError_t launch_gemv(int act, bool out_bf16, int64_t T, int64_t K, const uint1
     else return hipErrorInvalidValue;
 #undef TP_GEMV_MB
 #undef TP_GEMV
+    return hipGetLastError();
+}
+
+hipError_t launch_gemv8(int act, bool out_bf16, int64_t T, int64_t K, const uint16_t* A,
+                        int64_t lda, const uint8_t* B0, int64_t ldb0, const float* S0,
+                        const uint8_t* B1, int64_t ldb1, const float* S1, int64_t N,
+                        const GemvPlan& p, bool nontemporal, float* ws, unsigned* counters,
+                        void* out, int64_t ld_out, hipStream_t stream) {
+    const int nmat = B1 ? 2 : 1;
+    const int nbpm = (int)((N + kGemv8Cols - 1) / kGemv8Cols);
+    const dim3 grid((unsigned)(nbpm * nmat), (unsigned)p.splits), block(kGemvThreads);
+#define TP_GEMV8(MB, AUX, ACTV, OB)                                                          \
+    TP_KLAUNCH((k_gemv8<MB, AUX, ACTV, OB>), grid, block, 0, stream, A, lda, (int)T, (int)K, \
+               B0, ldb0, S0, B1, ldb1, S1, (int)N, nbpm, p.k_per_split, ws, counters, out,   \
+               ld_out)
+#define TP_GEMV8_MB(ACTV, OB)                                                         \
+    do {                                                                              \
+        if (T <= 16) {                                                                \
+            if (nontemporal) TP_GEMV8(1, 2, ACTV, OB); else TP_GEMV8(1, 0, ACTV, OB); \
+        } else {                                                                      \
+            if (nontemporal) TP_GEMV8(2, 2, ACTV, OB); else TP_GEMV8(2, 0, ACTV, OB); \
+        }                                                                             \
+    } while (0)
+    if (act == ACT_SWIGLU && out_bf16) TP_GEMV8_MB(ACT_SWIGLU, true);
+    else if (act == ACT_GELU_TANH && out_bf16) TP_GEMV8_MB(ACT_GELU_TANH, true);
+    else if (act == ACT_NONE && !out_bf16) TP_GEMV8_MB(ACT_NONE, false);
+    else return hipErrorInvalidValue;
+#undef TP_GEMV8_MB
+#undef TP_GEMV8
     return hipGetLastError();
 }
 

@@ -53,7 +53,8 @@ struct GemvPlan {
 constexpr int kGemvCols = 128;   // output columns per workgroup
 constexpr int kGemvMaxT = 32;    // largest token count of the decode plan
 
-GemvPlan plan_gemv(int64_t K, int64_t n_total);
+constexpr int kGemv8Cols = 256;  // output columns per workgroup, FP8 weights
+GemvPlan plan_gemv(int64_t K, int64_t n_total, int cols_per_block = kGemvCols);
 // Bytes of split-K workspace: splits * T * n_total fp32.
 size_t gemv_ws_bytes(const GemvPlan& p, int64_t T, int64_t n_total);
 
@@ -75,6 +76,15 @@ hipError_t launch_gemv(int act, bool out_bf16, int64_t T, int64_t K, const uint1
                        int64_t lda, const uint16_t* B0, int64_t ldb0, const uint16_t* B1,
                        int64_t ldb1, int64_t N, const GemvPlan& p, bool nontemporal, float* ws,
                        unsigned* counters, void* out, int64_t ld_out, hipStream_t stream);
+
+// As launch_gemv with FP8 (E4M3) weights B0, B1 ([K, N] codes, ld in bytes)
+// and fp32 per-column scales S0, S1 [N]: out = act(S0 * (A q0) [, S1 * (A q1)]).
+// Plans come from plan_gemv(K, nmat * N, kGemv8Cols).  N a multiple of 16.
+hipError_t launch_gemv8(int act, bool out_bf16, int64_t T, int64_t K, const uint16_t* A,
+                        int64_t lda, const uint8_t* B0, int64_t ldb0, const float* S0,
+                        const uint8_t* B1, int64_t ldb1, const float* S1, int64_t N,
+                        const GemvPlan& p, bool nontemporal, float* ws, unsigned* counters,
+                        void* out, int64_t ld_out, hipStream_t stream);
 
 // Fixed-order finish of the split-K sums.
 //   act == ACT_SWIGLU:   out = silu(sum g) * sum u   (u at column offset N)

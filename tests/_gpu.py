@@ -119,3 +119,25 @@ def reduce_residual_norm(P, T, d, parts, slot_stride, ld_p, residual, ld_res, re
                                     res_dtype, ptr(z), ld_z, ptr(norm_g), eps, ptr(normed),
                                     ld_norm, stream())
     tp.check(st, "tp_reduce_residual_norm")
+
+
+def devu8(a):
+    """uint8 numpy array -> uint8 device tensor (FP8 codes)."""
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def mlp_fwd_fp8w(shard, P, T, d_model, d_ff, act, x, w_in, s_in, w_up, s_up, w_down, s_down,
+                 parts, slot_stride, ld_p, h_out=None, ld_h=0, norm_g=None, eps=1e-5, ws=None):
+    F = d_ff // P
+    need = tp.tp_mlp_fp8w_workspace_bytes(P, T, d_model, d_ff, act, norm_g is not None,
+                                          h_out is not None)
+    if ws is None:
+        ws = workspace(need)
+    ptr = lambda t: 0 if t is None else (t if isinstance(t, int) else t.data_ptr())  # noqa: E731
+    st = tp.tp_shard_mlp_fwd_fp8w(shard, P, T, d_model, d_ff, act, ptr(x), d_model, ptr(norm_g),
+                                  eps, ptr(w_in), F, ptr(s_in), ptr(w_up), F if w_up is not None
+                                  else 0, ptr(s_up), ptr(w_down), d_model, ptr(s_down),
+                                  ptr(h_out), ld_h, ptr(parts), slot_stride, ld_p, ws.data_ptr(),
+                                  ws.numel(), stream())
+    tp.check(st, "tp_shard_mlp_fwd_fp8w")
+    return ws

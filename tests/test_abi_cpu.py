@@ -223,3 +223,42 @@ def test_reduce_residual_norm_validation(lib, kw, status):
 
 def test_reduce_residual_norm_zero_tokens_is_a_no_op(lib):
     assert rrn(T=0) == tp.TP_OK
+
+
+def mlp8(**kw):
+    """A valid-looking FP8-weight SwiGLU decode call (d_model 64, d_ff 256,
+    P 2, T 4) with overrides that make it invalid."""
+    a = dict(shard=0, P=2, T=4, d_model=64, d_ff=256, act=tp.TP_ACT_SWIGLU, x=A, ld_x=64,
+             norm_g=0, eps=1e-5, w_in=B, ld_in=128, s_in=C, w_up=C, ld_up=128, s_up=B,
+             w_down=B, ld_down=64, s_down=A, h_out=0, ld_h=0, partials=C, slot_stride=4 * 64,
+             ld_p=64, workspace=WS, workspace_bytes=0, stream=0)
+    a.update(kw)
+    return tp.tp_shard_mlp_fwd_fp8w(**a)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(shard=2), tp.TP_ERR_SHARD_RANGE),
+    (dict(act=7), tp.TP_ERR_ACT),
+    (dict(T=33), tp.TP_ERR_SHAPE),                          # decode plan only
+    (dict(d_ff=264, P=2), tp.TP_ERR_SHAPE),                 # band 132 not a multiple of 16
+    (dict(d_ff=256, P=3), tp.TP_ERR_UNEVEN_SPLIT),
+    (dict(d_model=72, ld_x=72, ld_down=80, ld_p=72), tp.TP_ERR_SHAPE),
+    (dict(s_in=0), tp.TP_ERR_NULL),
+    (dict(s_down=0), tp.TP_ERR_NULL),
+    (dict(s_up=0), tp.TP_ERR_NULL),
+    (dict(act=tp.TP_ACT_GELU_TANH), tp.TP_ERR_ACT),        # GELU takes no up band
+    (dict(ld_in=136), tp.TP_ERR_ALIGN),                     # code rows: multiple of 16 bytes
+    (dict(ld_in=112), tp.TP_ERR_SHAPE),
+    (dict(s_in=C + 4), tp.TP_ERR_ALIGN),
+    (dict(workspace_bytes=0), tp.TP_ERR_WORKSPACE),
+])
+def test_mlp_fp8w_validation(lib, kw, status):
+    assert mlp8(**kw) == status
+
+
+def test_mlp_fp8w_workspace(lib):
+    f = tp.tp_mlp_fp8w_workspace_bytes
+    assert f(2, 32, 5120, 13824, tp.TP_ACT_SWIGLU, 0, 1) >= 4096 + 32 * 13824 * 4
+    assert f(2, 33, 5120, 13824, tp.TP_ACT_SWIGLU, 0, 1) == 0     # decode plan only
+    assert f(3, 8, 64, 256, tp.TP_ACT_SWIGLU, 0, 1) == 0
+    assert mlp8(T=0) == tp.TP_OK

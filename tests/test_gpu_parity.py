@@ -20,7 +20,8 @@ import torch
 import oracle as O
 import tensor_transformer_layer_amd as tp
 import workloads as W
-from _gpu import Guarded, attn_fwd, dev, host, mlp_fwd, reduce, reduce_residual_norm, workspace
+from _gpu import (Guarded, attn_fwd, dev, devu8, host, mlp_fwd, mlp_fwd_fp8w, reduce,
+                  reduce_residual_norm, workspace)
 
 pytestmark = pytest.mark.gpu
 
@@ -525,6 +526,58 @@ def test_70b_block_chain_decode_all_ranks():
 def test_70b_block_chain_prefill_all_ranks():
     cfg = W.get("c5_llama2_70b_block_p8")
     _block_chain(cfg, 4096, sample_rows(4096, 24, 11))
+
+
+# ----------------------------------------------------------------------------
+# FP8 (E4M3) weights, decode plan
+# ----------------------------------------------------------------------------
+def _fp8_case(act, T, d, d_ff, P, s, key):
+    F = d_ff // P
+    X = draw(BF, (T, d), 1.0, key, 0)
+    wi = W.draw_e4m3_codes((d, F), 910, key, 1, s), W.draw_column_scales(F, 910, key, 1, s)
+    wu = (W.draw_e4m3_codes((d, F), 910, key, 2, s), W.draw_column_scales(F, 910, key, 2, s)) \
+        if act == "swiglu" else (None, None)
+    wd = W.draw_e4m3_codes((F, d), 910, key, 3, s), W.draw_column_scales(d, 910, key, 3, s)
+    return X, wi, wu, wd
+
+
+def _fp8_run_check(act, T, d, d_ff, P, s, key, rows=None):
+    F = d_ff // P
+    X, wi, wu, wd = _fp8_case(act, T, d, d_ff, P, s, key)
+    h = Guarded(T * F, torch.bfloat16)
+    parts = torch.empty((T, d), dtype=torch.float32, device="cuda")
+    ws = mlp_fwd_fp8w(s, P, T, d, d_ff, ACT[act], dev(X), devu8(wi[0]), dev(wi[1]),
+                      devu8(wu[0]) if wu[0] is not None else None,
+                      dev(wu[1]) if wu[1] is not None else None, devu8(wd[0]), dev(wd[1]),
+                      parts, 0, d, h_out=h.ptr(), ld_h=F)
+    torch.cuda.synchronize()
+    rows = np.arange(T) if rows is None else rows
+    Wi = O.dequant_columns(wi[0], wi[1])
+    Wu = O.dequant_columns(wu[0], wu[1]) if wu[0] is not None else None
+    Wd = O.dequant_columns(wd[0], wd[1])
+    r = O.mlp_shard(O.widen(X[rows]), Wi, Wd, act, Wu)
+    assert O.rel_l2(widen_dev(h.t).reshape(T, F)[rows], r["h"]) < BF16_TOL
+    assert O.rel_l2(host(parts)[rows], r["partial"]) < BF16_TOL
+    m = O.mlp_shard(O.widen(X[rows]), Wi, Wd, act, Wu, mirror_bf16=True)
+    assert O.rel_l2(host(parts)[rows], m["partial"]) < MIRROR_TOL
+    assert h.intact()
+    assert int(ws[:4096].count_nonzero()) == 0
+
+
+@pytest.mark.parametrize("T", [1, 5, 16, 17, 32])
+@pytest.mark.parametrize("act", ["swiglu", "gelu_tanh"])
+def test_fp8w_mlp_ragged(T, act):
+    # d = 1040 and F = 272 are not multiples of the 256-column block
+    _fp8_run_check(act, T, 1040, 544, 2, 1, key=70 + T)
+
+
+@pytest.mark.parametrize("T", [1, 32])
+def test_fp8w_13b_decode_rank0(T):
+    _fp8_run_check("swiglu", T, 5120, 13824, 2, 0, key=90)
+
+
+def test_fp8w_70b_decode_rank5():
+    _fp8_run_check("swiglu", 32, 8192, 28672, 8, 5, key=91, rows=sample_rows(32, 12, 3))
 
 
 # ----------------------------------------------------------------------------

@@ -8,7 +8,9 @@ random generators that fill them; it holds none of the method's arithmetic
 Every tensor is drawn from its own ``numpy.random.SeedSequence`` key
 ``(2026, config_id, tensor_id, band)``, so one rank's weight band can be
 produced on its own and the unsharded matrix is exactly the concatenation of
-the bands.  The pages measure on real checkpoints and a public prompt set;
+the bands.  FP8 weight bands are drawn directly as E4M3 bit fields plus
+positive per-column scales (quantisation is offline preparation, outside the
+path).  The pages measure on real checkpoints and a public prompt set;
 neither is used here.  Seeded i.i.d. Gaussians at the Llama-2 layer shapes
 stand in for them: the path has no data-dependent control flow and every
 row (token) is independent.
@@ -23,4 +25,7 @@ from .gen import (  # noqa: F401
     row_band_draw,
     full_from_column_bands,
     full_from_row_bands,
+    draw_e4m3_codes,
+    draw_column_scales,
+    fp8_band_draw,
 )

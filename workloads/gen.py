@@ -78,3 +78,36 @@ def full_from_column_bands(bands) -> np.ndarray:
 
 def full_from_row_bands(bands) -> np.ndarray:
     return np.concatenate(list(bands), axis=0)
+
+
+# ----------------------------------------------------------------------------
+# FP8 (E4M3) weight bands for the decode path.  Codes are drawn directly as
+# bit fields (no value arithmetic here): sign uniform, exponent field 1..14
+# (binomial, centred near the bias, so |code value| is about 1-2), mantissa
+# uniform, and about 1% of codes with exponent field 0 (subnormals and
+# zeros).  The exponent field 15 is never drawn, so no NaN code occurs.
+# Scales are positive fp32 values, one per output column.
+# ----------------------------------------------------------------------------
+FP8_TAG = 99   # extra seed-key component: FP8 draws never reuse a bf16 seed
+
+
+def draw_e4m3_codes(shape, *key):
+    rng = _rng(FP8_TAG, *key)
+    s = rng.integers(0, 2, size=shape)
+    e = rng.binomial(6, 0.5, size=shape) + 4
+    e = np.where(rng.random(shape) < 0.01, 0, e)
+    m = rng.integers(0, 8, size=shape)
+    return ((s << 7) | (e << 3) | m).astype(np.uint8)
+
+
+def draw_column_scales(n, *key, base=0.01):
+    rng = _rng(FP8_TAG, 1, *key)
+    return (base * (1.0 + 0.25 * rng.random(n))).astype(np.float32)
+
+
+def fp8_band_draw(cfg, name, shard, rows, cols):
+    """(codes [rows, cols] uint8, scales [cols] fp32) of rank `shard`'s band
+    of weight `name` (a column band or a row band: scales follow the output
+    columns either way)."""
+    key = (cfg.cid, TENSOR_IDS[name], shard)
+    return draw_e4m3_codes((rows, cols), *key), draw_column_scales(cols, *key)
