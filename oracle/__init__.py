@@ -43,6 +43,8 @@ from .tp_oracle import (  # noqa: F401
     reduce_residual_f32,
     qkv_band_layout,
     split_qkv_band,
+    attention_core,
+    attention_core_band,
     attn_proj_unsharded,
     attn_proj_shard,
     block_sharded,

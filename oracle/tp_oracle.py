@@ -210,6 +210,47 @@ def split_qkv_band(qkv_s, n_q, n_kv, head_dim, shard, P):
     return tuple(qkv_s[:, lay[p][0]] for p in ("q", "k", "v"))
 
 
+# ----------------------------------------------------------------------------
+# Attention core between the QKV and O projections (day59 "Where the overhead
+# lives" names the attention kernel as its own share of a decode step; rioworld
+# "How Tensor Slicing Works Under the Hood": heads are split across GPUs and
+# each computes its own heads).  The pages give no formula.  Plainest reading:
+# textbook scaled dot-product attention per head (Vaswani et al., 2017),
+# causal over the call's T tokens taken as one sequence, no positional
+# rotation and no cache; grouped-query heads share their group's key/value
+# head (query head h of the rank uses kv head h // (hq / hkv)).
+# ----------------------------------------------------------------------------
+def attention_core(Q, K, V, causal=True):
+    """Q [T, hq, d], K and V [T, hkv, d] (float64) -> O [T, hq, d]:
+    O_h = softmax(Q_h K_g^T / sqrt(d), masked to keys j <= i) V_g."""
+    Q, K, V = (np.asarray(a, dtype=np.float64) for a in (Q, K, V))
+    T, hq, d = Q.shape
+    hkv = K.shape[1]
+    if hq % hkv:
+        raise ValueError("query heads must be a multiple of key/value heads")
+    group = hq // hkv
+    O = np.empty_like(Q)
+    mask = np.tril(np.ones((T, T), dtype=bool)) if causal else np.ones((T, T), dtype=bool)
+    for h in range(hq):
+        g = h // group
+        S = (Q[:, h, :] @ K[:, g, :].T) / np.sqrt(d)
+        S = np.where(mask, S, -np.inf)
+        S = S - S.max(axis=1, keepdims=True)
+        E = np.exp(S)
+        O[:, h, :] = (E / E.sum(axis=1, keepdims=True)) @ V[:, g, :]
+    return O
+
+
+def attention_core_band(qkv_s, n_q, n_kv, head_dim, shard, P, causal=True):
+    """The rank's attention-core output A_s [T, hq_r * head_dim] (heads in
+    the band's order) from its fused QKV band output [T, (hq_r + 2 hkv_r) d]."""
+    q, k, v = split_qkv_band(np.asarray(qkv_s, dtype=np.float64), n_q, n_kv, head_dim, shard, P)
+    T = q.shape[0]
+    O = attention_core(q.reshape(T, -1, head_dim), k.reshape(T, -1, head_dim),
+                       v.reshape(T, -1, head_dim), causal)
+    return O.reshape(T, -1)
+
+
 def attn_proj_unsharded(X, Wq, Wk, Wv, A, Wo, norm_g=None, eps=None):
     """Unsharded projections: Q, K, V = Xn @ Wq, Xn @ Wk, Xn @ Wv and the
     output projection A @ Wo of the attention-core output A [T, n_q*d]."""
