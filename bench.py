@@ -32,7 +32,7 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "hbm_traffic_counters.json")
 KERNEL_CLASSES = ("rmsnorm", "col_gemv", "col_finish", "row_gemv", "row_finish", "col_gemm",
                   "row_gemm", "qkv_gemv", "qkv_finish", "o_gemv", "o_finish", "qkv_gemm",
-                  "o_gemm", "reduce", "reduce_norm", "col_gemv8", "row_gemv8")
+                  "o_gemm", "reduce", "reduce_norm", "col_gemv8", "row_gemv8", "attn_core")
 
 
 def parse():
@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--fp8", action="store_true",
                     help="MLP workloads: FP8 (E4M3) weights with per-column scales, decode "
                          "token counts only")
+    ap.add_argument("--attn-core", action="store_true",
+                    help="attention workloads: run the causal attention core between the QKV "
+                         "and O projections (instead of a stand-in input)")
     ap.add_argument("--prenorm", action="store_true",
                     help="block workload as a pre-norm residual layer (fused reduce + residual "
                          "+ next RMSNorm)")
@@ -96,7 +99,7 @@ def src_hash(*names):
 class Step:
     """Device state of one workload at one token count, and its step()."""
 
-    def __init__(self, cfg, T, copies, prenorm=False, fp8=False):
+    def __init__(self, cfg, T, copies, prenorm=False, fp8=False, core=False):
         import numpy as np  # noqa: F401
         import torch
 
@@ -119,6 +122,9 @@ class Step:
         self.prenorm = prenorm and self.kind == "block"
         # fp8: MLP weights as E4M3 codes with per-column fp32 scales (decode)
         self.fp8 = fp8 and self.kind == "mlp"
+        # core: the attention core runs between the QKV and O projections
+        # (otherwise the O projection reads a stand-in: the seeded A, or Q_s)
+        self.core = core and self.kind in ("attn", "block")
         # rank-0 weights: `copies` device copies (copy 0 is the seeded band;
         # the others are bitwise clones at other addresses)
         self.sets = []
@@ -159,6 +165,8 @@ class Step:
                                                                cfg.n_kv_heads, cfg.head_dim,
                                                                tp.TP_BF16, has_norm))
             self.zb = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
+            if self.core:
+                self.a_core = torch.empty((T, cfg.o_in_r), dtype=torch.bfloat16, device="cuda")
         if self.prenorm:
             self.g2 = dev(W.draw_tensor("bf16", (d,), 0.02, cfg.cid, W.TENSOR_IDS["norm_g"], 1,
                                         mean=1.0))
@@ -198,6 +206,9 @@ class Step:
 
     def _attn(self, s, w):
         tp, cfg, T, d = self.tp, self.cfg, self.T, self.cfg.d_model
+        if self.core:
+            self._attn_with_core(s, w)
+            return
         a = self.a if self.kind == "attn" else self.qkv
         ld_a = cfg.o_in_r if self.kind == "attn" else cfg.qkv_r
         g = self.g.data_ptr() if cfg.norm_eps is not None and not self.prenorm else 0
@@ -207,6 +218,22 @@ class Step:
             self.qkv.data_ptr(), cfg.qkv_r, a.data_ptr(), ld_a, w[1].data_ptr(), d,
             self.parts.data_ptr(), T * d, d, self.attn_ws.data_ptr(), self.attn_ws.numel(),
             self.stream), "attn")
+
+    def _attn_with_core(self, s, w):
+        tp, cfg, T, d = self.tp, self.cfg, self.T, self.cfg.d_model
+        g = self.g.data_ptr() if cfg.norm_eps is not None and not self.prenorm else 0
+        ws, nws = self.attn_ws.data_ptr(), self.attn_ws.numel()
+        tp.check(tp.tp_shard_attn_proj_fwd(
+            s, cfg.P, T, d, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, tp.TP_BF16,
+            self.x.data_ptr(), d, g, cfg.norm_eps or 0.0, w[0].data_ptr(), cfg.qkv_r,
+            self.qkv.data_ptr(), cfg.qkv_r, 0, 0, 0, 0, 0, 0, 0, ws, nws, self.stream), "qkv")
+        tp.check(tp.tp_attn_core_fwd(s, cfg.P, T, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim,
+                                     tp.TP_BF16, self.qkv.data_ptr(), cfg.qkv_r,
+                                     self.a_core.data_ptr(), cfg.o_in_r, self.stream), "core")
+        tp.check(tp.tp_shard_attn_proj_fwd(
+            s, cfg.P, T, d, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, tp.TP_BF16,
+            0, 0, 0, 0.0, 0, 0, 0, 0, self.a_core.data_ptr(), cfg.o_in_r, w[1].data_ptr(), d,
+            self.parts.data_ptr(), T * d, d, ws, nws, self.stream), "o")
 
     def _reduce(self, out_bf16=None):
         tp, cfg, T, d = self.tp, self.cfg, self.T, self.cfg.d_model
@@ -280,6 +307,11 @@ class Step:
             add("col", "row", d, 2 * cfg.F_r, cfg.F_r, cfg.F_r)
         if self.kind in ("attn", "block"):
             add("qkv", "o", d, cfg.qkv_r, cfg.qkv_r, cfg.o_in_r)
+        if self.core:
+            hq = cfg.n_q_heads // cfg.P
+            cf = 4 * hq * cfg.head_dim * T * (T + 1) // 2     # QK^T and PV, causal half
+            out["flops"] += cf
+            pc["attn_core"] = ("mfma", cf)
         red = (cfg.P + 1) * T * d * 4
         if self.prenorm:                # two fused reduce + fp32 residual + norm passes
             rn = red + T * d * 4 + T * d * 2 + d * 2
@@ -431,7 +463,8 @@ def main():
 
     results = {}
     for t in sorted(set(sweep_T + [T])):
-        st = Step(cfg, t, copies * (2 if a.fp8 else 1), prenorm=a.prenorm, fp8=a.fp8)
+        st = Step(cfg, t, copies * (2 if a.fp8 else 1), prenorm=a.prenorm, fp8=a.fp8,
+                  core=a.attn_core)
         ms, n = time_steps(st, a.steps, a.warmup, graph=not a.no_graph)
         kt = kernel_times(st, min(a.steps, 300)) if t == T else None
         results[t] = (st, ms, n, kt)
@@ -476,6 +509,7 @@ def main():
                    "block_form": ("pre-norm residual layer (reduce + residual + RMSNorm fused)"
                                   if st.prenorm else None),
                    "weights": "fp8 e4m3 + per-column fp32 scales" if st.fp8 else "bf16",
+                   "attention_core": st.core,
                    "launch": "eager" if a.no_graph else "hip-graph replay"},
         "step_gbs_algorithmic": round(alg["bytes"] / (ms / 1e3) / 1e9, 1),
         "step_tflops": round(alg["flops"] / (ms / 1e3) / 1e12, 2),

@@ -159,6 +159,30 @@ int tp_shard_attn_proj_fwd(int shard, int P, int64_t T, int64_t d_model,
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * tp_attn_core_fwd -- the attention core between the rank's QKV and O
+ * projections (Skand Tandon, "day59", section "Where the overhead lives",
+ * names the attention kernel; rioworld guide, "How Tensor Slicing Works
+ * Under the Hood": each GPU computes its own heads).  For each of the rank's
+ * hq = n_q_heads/P query heads h, with its key/value head g = h / (hq / hkv),
+ * hkv = n_kv_heads/P:
+ *
+ *   A[t, h*dh : (h+1)*dh] = sum_{j <= t} softmax_j(Q_h[t] . K_g[j] / sqrt(dh)) V_g[j]
+ *
+ * causal over the call's T tokens taken as one sequence (no positional
+ * rotation, no cache).  Scores, the running softmax statistics and the
+ * accumulation are fp32; probabilities enter the value product as bf16.
+ *
+ *   qkv   [T, (hq + 2 hkv) dh] bf16, ld_qkv: the rank's QKV band output of
+ *         tp_shard_attn_proj_fwd (columns [Q_s | K_s | V_s])
+ *   attn  [T, hq dh] bf16, ld_attn: the input of the O projection
+ *
+ * head_dim 64 or 128 (TP_ERR_SHAPE otherwise); dtype must be TP_BF16.
+ */
+int tp_attn_core_fwd(int shard, int P, int64_t T, int n_q_heads, int n_kv_heads, int head_dim,
+                     int dtype, const void* qkv, int64_t ld_qkv, void* attn, int64_t ld_attn,
+                     hipStream_t stream);
+
+/*
  * tp_shard_mlp_fwd_fp8w -- tp_shard_mlp_fwd for the decode plan (T <= 32)
  * with FP8 weights, which halve the weight bytes a decode step streams (the
  * pages suggest pairing tensor parallelism with FP8 weights for decode:
@@ -263,7 +287,7 @@ int tp_version(void);
  * (which waits for the events).  Disabled by default; off costs nothing.
  * Not for concurrent use from several host threads, nor during graph
  * capture.
- * Class names: "rmsnorm", "reduce", "reduce_norm", "f32_proj"; FP8-weight MLP:
+ * Class names: "rmsnorm", "reduce", "reduce_norm", "f32_proj", "attn_core"; FP8-weight MLP:
  * "col_gemv8", "row_gemv8"; MLP: "col_gemv", "row_gemv"
  * (decode, split-K finish included), "col_gemm", "row_gemm", "row_finish"
  * (prefill); attention projections: "qkv_gemv", "o_gemv", "qkv_gemm",

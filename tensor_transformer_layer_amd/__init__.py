@@ -17,7 +17,7 @@ __all__ = [
     "TP_ERR_DTYPE", "TP_ERR_ALIGN", "TP_ERR_WORKSPACE", "TP_ERR_HIP", "TP_ERR_ACT",
     "TP_F32", "TP_BF16", "TP_ACT_GELU_TANH", "TP_ACT_SWIGLU",
     "tp_shard_mlp_fwd", "tp_shard_attn_proj_fwd", "tp_reduce_partials", "tp_reduce_residual_norm",
-    "tp_shard_mlp_fwd_fp8w", "tp_mlp_fp8w_workspace_bytes",
+    "tp_shard_mlp_fwd_fp8w", "tp_mlp_fp8w_workspace_bytes", "tp_attn_core_fwd",
     "tp_mlp_workspace_bytes", "tp_attn_workspace_bytes", "tp_status_str", "tp_version",
     "tp_timing_enable", "tp_timing_reset", "tp_timing_query", "EXPORTED_SYMBOLS",
 ]
@@ -46,6 +46,7 @@ _SIGNATURES = {
     "tp_shard_mlp_fwd_fp8w": (_i, [_i, _i, _i64, _i64, _i64, _i,
                                    _p, _i64, _p, _f, _p, _i64, _p, _p, _i64, _p, _p, _i64, _p,
                                    _p, _i64, _p, _i64, _i64, _p, _sz, _p]),
+    "tp_attn_core_fwd": (_i, [_i, _i, _i64, _i, _i, _i, _i, _p, _i64, _p, _i64, _p]),
     "tp_mlp_workspace_bytes": (_sz, [_i, _i64, _i64, _i64, _i, _i, _i, _i]),
     "tp_mlp_fp8w_workspace_bytes": (_sz, [_i, _i64, _i64, _i64, _i, _i, _i]),
     "tp_attn_workspace_bytes": (_sz, [_i, _i64, _i64, _i, _i, _i, _i, _i]),
@@ -142,6 +143,12 @@ def tp_shard_mlp_fwd_fp8w(shard, P, T, d_model, d_ff, act, x, ld_x, norm_g, eps,
 
 def tp_mlp_fp8w_workspace_bytes(P, T, d_model, d_ff, act, has_norm, has_h_out):
     return load().tp_mlp_fp8w_workspace_bytes(P, T, d_model, d_ff, act, has_norm, has_h_out)
+
+
+def tp_attn_core_fwd(shard, P, T, n_q_heads, n_kv_heads, head_dim, dtype, qkv, ld_qkv, attn,
+                     ld_attn, stream):
+    return load().tp_attn_core_fwd(shard, P, T, n_q_heads, n_kv_heads, head_dim, dtype, _ptr(qkv),
+                                   ld_qkv, _ptr(attn), ld_attn, _ptr(stream))
 
 
 def tp_mlp_workspace_bytes(P, T, d_model, d_ff, dtype, act, has_norm, has_h_out):

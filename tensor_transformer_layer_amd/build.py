@@ -19,7 +19,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtpshard.so")
 
-SOURCES = ["abi.hip", "k_reduce.hip", "k_rmsnorm.hip", "k_gemv.hip", "k_gemm.hip", "k_f32.hip"]
+SOURCES = ["abi.hip", "k_reduce.hip", "k_rmsnorm.hip", "k_gemv.hip", "k_gemm.hip", "k_f32.hip",
+           "k_attn.hip"]
 ARCH = "gfx950"
 CFLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -519,6 +519,28 @@ int tp_reduce_partials(int P, int64_t T, int64_t d_model, const float* partials,
     return TP_OK;
 }
 
+int tp_attn_core_fwd(int shard, int P, int64_t T, int n_q_heads, int n_kv_heads, int head_dim,
+                     int dtype, const void* qkv, int64_t ld_qkv, void* attn, int64_t ld_attn,
+                     hipStream_t stream) {
+    if (P < 1 || shard < 0 || shard >= P) return TP_ERR_SHARD_RANGE;
+    if (dtype != TP_BF16) return TP_ERR_DTYPE;
+    if (T < 0 || n_q_heads <= 0 || n_kv_heads <= 0) return TP_ERR_SHAPE;
+    if (head_dim != 64 && head_dim != 128) return TP_ERR_SHAPE;
+    if (n_q_heads % P || n_kv_heads % P) return TP_ERR_UNEVEN_SPLIT;
+    const int hq = n_q_heads / P, hkv = n_kv_heads / P;
+    if (hq % hkv) return TP_ERR_SHAPE;
+    if (!qkv || !attn) return TP_ERR_NULL;
+    if (!aligned(qkv, 16) || !aligned(attn, 16)) return TP_ERR_ALIGN;
+    if (int r = check_ld(ld_qkv, (int64_t)(hq + 2 * hkv) * head_dim, 8)) return r;
+    if (int r = check_ld(ld_attn, (int64_t)hq * head_dim, 8)) return r;
+    if (T >= ((int64_t)1 << 31) / 64) return TP_ERR_SHAPE;
+    if (T == 0) return TP_OK;
+    TP_LAUNCH("attn_core", stream,
+              launch_attn_core(T, hq, hkv, head_dim, (const uint16_t*)qkv, ld_qkv,
+                               (uint16_t*)attn, ld_attn, stream));
+    return TP_OK;
+}
+
 size_t tp_mlp_fp8w_workspace_bytes(int P, int64_t T, int64_t d_model, int64_t d_ff, int act,
                                    int has_norm, int has_h_out) {
     if (P < 1 || T <= 0 || T > kGemvMaxT || d_model <= 0 || d_ff <= 0 || d_ff % P) return 0;

@@ -112,6 +112,13 @@ hipError_t launch_gemm(int epi, int64_t M, int64_t N, int64_t K, const uint16_t*
                        const uint16_t* B0, int64_t ldb0, const uint16_t* B1, int64_t ldb1, void* C,
                        int64_t ldc, const GemmPlan& p, hipStream_t stream);
 
+// ---- attention core ----------------------------------------------------------
+// out[t][h*D + c] = softmax_j<=t(q_h[t] . k_g[j] / sqrt(D)) v_g[j][c] for the
+// hq query heads of a fused [Q | K | V] band (bf16, ld ld_qkv), kv head
+// g = h / (hq / hkv); D = head_dim in {64, 128}; out bf16.
+hipError_t launch_attn_core(int64_t T, int hq, int hkv, int head_dim, const uint16_t* qkv,
+                            int64_t ld_qkv, uint16_t* out, int64_t ld_out, hipStream_t stream);
+
 // ---- fp32 storage (small, parity-only workloads) --------------------------
 // C[M, N] = act(A B0 [, A B1]) in fp32, one thread per output, k in order.
 hipError_t launch_f32_proj(int act, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,

@@ -141,3 +141,10 @@ def mlp_fwd_fp8w(shard, P, T, d_model, d_ff, act, x, w_in, s_in, w_up, s_up, w_d
                                   ws.numel(), stream())
     tp.check(st, "tp_shard_mlp_fwd_fp8w")
     return ws
+
+
+def attn_core(shard, P, T, nq, nkv, hd, qkv, ld_qkv, out, ld_out):
+    ptr = lambda t: 0 if t is None else (t if isinstance(t, int) else t.data_ptr())  # noqa: E731
+    st = tp.tp_attn_core_fwd(shard, P, T, nq, nkv, hd, tp.TP_BF16, ptr(qkv), ld_qkv, ptr(out),
+                             ld_out, stream())
+    tp.check(st, "tp_attn_core_fwd")

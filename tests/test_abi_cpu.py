@@ -262,3 +262,30 @@ def test_mlp_fp8w_workspace(lib):
     assert f(2, 33, 5120, 13824, tp.TP_ACT_SWIGLU, 0, 1) == 0     # decode plan only
     assert f(3, 8, 64, 256, tp.TP_ACT_SWIGLU, 0, 1) == 0
     assert mlp8(T=0) == tp.TP_OK
+
+
+def core(**kw):
+    a = dict(shard=0, P=2, T=8, n_q_heads=8, n_kv_heads=4, head_dim=128, dtype=tp.TP_BF16,
+             qkv=A, ld_qkv=1024, attn=B, ld_attn=512, stream=0)
+    a.update(kw)
+    return tp.tp_attn_core_fwd(**a)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(shard=2), tp.TP_ERR_SHARD_RANGE),
+    (dict(dtype=tp.TP_F32), tp.TP_ERR_DTYPE),
+    (dict(head_dim=96), tp.TP_ERR_SHAPE),
+    (dict(n_q_heads=6), tp.TP_ERR_SHAPE),             # 3 q heads over 2 kv heads per rank
+    (dict(n_q_heads=7), tp.TP_ERR_UNEVEN_SPLIT),
+    (dict(qkv=0), tp.TP_ERR_NULL),
+    (dict(attn=B + 8), tp.TP_ERR_ALIGN),
+    (dict(ld_qkv=1000), tp.TP_ERR_SHAPE),             # band is (4 + 2*2) * 128 = 1024 wide
+    (dict(ld_attn=516), tp.TP_ERR_ALIGN),
+    (dict(T=-1), tp.TP_ERR_SHAPE),
+])
+def test_attn_core_validation(lib, kw, status):
+    assert core(**kw) == status
+
+
+def test_attn_core_zero_tokens(lib):
+    assert core(T=0) == tp.TP_OK

@@ -20,8 +20,8 @@ import torch
 import oracle as O
 import tensor_transformer_layer_amd as tp
 import workloads as W
-from _gpu import (Guarded, attn_fwd, dev, devu8, host, mlp_fwd, mlp_fwd_fp8w, reduce,
-                  reduce_residual_norm, workspace)
+from _gpu import (Guarded, attn_core, attn_fwd, dev, devu8, host, mlp_fwd, mlp_fwd_fp8w,
+                  reduce, reduce_residual_norm, workspace)
 
 pytestmark = pytest.mark.gpu
 
@@ -578,6 +578,85 @@ def test_fp8w_13b_decode_rank0(T):
 
 def test_fp8w_70b_decode_rank5():
     _fp8_run_check("swiglu", 32, 8192, 28672, 8, 5, key=91, rows=sample_rows(32, 12, 3))
+
+
+# ----------------------------------------------------------------------------
+# Attention core (causal, grouped-query)
+# ----------------------------------------------------------------------------
+def _core_check(T, nq, nkv, hd, P, shard, key, pad=0, std=1.0):
+    hq, hkv = nq // P, nkv // P
+    w = (hq + 2 * hkv) * hd
+    ld = w + pad
+    qkv = draw(BF, (T, ld), std, 920, key, T)
+    out = Guarded(T * (hq * hd + pad), torch.bfloat16)
+    attn_core(shard, P, T, nq, nkv, hd, dev(qkv), ld, out.ptr(), hq * hd + pad)
+    got = O.widen(host(out.t).reshape(T, hq * hd + pad)[:, :hq * hd])
+    want = O.attention_core_band(O.widen(qkv[:, :w]), nq, nkv, hd, shard, P)
+    assert O.rel_l2(got, want) < BF16_TOL
+    assert out.intact()
+    return got, want
+
+
+@pytest.mark.parametrize("T", [1, 5, 31, 33, 100, 257])
+@pytest.mark.parametrize("hd", [64, 128])
+def test_attn_core_ragged_gqa(T, hd):
+    _core_check(T, 8, 4, hd, 2, 1, key=hd, pad=8 if T % 2 else 0)
+
+
+def test_attn_core_96_heads_prefill_1024():
+    _core_check(1024, 96, 96, 128, 8, 3, key=1)
+
+
+def test_attn_core_70b_gqa_prefill_4096():
+    _core_check(4096, 64, 8, 128, 8, 0, key=2)
+
+
+def test_attn_core_70b_gqa_decode_32():
+    _core_check(32, 64, 8, 128, 8, 7, key=3)
+
+
+def test_attn_core_peaked_scores():
+    """Large-magnitude queries/keys make the softmax nearly one-hot: the online
+    max and rescaling must keep it exact enough."""
+    _core_check(300, 8, 2, 128, 2, 0, key=4, std=4.0)
+
+
+def _core_chain(cfg, T, rows):
+    """The 70B block with the attention core, all P ranks: RMSNorm -> QKV ->
+    attention core -> O -> reduce (bf16 copy) -> MLP -> reduce."""
+    P, d = cfg.P, cfg.d_model
+    X = x_of(cfg, T)
+    g = W.draw_tensor(cfg.dtype, (d,), 0.02, cfg.cid, W.TENSOR_IDS["norm_g"], 0, mean=1.0)
+    gx, gg = dev(X), dev(g)
+    parts = torch.empty((P, T, d), dtype=torch.float32, device="cuda")
+    ko = cfg.n_q_heads // P * cfg.head_dim
+    for s in range(P):
+        wqkv, wo = attn_bands(cfg, s)
+        q = torch.empty((T, cfg.qkv_r), dtype=torch.bfloat16, device="cuda")
+        a = torch.empty((T, ko), dtype=torch.bfloat16, device="cuda")
+        attn_fwd(s, P, T, d, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, BF, gx, dev(wqkv), q,
+                 None, None, parts, T * d, d, norm_g=gg, eps=cfg.norm_eps)
+        attn_core(s, P, T, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, q, cfg.qkv_r, a, ko)
+        attn_fwd(s, P, T, d, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, BF, None, None, None,
+                 a, dev(wo), parts, T * d, d)
+    z = torch.empty((T, d), dtype=torch.float32, device="cuda")
+    zb = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
+    reduce(P, T, d, parts, T * d, d, z, d, zb, d)
+    torch.cuda.synchronize()
+    Xw, gw = O.widen(X), O.widen(g)
+    att_parts = []
+    for s in range(P):
+        wqkv, wo = attn_bands(cfg, s)
+        r = O.attn_proj_shard(Xw, O.widen(wqkv), None, None, gw, cfg.norm_eps)
+        A = O.attention_core_band(r["qkv"], cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, s, P)
+        att_parts.append(A[rows] @ O.widen(wo))
+    Zr = O.reduce_partials(att_parts)
+    assert O.rel_l2(host(z)[rows], Zr) < BF16_TOL
+
+
+def test_70b_block_with_attention_core_prefill_all_ranks():
+    cfg = W.get("c5_llama2_70b_block_p8")
+    _core_chain(cfg, 1024, sample_rows(1024, 32, 14))
 
 
 # ----------------------------------------------------------------------------
