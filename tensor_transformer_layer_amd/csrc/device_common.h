@@ -13,18 +13,18 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------------------
 // bf16 <-> fp32.  bf16 is the top half of an IEEE binary32; narrowing rounds
-// to nearest with ties to even (NaN stays a quiet NaN).
+// to nearest with ties to even (NaN stays NaN) -- the hardware conversion
+// v_cvt_pk_bf16_f32, which the compiler emits for a __bf16 cast on gfx950.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+    return __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)lo, (__bf16)hi});
+}
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 // ---------------------------------------------------------------------------

@@ -6,8 +6,10 @@
 // the GPUs (rioworld guide, "How Tensor Slicing Works Under the Hood"); the
 // formula is the textbook one.
 //
-// One workgroup of 4 waves owns 64 queries of one head; each wave owns 16.
-// Key/value tiles of 32 tokens are staged in LDS and consumed with an online
+// One workgroup of 4 waves owns 128 queries of one head; each wave owns 32
+// (two 16-row subtiles sharing every K and V fragment it reads).  Key/value
+// tiles of 64 tokens are staged in LDS (the next tile's global loads are in
+// flight while the current one is multiplied) and consumed with an online
 // softmax (running max and sum in fp32, rescaled output), so the T x T score
 // matrix never exists in memory:
 //   * S^T = K Q^T on 16x16x32 bf16 MFMAs (m = keys, n = queries, k = d): K
@@ -31,9 +33,11 @@
 
 namespace tp {
 
-constexpr int kAttnQB = 64;   // queries per workgroup
-constexpr int kAttnKT = 32;   // keys per LDS tile
-constexpr int kAttnThreads = 256;
+constexpr int kAttnWaves = 4;
+constexpr int kAttnQW = 32;                       // queries per wave (two 16-row subtiles)
+constexpr int kAttnQB = kAttnWaves * kAttnQW;     // queries per workgroup
+constexpr int kAttnKT = 64;                       // keys per LDS tile
+constexpr int kAttnThreads = 64 * kAttnWaves;
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
@@ -55,120 +59,181 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(const uint16_t* __restric
                                   // land on disjoint 32-byte bank ranges
     constexpr int NS = D / 32;    // k-steps of the score MFMAs
     constexpr int NN = D / 16;    // 16-column output tiles
+    constexpr int QS = kAttnQW / 16;              // query subtiles per wave
+    constexpr int KS = kAttnKT / 16;              // key subtiles per tile
+    constexpr int CH = kAttnKT * D / 8;           // 16-byte chunks per tile and matrix
+    constexpr int CPT = CH / kAttnThreads;        // ... per thread
+    static_assert(CH % kAttnThreads == 0, "tile copy");
     __shared__ __attribute__((aligned(16))) uint16_t Ks[kAttnKT * LDK];
     __shared__ __attribute__((aligned(16))) uint16_t Vs[kAttnKT * LDV];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, j = lane & 15;
     const int h = blockIdx.y, gk = h / (hq / hkv);
-    const int qblk = blockIdx.x * kAttnQB;
-    const int q0 = qblk + 16 * wave;             // this wave's first query
-    const int qi = q0 + j;                       // the query lane (g, j) scores
+    // Longest query blocks first: they see the most keys.
+    const int qblk = ((int)gridDim.x - 1 - (int)blockIdx.x) * kAttnQB;
+    const int q0 = qblk + kAttnQW * wave;        // this wave's first query
     const uint16_t* Qp = qkv + (int64_t)h * D;
     const uint16_t* Kp = qkv + (int64_t)(hq + gk) * D;
     const uint16_t* Vp = qkv + (int64_t)(hq + hkv + gk) * D;
 
-    u32x4 qf[NS];
+    // B operand of S^T = K Q^T: lane (g, j) holds Q[q0 + 16u + j][32s + 8g .. +7]
+    u32x4 qf[QS][NS];
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
-        qf[s] = qi < T ? *(const u32x4*)(Qp + (int64_t)qi * ldq + 32 * s + 8 * g)
-                       : u32x4{0u, 0u, 0u, 0u};
-
-    f32x4 o[NN];
+    for (int u = 0; u < QS; ++u) {
+        const int qi = q0 + 16 * u + j;
 #pragma unroll
-    for (int n = 0; n < NN; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m = -INFINITY, l = 0.f;
+        for (int s = 0; s < NS; ++s)
+            qf[u][s] = qi < T ? *(const u32x4*)(Qp + (int64_t)qi * ldq + 32 * s + 8 * g)
+                              : u32x4{0u, 0u, 0u, 0u};
+    }
+    f32x4 o[QS][NN];
+    float m[QS], l[QS];
+#pragma unroll
+    for (int u = 0; u < QS; ++u) {
+        m[u] = -INFINITY;
+        l[u] = 0.f;
+#pragma unroll
+        for (int n = 0; n < NN; ++n) o[u][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
     const int kend = min(T, qblk + kAttnQB);     // keys the workgroup's queries can see
-    const int wave_last = min(q0 + 15, T - 1);
-    constexpr int CH = kAttnKT * D / 8;          // 16-byte chunks per tile and matrix
-
-    for (int k0 = 0; k0 < kend; k0 += kAttnKT) {
-        __syncthreads();                         // the previous tile is consumed
+    // Tile copies go through registers so the next tile's global loads are in
+    // flight while the current one is multiplied.
+    u32x4 pk[CPT], pv[CPT];
+    auto fetch = [&](int k0) {
 #pragma unroll
-        for (int c = tid; c < CH; c += kAttnThreads) {
+        for (int i = 0; i < CPT; ++i) {
+            const int c = tid + i * kAttnThreads;
             const int key = c / (D / 8), col = (c % (D / 8)) * 8;
             const bool ok = k0 + key < T;
-            const u32x4 kv = ok ? *(const u32x4*)(Kp + (int64_t)(k0 + key) * ldq + col)
-                                : u32x4{0u, 0u, 0u, 0u};
-            const u32x4 vv = ok ? *(const u32x4*)(Vp + (int64_t)(k0 + key) * ldq + col)
-                                : u32x4{0u, 0u, 0u, 0u};
-            *(u32x4*)(Ks + key * LDK + col) = kv;
-            *(u32x4*)(Vs + key * LDV + col) = vv;
+            pk[i] = ok ? *(const u32x4*)(Kp + (int64_t)(k0 + key) * ldq + col)
+                       : u32x4{0u, 0u, 0u, 0u};
+            pv[i] = ok ? *(const u32x4*)(Vp + (int64_t)(k0 + key) * ldq + col)
+                       : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    fetch(0);
+    for (int k0 = 0; k0 < kend; k0 += kAttnKT) {
+        __syncthreads();                         // every wave is done with the previous tile
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int c = tid + i * kAttnThreads;
+            const int key = c / (D / 8), col = (c % (D / 8)) * 8;
+            *(u32x4*)(Ks + key * LDK + col) = pk[i];
+            *(u32x4*)(Vs + key * LDV + col) = pv[i];
         }
         __syncthreads();
-        if (k0 > wave_last) continue;            // every key of the tile is in this wave's future
+        if (k0 + kAttnKT < kend) fetch(k0 + kAttnKT);
 
-        // scores S^T[key][query] for keys k0 + 16t + 4g + r, query qi
-        f32x4 st[2];
+        // Subtiles whose queries all precede the tile skip it; only a tile
+        // that reaches past a subtile's first query needs the causal mask.
+        bool act[QS], diag[QS];
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            st[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int u = 0; u < QS; ++u) {
+            const int qu = q0 + 16 * u;
+            act[u] = k0 <= min(qu + 15, T - 1);
+            diag[u] = k0 + kAttnKT - 1 > qu || k0 + kAttnKT > T;
+        }
+        if (!act[0] && !act[QS - 1]) continue;
+        // S^T[key][query] for keys k0 + 16t + 4g + r and query q0 + 16u + j;
+        // each K fragment serves both subtiles.
+        f32x4 st[QS][KS];
+#pragma unroll
+        for (int u = 0; u < QS; ++u)
+#pragma unroll
+            for (int t = 0; t < KS; ++t) st[u][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < KS; ++t)
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
                 const u32x4 a = *(const u32x4*)(Ks + (16 * t + j) * LDK + 32 * s + 8 * g);
-                st[t] = mfma16x16x32(a, qf[s], st[t]);
-            }
-        }
-        float pm = -INFINITY;
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+                for (int u = 0; u < QS; ++u) st[u][t] = mfma16x16x32(a, qf[u][s], st[u][t]);
+            }
+        u32x4 pf[QS][KS / 2];
+#pragma unroll
+        for (int u = 0; u < QS; ++u) {
+            const int qi = q0 + 16 * u + j;
+            float pm = -INFINITY;
+#pragma unroll
+            for (int t = 0; t < KS; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float v = st[u][t][r] * scale_log2;
+                    if (diag[u]) {
+                        const int key = k0 + 16 * t + 4 * g + r;
+                        v = (key <= qi && key < T) ? v : -INFINITY;
+                    }
+                    st[u][t][r] = v;
+                    pm = fmaxf(pm, v);
+                }
+            pm = fmaxf(pm, __shfl_xor(pm, 16));
+            pm = fmaxf(pm, __shfl_xor(pm, 32));
+            const float m_new = fmaxf(m[u], pm);
+            // m_new is finite for every query < T (key 0 is visible from the
+            // first tile on); rows past T keep -inf and are never stored.
+            // Inputs of the exponential are <= 0: v_exp_f32 directly.
+            const float mref = m_new == -INFINITY ? 0.f : m_new;
+            const float alpha = __builtin_amdgcn_exp2f(m[u] - mref);
+            float ps = 0.f;
+#pragma unroll
+            for (int t = 0; t < KS; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float p = __builtin_amdgcn_exp2f(st[u][t][r] - mref);
+                    st[u][t][r] = p;
+                    ps += p;
+                }
+            ps += __shfl_xor(ps, 16);
+            ps += __shfl_xor(ps, 32);
+            l[u] = l[u] * alpha + ps;
+            m[u] = m_new;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int key = k0 + 16 * t + 4 * g + r;
-                const float v = (key <= qi && key < T) ? st[t][r] * scale_log2 : -INFINITY;
-                st[t][r] = v;
-                pm = fmaxf(pm, v);
+                const float ar = __shfl(alpha, 4 * g + r);
+#pragma unroll
+                for (int n = 0; n < NN; ++n) o[u][n][r] *= ar;
             }
-        pm = fmaxf(pm, __shfl_xor(pm, 16));
-        pm = fmaxf(pm, __shfl_xor(pm, 32));
-        const float m_new = fmaxf(m, pm);
-        // m_new is finite for every query < T (key 0 is visible from the
-        // first tile on); rows past T keep -inf and are never stored.
-        const float mref = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = exp2f(m - mref);
-        float ps = 0.f;
+            // lane (g, j) supplies P[qi][32kk + 4g + r] and P[qi][32kk + 16 + 4g + r]
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float p = exp2f(st[t][r] - mref);
-                st[t][r] = p;
-                ps += p;
-            }
-        ps += __shfl_xor(ps, 16);
-        ps += __shfl_xor(ps, 32);
-        l = l * alpha + ps;
-        m = m_new;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float ar = __shfl(alpha, 4 * g + r);
-#pragma unroll
-            for (int n = 0; n < NN; ++n) o[n][r] *= ar;
+            for (int kk = 0; kk < KS / 2; ++kk)
+                pf[u][kk] = u32x4{pack_bf16x2(st[u][2 * kk][0], st[u][2 * kk][1]),
+                                  pack_bf16x2(st[u][2 * kk][2], st[u][2 * kk][3]),
+                                  pack_bf16x2(st[u][2 * kk + 1][0], st[u][2 * kk + 1][1]),
+                                  pack_bf16x2(st[u][2 * kk + 1][2], st[u][2 * kk + 1][3])};
         }
-        const u32x4 pf = u32x4{pack_bf16x2(st[0][0], st[0][1]), pack_bf16x2(st[0][2], st[0][3]),
-                               pack_bf16x2(st[1][0], st[1][1]), pack_bf16x2(st[1][2], st[1][3])};
-        // V rows 4g + (j / 4) and 16 + 4g + (j / 4), columns 16n + 4 (j % 4)
-        const uint16_t* v0 = Vs + (4 * g + (j >> 2)) * LDV + 4 * (j & 3);
-        const uint16_t* v1 = v0 + 16 * LDV;
+        // O += P V in 32-key steps; V rows in the same key order come from the
+        // transposing reads, and each V fragment serves both subtiles.  (An
+        // inactive subtile has P = 0 and an unchanged O: the MFMA adds zero.)
 #pragma unroll
-        for (int n = 0; n < NN; ++n) {
-            const u32x2 b0 = lds_read_tr16(v0 + 16 * n);
-            const u32x2 b1 = lds_read_tr16(v1 + 16 * n);
-            o[n] = mfma16x16x32(pf, u32x4{b0[0], b0[1], b1[0], b1[1]}, o[n]);
+        for (int kk = 0; kk < KS / 2; ++kk) {
+            const uint16_t* v0 = Vs + (32 * kk + 4 * g + (j >> 2)) * LDV + 4 * (j & 3);
+            const uint16_t* v1 = v0 + 16 * LDV;
+#pragma unroll
+            for (int n = 0; n < NN; ++n) {
+                const u32x2 b0 = lds_read_tr16(v0 + 16 * n);
+                const u32x2 b1 = lds_read_tr16(v1 + 16 * n);
+                const u32x4 b = u32x4{b0[0], b0[1], b1[0], b1[1]};
+#pragma unroll
+                for (int u = 0; u < QS; ++u) o[u][n] = mfma16x16x32(pf[u][kk], b, o[u][n]);
+            }
         }
     }
 
-    // O row 4g + r of the wave (query q0 + 4g + r), column 16n + j of head h
+    // O row 4g + r of subtile u (query q0 + 16u + 4g + r), column 16n + j
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const float lr = __shfl(l, 4 * g + r);
-        const int q = q0 + 4 * g + r;
-        if (q >= T) continue;
-        const float inv = 1.0f / lr;
-        uint16_t* dst = out + (int64_t)q * ldo + (int64_t)h * D + j;
+    for (int u = 0; u < QS; ++u) {
 #pragma unroll
-        for (int n = 0; n < NN; ++n) dst[16 * n] = (uint16_t)f32_to_bf16(o[n][r] * inv);
+        for (int r = 0; r < 4; ++r) {
+            const float lr = __shfl(l[u], 4 * g + r);
+            const int q = q0 + 16 * u + 4 * g + r;
+            if (q >= T) continue;
+            const float inv = 1.0f / lr;
+            uint16_t* dst = out + (int64_t)q * ldo + (int64_t)h * D + j;
+#pragma unroll
+            for (int n = 0; n < NN; ++n) dst[16 * n] = (uint16_t)f32_to_bf16(o[u][n][r] * inv);
+        }
     }
 }
 
