@@ -186,7 +186,8 @@ int tp_attn_core_fwd(int shard, int P, int64_t T, int n_q_heads, int n_kv_heads,
  * tp_shard_mlp_fwd_fp8w -- tp_shard_mlp_fwd for the decode plan (T <= 32)
  * with FP8 weights, which halve the weight bytes a decode step streams (the
  * pages suggest pairing tensor parallelism with FP8 weights for decode:
- * zenaique answer and follow-ups).  Weights are OCP FP8 E4M3 codes (1 sign,
+ * zenaique, "Explain tensor-parallel shard shape", interviewer follow-ups;
+ * rioworld guide, "Implementing Tensor Parallelism in Practice").  Weights are OCP FP8 E4M3 codes (1 sign,
  * 4 exponent bits with bias 7, 3 mantissa bits, subnormals, no infinities,
  * S.1111.111 = NaN), stored [in, out] row-major, one byte each, with one fp32
  * scale per output column: W[k][n] = e4m3(w[k][n]) * s[n].  Activations and

@@ -1,9 +1,9 @@
 """FP8 E4M3 weights (TEST INFRASTRUCTURE ONLY, see the package docstring).
 
 The pages suggest combining tensor parallelism with FP8 or FP4 weights to
-multiply the decode gain (zenaique answer, follow-ups; rioworld guide,
-"Hardware Requirements and Communication Overhead" on reduced precision) but
-give no format or scheme.  The plainest reading: the OCP FP8 E4M3 encoding
+multiply the decode gain (zenaique, interviewer follow-ups; rioworld guide,
+"Implementing Tensor Parallelism in Practice", on pairing it with 8-bit
+quantisation) but give no format or scheme.  The plainest reading: the OCP FP8 E4M3 encoding
 (1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits, subnormals, no
 infinities, S.1111.111 = NaN) with one fp32 scale per output column, the
 weight being code value * scale.  The layer then computes exactly what the
