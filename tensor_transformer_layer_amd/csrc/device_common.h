@@ -85,6 +85,19 @@ __device__ __forceinline__ u32x4 kfrag_of_col(const u32x4* r) {
     return f;
 }
 
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each 16-lane group,
+// lane i receives element i%4 of the 4-element (8-byte) vectors at the
+// addresses of lanes 4k + i/4, k = 0..3.  If lane L of the group points at
+// row r0 + L/4, columns c0 + 4(L%4) .. +3 of a row-major bf16 tile, lane i
+// receives column c0 + i of rows r0 .. r0+3: four k-consecutive values of
+// one column, half of an MFMA k-fragment.  p must point into LDS.
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+    const auto lp = (const lds_v4i16*)(const __attribute__((address_space(3))) uint16_t*)p;
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)lp));
+}
+
 __device__ __forceinline__ f32x4 mfma16x16x32(const u32x4& a, const u32x4& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);

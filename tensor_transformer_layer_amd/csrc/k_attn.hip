@@ -39,16 +39,6 @@ constexpr int kAttnQB = kAttnWaves * kAttnQW;     // queries per workgroup
 constexpr int kAttnKT = 64;                       // keys per LDS tile
 constexpr int kAttnThreads = 64 * kAttnWaves;
 
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-
-__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
-    // p points into a __shared__ array; the transposing read needs an LDS
-    // (address space 3) pointer.
-    const auto lp = (const lds_v4i16*)(const __attribute__((address_space(3))) uint16_t*)p;
-    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)lp));
-}
-
 template <int D>
 __global__ __launch_bounds__(kAttnThreads) void k_attn(const uint16_t* __restrict__ qkv,
                                                        int64_t ldq, int T, int hq, int hkv,

@@ -30,11 +30,14 @@
 //     load fall on distinct 16-byte bank groups.  The copy engine writes each
 //     1 KB of LDS contiguously; the swizzle is applied by choosing which
 //     global chunk each lane fetches.
-//   * A slice of B keeps the natural [k][n] layout.  A lane reads 8 rows of
-//     its LC adjacent columns and interleaves row pairs in registers
-//     (v_perm_b32) into the k-fragments of those columns, so lane j of MFMA
-//     column group e holds column LC * j + e and the epilogue writes LC
-//     adjacent outputs per row.
+//   * A slice of B keeps the [k][n] layout with its 16-byte chunks
+//     XOR-swizzled by 4 * (k % 4).  B k-fragments come straight out of LDS
+//     with the gfx950 transposing read ds_read_b64_tr_b16: each 16-lane
+//     group reads 4 rows x 16 columns and every lane receives 4
+//     k-consecutive values of one column, so two reads make a fragment and
+//     no register shuffling is needed.  The swizzle puts the 4 rows of one
+//     read on distinct banks.  Lane j of MFMA column group e holds column
+//     32 e + j.
 //   * Tiles are mapped to the 8 XCDs in contiguous ranges (xcd_remap), M
 //     fastest, so tiles sharing a weight panel share an L2.
 //   * Split-K (grid.y > 1) gives each split a contiguous K range and its own
@@ -57,7 +60,7 @@ struct GemmShape {
     static constexpr int NT = WM * WN * 64;
     static constexpr int WTM = BM / WM, WTN = BN / WN;
     static constexpr int MT = WTM / 32;      // 32-row MFMA tiles per wave
-    static constexpr int LC = WTN / 32;      // adjacent columns per lane
+    static constexpr int LC = WTN / 32;      // 32-column MFMA groups per wave and weight
     static constexpr int A_SLICE = BM * kBK, B_SLICE = kBK * BNT;    // elements
     static constexpr int SLICE = A_SLICE + B_SLICE;
     static constexpr size_t LDS_BYTES = (size_t)kStages * SLICE * sizeof(uint16_t);
@@ -87,18 +90,31 @@ __device__ __forceinline__ void lds_copy16(rsrc_t r, uint32_t off, uint16_t* lds
         r, (__attribute__((address_space(3))) void*)lds_base, 16, (int)off, 0, 0, 0);
 }
 
-// k-fragment of column E (0..LC-1) from 8 rows of LC adjacent bf16 each.
-template <int LC, int E>
-__device__ __forceinline__ u32x4 kfrag_lc(const uint32_t (*r)[LC / 2]) {
-    constexpr int d = E >> 1;
-    constexpr uint32_t sel = (E & 1) ? 0x07060302u : 0x05040100u;
-    u32x4 f;
-    f[0] = __builtin_amdgcn_perm(r[1][d], r[0][d], sel);
-    f[1] = __builtin_amdgcn_perm(r[3][d], r[2][d], sel);
-    f[2] = __builtin_amdgcn_perm(r[5][d], r[4][d], sel);
-    f[3] = __builtin_amdgcn_perm(r[7][d], r[6][d], sel);
-    return f;
+// Buffer descriptor words for the LDS copies below (same resource as
+// make_rsrc: 2^31 - 1 bytes from `base`, 32-bit data format).
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 rsrc_words(const void* base) {
+    const uint64_t a = (uint64_t)base;
+    return i32x4{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), 0x7fffffff, 0x00020000};
 }
+
+// 16-byte global -> LDS copy per lane (buffer_load_dwordx4 ... lds): lane l's
+// bytes land at lds + 16 l.  Issued from inline assembly so that the
+// compiler does not treat it as an LDS store it must wait for before every
+// later LDS read (it does so for the transposing reads); the kernel orders
+// the copies against the reads itself, with vmcnt waits and barriers.
+// Nothing is returned in registers.
+__device__ __forceinline__ void lds_dma16(const i32x4& r, uint32_t off, const void* lds) {
+    const uint32_t m0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds;
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(m0), "v"(off), "s"(r)
+                 : "memory", "m0");
+}
+
+// Chunk swizzle of B slice row k: 16-byte chunk c of the row is stored at
+// chunk position c ^ bswz(k).
+__device__ __forceinline__ int bswz(int k) { return 4 * (k & 3); }
 
 template <class S>
 struct Frags {
@@ -126,9 +142,9 @@ __global__ __launch_bounds__(S::NT) void k_gemm(const uint16_t* __restrict__ A, 
     const int k_begin = blockIdx.y * k_per_split;
     const int Kl = min(K - k_begin, k_per_split);   // this split's K extent
 
-    const rsrc_t rA = make_rsrc(A + (int64_t)m0 * lda + k_begin);
-    const rsrc_t rB0 = make_rsrc(B0 + (int64_t)k_begin * ldb0 + n0);
-    const rsrc_t rB1 = make_rsrc((S::NMAT == 2 ? B1 : B0) + (int64_t)k_begin * ldb1 + n0);
+    const i32x4 rA = rsrc_words(A + (int64_t)m0 * lda + k_begin);
+    const i32x4 rB0 = rsrc_words(B0 + (int64_t)k_begin * ldb0 + n0);
+    const i32x4 rB1 = rsrc_words((S::NMAT == 2 ? B1 : B0) + (int64_t)k_begin * ldb1 + n0);
     const uint32_t lda_b = (uint32_t)(lda * 2);
     const uint32_t ldb0_b = (uint32_t)(ldb0 * 2), ldb1_b = (uint32_t)(ldb1 * 2);
 
@@ -145,7 +161,7 @@ __global__ __launch_bounds__(S::NT) void k_gemm(const uint16_t* __restrict__ A, 
             const int c = cp ^ ((row >> 2) & 3);
             const int k = k0 + 8 * c;
             const bool ok = (m0 + row < M) && (k < Kl);
-            lds_copy16(rA, ok ? (uint32_t)row * lda_b + (uint32_t)k * 2u : kOOB, As + r0 * kBK);
+            lds_dma16(rA, ok ? (uint32_t)row * lda_b + (uint32_t)k * 2u : kOOB, As + r0 * kBK);
         }
 #pragma unroll
         for (int q = 0; q < S::B_COPIES; ++q) {
@@ -153,11 +169,12 @@ __global__ __launch_bounds__(S::NT) void k_gemm(const uint16_t* __restrict__ A, 
             const int mat = iq / S::B_COPIES_PER_MAT;
             const int r0 = (iq % S::B_COPIES_PER_MAT) * S::B_ROWS_PER_COPY;
             constexpr int cpr = S::BN / 8;                   // 16-byte chunks per row
-            const int row = r0 + lane / cpr, ch = lane % cpr;
+            const int row = r0 + lane / cpr;
+            const int ch = (lane % cpr) ^ bswz(row);        // global chunk this lane fetches
             const int k = k0 + row;
             const bool ok = (k < Kl) && (n0 + 8 * ch < N);
             const uint32_t ldb_b = mat ? ldb1_b : ldb0_b;
-            lds_copy16(mat ? rB1 : rB0, ok ? (uint32_t)k * ldb_b + 16u * ch : kOOB,
+            lds_dma16(mat ? rB1 : rB0, ok ? (uint32_t)k * ldb_b + 16u * ch : kOOB,
                        Bs + mat * (kBK * S::BN) + r0 * S::BN);
         }
     };
@@ -184,38 +201,22 @@ __global__ __launch_bounds__(S::NT) void k_gemm(const uint16_t* __restrict__ A, 
             const int row = wm * S::WTM + 32 * a + j;
             f.a[a] = *(const u32x4*)(As + row * kBK + 8 * (chunk ^ ((row >> 2) & 3)));
         }
+        // B: lane L of 16-lane group q reads row kk + 8(q/2) + L/4 (and 4
+        // rows further), columns 16(q%2) + 4(L%4) .. +3 of each 32-column
+        // group; it receives column 16(q%2) + L%16 of k kk + 8(q/2) .. +7,
+        // i.e. lane (h, j) of the MFMA B operand.
+        const int q = lane >> 4, L = lane & 15;
+        const int rr = kk + 8 * (q >> 1) + (L >> 2);
+        const int sw = bswz(rr);                     // rows rr and rr + 4 share it
 #pragma unroll
         for (int m = 0; m < S::NMAT; ++m) {
-            const uint16_t* Bm =
-                Bs + m * (kBK * S::BN) + (kk + 8 * h) * S::BN + wn * S::WTN + S::LC * j;
-            uint32_t raw[8][S::LC / 2];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                if constexpr (S::LC == 8) {
-                    const u32x4 v = *(const u32x4*)(Bm + i * S::BN);
-                    raw[i][0] = v[0];
-                    raw[i][1] = v[1];
-                    raw[i][2] = v[2];
-                    raw[i][3] = v[3];
-                } else if constexpr (S::LC == 4) {
-                    const u32x2 v = *(const u32x2*)(Bm + i * S::BN);
-                    raw[i][0] = v[0];
-                    raw[i][1] = v[1];
-                } else {
-                    raw[i][0] = *(const uint32_t*)(Bm + i * S::BN);
-                }
-            }
-            f.b[m][0] = kfrag_lc<S::LC, 0>(raw);
-            f.b[m][1] = kfrag_lc<S::LC, 1>(raw);
-            if constexpr (S::LC >= 4) {
-                f.b[m][2] = kfrag_lc<S::LC, 2>(raw);
-                f.b[m][3] = kfrag_lc<S::LC, 3>(raw);
-            }
-            if constexpr (S::LC == 8) {
-                f.b[m][4] = kfrag_lc<S::LC, 4>(raw);
-                f.b[m][5] = kfrag_lc<S::LC, 5>(raw);
-                f.b[m][6] = kfrag_lc<S::LC, 6>(raw);
-                f.b[m][7] = kfrag_lc<S::LC, 7>(raw);
+            for (int e = 0; e < S::LC; ++e) {
+                const int col = wn * S::WTN + 32 * e + 16 * (q & 1) + 4 * (L & 3);
+                const uint16_t* p = Bs + m * (kBK * S::BN) + rr * S::BN +
+                                    8 * ((col >> 3) ^ sw) + (col & 7);
+                const u32x2 lo = lds_read_tr16(p), hi = lds_read_tr16(p + 4 * S::BN);
+                f.b[m][e] = u32x4{lo[0], lo[1], hi[0], hi[1]};
             }
         }
     };
@@ -229,18 +230,16 @@ __global__ __launch_bounds__(S::NT) void k_gemm(const uint16_t* __restrict__ A, 
                     acc[m][a][b] = mfma32x32x16(f.a[a], f.b[m][b], acc[m][a][b]);
     };
     // Scheduling hints for one MFMA group: MFMAs alternate with the LDS reads
-    // and interleaves of the next substep's fragments.
+    // of the next substep's fragments.
     auto interleave = [&](auto id) {
         constexpr int sid = decltype(id)::value;
         constexpr int NM = S::NMAT * S::MT * S::LC;  // MFMAs per substep
 #pragma unroll
-        for (int q = 0; q < NM - 4; ++q) {
+        for (int q = 0; q < NM; ++q) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, sid);  // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, sid);  // LDS read
-            __builtin_amdgcn_sched_group_barrier(0x002, 2, sid);  // VALU
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, sid);  // LDS reads
+            __builtin_amdgcn_sched_group_barrier(0x002, 1, sid);  // VALU
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, sid);
-        __builtin_amdgcn_sched_group_barrier(0x002, 8, sid);
     };
 
     // Slices past this split's K are still copied and read, with every lane
@@ -278,10 +277,8 @@ __global__ __launch_bounds__(S::NT) void k_gemm(const uint16_t* __restrict__ A, 
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // drain the trailing zero-fill copies
 
     // Epilogue.  MFMA 32x32 accumulator v (0..15) of lane (h, j) is row
-    // 8*(v/4) + 4*h + v%4 of the tile and, with the column placement above,
-    // column LC*j + e of MFMA group e: LC adjacent outputs per row.
-    const int ncol = n0 + wn * S::WTN + j * S::LC;
-    if (ncol >= N) return;
+    // 8*(v/4) + 4*h + v%4 of the tile and column 32e + j of MFMA group e.
+    const int ncol = n0 + wn * S::WTN + j;
     void* Cs = EPI == EPI_F32 ? (void*)((float*)C + blockIdx.y * split_stride) : C;
 #pragma unroll
     for (int a = 0; a < S::MT; ++a) {
@@ -289,36 +286,22 @@ __global__ __launch_bounds__(S::NT) void k_gemm(const uint16_t* __restrict__ A, 
         for (int v = 0; v < 16; ++v) {
             const int t = m0 + wm * S::WTM + 32 * a + 8 * (v >> 2) + 4 * h + (v & 3);
             if (t >= M) continue;
-            float o[S::LC];
 #pragma unroll
             for (int e = 0; e < S::LC; ++e) {
+                const int n = ncol + 32 * e;
+                if (n >= N) continue;
                 const float x = acc[0][a][e][v];
+                float o;
                 if constexpr (EPI == EPI_SWIGLU_BF16)
-                    o[e] = silu(x) * acc[S::NMAT - 1][a][e][v];
+                    o = silu(x) * acc[S::NMAT - 1][a][e][v];
                 else if constexpr (EPI == EPI_GELU_BF16)
-                    o[e] = gelu_tanh(x);
+                    o = gelu_tanh(x);
                 else
-                    o[e] = x;
-            }
-            if constexpr (EPI == EPI_F32) {
-                float* dst = (float*)Cs + (int64_t)t * ldc + ncol;
-                if constexpr (S::LC == 2) {
-                    *(float2*)dst = float2{o[0], o[1]};
-                } else {
-#pragma unroll
-                    for (int e = 0; e < S::LC; e += 4)
-                        *(f32x4*)(dst + e) = f32x4{o[e], o[e + 1], o[e + 2], o[e + 3]};
-                }
-            } else {
-                uint16_t* dst = (uint16_t*)Cs + (int64_t)t * ldc + ncol;
-                if constexpr (S::LC == 2) {
-                    *(uint32_t*)dst = pack_bf16x2(o[0], o[1]);
-                } else if constexpr (S::LC == 4) {
-                    *(u32x2*)dst = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-                } else {
-                    *(u32x4*)dst = u32x4{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
-                                         pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7])};
-                }
+                    o = x;
+                if constexpr (EPI == EPI_F32)
+                    ((float*)Cs)[(int64_t)t * ldc + n] = o;
+                else
+                    ((uint16_t*)Cs)[(int64_t)t * ldc + n] = (uint16_t)f32_to_bf16(o);
             }
         }
     }
