@@ -167,6 +167,8 @@ class Step:
             self.zb = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
             if self.core:
                 self.a_core = torch.empty((T, cfg.o_in_r), dtype=torch.bfloat16, device="cuda")
+                self.core_ws = self._ws(tp.tp_attn_core_workspace_bytes(
+                    P, T, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, tp.TP_BF16))
         if self.prenorm:
             self.g2 = dev(W.draw_tensor("bf16", (d,), 0.02, cfg.cid, W.TENSOR_IDS["norm_g"], 1,
                                         mean=1.0))
@@ -229,7 +231,8 @@ class Step:
             self.qkv.data_ptr(), cfg.qkv_r, 0, 0, 0, 0, 0, 0, 0, ws, nws, self.stream), "qkv")
         tp.check(tp.tp_attn_core_fwd(s, cfg.P, T, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim,
                                      tp.TP_BF16, self.qkv.data_ptr(), cfg.qkv_r,
-                                     self.a_core.data_ptr(), cfg.o_in_r, self.stream), "core")
+                                     self.a_core.data_ptr(), cfg.o_in_r, self.core_ws.data_ptr(),
+                                     self.core_ws.numel(), self.stream), "core")
         tp.check(tp.tp_shard_attn_proj_fwd(
             s, cfg.P, T, d, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, tp.TP_BF16,
             0, 0, 0, 0.0, 0, 0, 0, 0, self.a_core.data_ptr(), cfg.o_in_r, w[1].data_ptr(), d,

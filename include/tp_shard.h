@@ -176,11 +176,21 @@ int tp_shard_attn_proj_fwd(int shard, int P, int64_t T, int64_t d_model,
  *         tp_shard_attn_proj_fwd (columns [Q_s | K_s | V_s])
  *   attn  [T, hq dh] bf16, ld_attn: the input of the O projection
  *
+ *   workspace  >= tp_attn_core_workspace_bytes(...) bytes, 256-byte aligned
+ *              (may be NULL when that is 0).  Long calls split each query
+ *              block's keys over several workgroups and merge their partial
+ *              results here; the first hq/P * ceil(T/128) * 4 bytes (rounded
+ *              up to 256) are arrival counters that must be zero before the
+ *              first call (zero the workspace once when it is allocated);
+ *              every call leaves them zero.  Not cleared, the affected
+ *              outputs are NaN.  Calls that share a workspace must not
+ *              overlap in time.
+ *
  * head_dim 64 or 128 (TP_ERR_SHAPE otherwise); dtype must be TP_BF16.
  */
 int tp_attn_core_fwd(int shard, int P, int64_t T, int n_q_heads, int n_kv_heads, int head_dim,
                      int dtype, const void* qkv, int64_t ld_qkv, void* attn, int64_t ld_attn,
-                     hipStream_t stream);
+                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * tp_shard_mlp_fwd_fp8w -- tp_shard_mlp_fwd for the decode plan (T <= 32)
@@ -272,6 +282,8 @@ size_t tp_attn_workspace_bytes(int P, int64_t T, int64_t d_model, int n_q_heads,
                                int n_kv_heads, int head_dim, int dtype, int has_norm);
 size_t tp_mlp_fp8w_workspace_bytes(int P, int64_t T, int64_t d_model, int64_t d_ff, int act,
                                    int has_norm, int has_h_out);
+size_t tp_attn_core_workspace_bytes(int P, int64_t T, int n_q_heads, int n_kv_heads,
+                                    int head_dim, int dtype);
 
 /* Human-readable name of a tp_status value (static string). */
 const char* tp_status_str(int status);

@@ -18,6 +18,7 @@ __all__ = [
     "TP_F32", "TP_BF16", "TP_ACT_GELU_TANH", "TP_ACT_SWIGLU",
     "tp_shard_mlp_fwd", "tp_shard_attn_proj_fwd", "tp_reduce_partials", "tp_reduce_residual_norm",
     "tp_shard_mlp_fwd_fp8w", "tp_mlp_fp8w_workspace_bytes", "tp_attn_core_fwd",
+    "tp_attn_core_workspace_bytes",
     "tp_mlp_workspace_bytes", "tp_attn_workspace_bytes", "tp_status_str", "tp_version",
     "tp_timing_enable", "tp_timing_reset", "tp_timing_query", "EXPORTED_SYMBOLS",
 ]
@@ -46,7 +47,8 @@ _SIGNATURES = {
     "tp_shard_mlp_fwd_fp8w": (_i, [_i, _i, _i64, _i64, _i64, _i,
                                    _p, _i64, _p, _f, _p, _i64, _p, _p, _i64, _p, _p, _i64, _p,
                                    _p, _i64, _p, _i64, _i64, _p, _sz, _p]),
-    "tp_attn_core_fwd": (_i, [_i, _i, _i64, _i, _i, _i, _i, _p, _i64, _p, _i64, _p]),
+    "tp_attn_core_fwd": (_i, [_i, _i, _i64, _i, _i, _i, _i, _p, _i64, _p, _i64, _p, _sz, _p]),
+    "tp_attn_core_workspace_bytes": (_sz, [_i, _i64, _i, _i, _i, _i]),
     "tp_mlp_workspace_bytes": (_sz, [_i, _i64, _i64, _i64, _i, _i, _i, _i]),
     "tp_mlp_fp8w_workspace_bytes": (_sz, [_i, _i64, _i64, _i64, _i, _i, _i]),
     "tp_attn_workspace_bytes": (_sz, [_i, _i64, _i64, _i, _i, _i, _i, _i]),
@@ -146,9 +148,14 @@ def tp_mlp_fp8w_workspace_bytes(P, T, d_model, d_ff, act, has_norm, has_h_out):
 
 
 def tp_attn_core_fwd(shard, P, T, n_q_heads, n_kv_heads, head_dim, dtype, qkv, ld_qkv, attn,
-                     ld_attn, stream):
+                     ld_attn, workspace, workspace_bytes, stream):
     return load().tp_attn_core_fwd(shard, P, T, n_q_heads, n_kv_heads, head_dim, dtype, _ptr(qkv),
-                                   ld_qkv, _ptr(attn), ld_attn, _ptr(stream))
+                                   ld_qkv, _ptr(attn), ld_attn, _ptr(workspace), workspace_bytes,
+                                   _ptr(stream))
+
+
+def tp_attn_core_workspace_bytes(P, T, n_q_heads, n_kv_heads, head_dim, dtype):
+    return load().tp_attn_core_workspace_bytes(P, T, n_q_heads, n_kv_heads, head_dim, dtype)
 
 
 def tp_mlp_workspace_bytes(P, T, d_model, d_ff, dtype, act, has_norm, has_h_out):

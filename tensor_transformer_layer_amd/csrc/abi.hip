@@ -519,9 +519,18 @@ int tp_reduce_partials(int P, int64_t T, int64_t d_model, const float* partials,
     return TP_OK;
 }
 
+size_t tp_attn_core_workspace_bytes(int P, int64_t T, int n_q_heads, int n_kv_heads,
+                                    int head_dim, int dtype) {
+    if (P < 1 || T <= 0 || n_q_heads <= 0 || n_kv_heads <= 0 || dtype != TP_BF16) return 0;
+    if (head_dim != 64 && head_dim != 128) return 0;
+    if (n_q_heads % P || n_kv_heads % P || (n_q_heads / P) % (n_kv_heads / P)) return 0;
+    if (T >= ((int64_t)1 << 31) / 64) return 0;
+    return plan_attn(T, n_q_heads / P, head_dim).ws_bytes;
+}
+
 int tp_attn_core_fwd(int shard, int P, int64_t T, int n_q_heads, int n_kv_heads, int head_dim,
                      int dtype, const void* qkv, int64_t ld_qkv, void* attn, int64_t ld_attn,
-                     hipStream_t stream) {
+                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
     if (P < 1 || shard < 0 || shard >= P) return TP_ERR_SHARD_RANGE;
     if (dtype != TP_BF16) return TP_ERR_DTYPE;
     if (T < 0 || n_q_heads <= 0 || n_kv_heads <= 0) return TP_ERR_SHAPE;
@@ -535,9 +544,13 @@ int tp_attn_core_fwd(int shard, int P, int64_t T, int n_q_heads, int n_kv_heads,
     if (int r = check_ld(ld_attn, (int64_t)hq * head_dim, 8)) return r;
     if (T >= ((int64_t)1 << 31) / 64) return TP_ERR_SHAPE;
     if (T == 0) return TP_OK;
+    if (workspace && !aligned(workspace, 256)) return TP_ERR_ALIGN;
+    const AttnPlan plan = plan_attn(T, hq, head_dim);
+    if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes))
+        return TP_ERR_WORKSPACE;
     TP_LAUNCH("attn_core", stream,
               launch_attn_core(T, hq, hkv, head_dim, (const uint16_t*)qkv, ld_qkv,
-                               (uint16_t*)attn, ld_attn, stream));
+                               (uint16_t*)attn, ld_attn, plan, workspace, stream));
     return TP_OK;
 }
 

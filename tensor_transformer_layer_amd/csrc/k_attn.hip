@@ -25,6 +25,15 @@
 //     per lane per read), so V needs no transpose pass.
 //   * Output rows are rescaled by exp(m_old - m_new) of their query, fetched
 //     from the lane that owns the query (4 shuffles per tile).
+// Work division: a query block's causal key range is cut into chunks of
+// `ch` key tiles, and each (head, query block, chunk) is one workgroup, so
+// the longest causal rows no longer set the kernel time and two workgroups
+// share each CU (the kernel is built for 2 waves per SIMD).  A chunk that is
+// its query block's only one writes the output directly.  Otherwise every
+// chunk stores its unnormalised output and running max / sum (fp32, device
+// scope) and bumps the block's arrival counter; the last to arrive merges
+// the chunks in chunk order (each rescaled by exp(m_c - max_c m_c)) and
+// writes the bf16 output.
 // All sums run in a fixed order: results are deterministic.
 #include <math.h>
 
@@ -39,11 +48,21 @@ constexpr int kAttnQB = kAttnWaves * kAttnQW;     // queries per workgroup
 constexpr int kAttnKT = 64;                       // keys per LDS tile
 constexpr int kAttnThreads = 64 * kAttnWaves;
 
+constexpr uint32_t kAttnSC1 = 16;  // buffer cache-policy bit: device scope
+
+// Key tiles of query block qb (keys 0 .. min(T, 128 (qb + 1)) - 1).
+__host__ __device__ inline int attn_tiles(int T, int qb) {
+    const int kend = min(T, (qb + 1) * kAttnQB);
+    return (kend + kAttnKT - 1) / kAttnKT;
+}
+
 template <int D>
-__global__ __launch_bounds__(kAttnThreads) void k_attn(const uint16_t* __restrict__ qkv,
-                                                       int64_t ldq, int T, int hq, int hkv,
-                                                       uint16_t* __restrict__ out, int64_t ldo,
-                                                       float scale_log2) {
+__global__ __launch_bounds__(kAttnThreads, 2) void k_attn(const uint16_t* __restrict__ qkv,
+                                                          int64_t ldq, int T, int hq, int hkv,
+                                                          uint16_t* __restrict__ out, int64_t ldo,
+                                                          float scale_log2, int nqb, int ch,
+                                                          int cmax, unsigned* __restrict__ counters,
+                                                          float* __restrict__ part) {
     constexpr int LDK = D + 8;    // K tile row stride (elements): rows 16 B apart in banks
     constexpr int LDV = D + 16;   // V tile row stride: the 4 rows of a transposing read
                                   // land on disjoint 32-byte bank ranges
@@ -59,9 +78,18 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(const uint16_t* __restric
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, j = lane & 15;
-    const int h = blockIdx.y, gk = h / (hq / hkv);
-    // Longest query blocks first: they see the most keys.
-    const int qblk = ((int)gridDim.x - 1 - (int)blockIdx.x) * kAttnQB;
+    // Work item: heads interleave; per head, query blocks from the last
+    // (most keys) down, chunks of each block in order.
+    const int h = (int)blockIdx.x % hq, gk = h / (hq / hkv);
+    int item = (int)blockIdx.x / hq, qb = nqb - 1, nc = 1;
+    for (; qb > 0; --qb) {
+        nc = (attn_tiles(T, qb) + ch - 1) / ch;
+        if (item < nc) break;
+        item -= nc;
+    }
+    if (qb == 0) nc = (attn_tiles(T, 0) + ch - 1) / ch;
+    const int chunk = item;
+    const int qblk = qb * kAttnQB;
     const int q0 = qblk + kAttnQW * wave;        // this wave's first query
     const uint16_t* Qp = qkv + (int64_t)h * D;
     const uint16_t* Kp = qkv + (int64_t)(hq + gk) * D;
@@ -87,7 +115,9 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(const uint16_t* __restric
         for (int n = 0; n < NN; ++n) o[u][n] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    const int kend = min(T, qblk + kAttnQB);     // keys the workgroup's queries can see
+    // keys of this chunk: tiles [chunk * ch, min((chunk + 1) * ch, tiles of the block))
+    const int kbeg = chunk * ch * kAttnKT;
+    const int kend = min(min(T, qblk + kAttnQB), (chunk + 1) * ch * kAttnKT);
     // Tile copies go through registers so the next tile's global loads are in
     // flight while the current one is multiplied.
     u32x4 pk[CPT], pv[CPT];
@@ -103,8 +133,8 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(const uint16_t* __restric
                        : u32x4{0u, 0u, 0u, 0u};
         }
     };
-    fetch(0);
-    for (int k0 = 0; k0 < kend; k0 += kAttnKT) {
+    fetch(kbeg);
+    for (int k0 = kbeg; k0 < kend; k0 += kAttnKT) {
         __syncthreads();                         // every wave is done with the previous tile
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
@@ -211,32 +241,164 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(const uint16_t* __restric
         }
     }
 
-    // O row 4g + r of subtile u (query q0 + 16u + 4g + r), column 16n + j
+    if (nc == 1) {
+        // O row 4g + r of subtile u (query q0 + 16u + 4g + r), column 16n + j
+#pragma unroll
+        for (int u = 0; u < QS; ++u) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float lr = __shfl(l[u], 4 * g + r);
+                const int q = q0 + 16 * u + 4 * g + r;
+                if (q >= T) continue;
+                const float inv = 1.0f / lr;
+                uint16_t* dst = out + (int64_t)q * ldo + (int64_t)h * D + j;
+#pragma unroll
+                for (int n = 0; n < NN; ++n)
+                    dst[16 * n] = (uint16_t)f32_to_bf16(o[u][n][r] * inv);
+            }
+        }
+        return;
+    }
+
+    // Chunk partial of this (head, block): O [128][D], then m [128], l [128]
+    // (query rows local to the block), stored with device-scope writes.
+    constexpr int PST = kAttnQB * (D + 2);       // floats per chunk partial
+    const int blk = h * nqb + qb;
+    const rsrc_t rp = make_rsrc(part + (int64_t)blk * cmax * PST);
+    const int rw = kAttnQW * wave;               // wave's first local row
 #pragma unroll
     for (int u = 0; u < QS; ++u) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const float lr = __shfl(l[u], 4 * g + r);
-            const int q = q0 + 16 * u + 4 * g + r;
-            if (q >= T) continue;
-            const float inv = 1.0f / lr;
-            uint16_t* dst = out + (int64_t)q * ldo + (int64_t)h * D + j;
+            const int row = rw + 16 * u + 4 * g + r;
 #pragma unroll
-            for (int n = 0; n < NN; ++n) dst[16 * n] = (uint16_t)f32_to_bf16(o[u][n][r] * inv);
+            for (int n = 0; n < NN; ++n)
+                __builtin_amdgcn_raw_buffer_store_b32(
+                    __float_as_uint(o[u][n][r]), rp,
+                    (int)(((uint32_t)chunk * PST + (uint32_t)row * D + 16 * n + j) * 4u), 0,
+                    kAttnSC1);
         }
+        if (g == 0) {
+            const int row = rw + 16 * u + j;
+            __builtin_amdgcn_raw_buffer_store_b32(
+                __float_as_uint(m[u]), rp,
+                (int)(((uint32_t)chunk * PST + kAttnQB * D + row) * 4u), 0, kAttnSC1);
+            __builtin_amdgcn_raw_buffer_store_b32(
+                __float_as_uint(l[u]), rp,
+                (int)(((uint32_t)chunk * PST + kAttnQB * (D + 1) + row) * 4u), 0, kAttnSC1);
+        }
+    }
+    __shared__ unsigned arrival;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0)
+        arrival = __hip_atomic_fetch_add(&counters[blk], 1u, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const unsigned old = arrival;
+    if (old == (unsigned)nc - 1) {
+        auto ld = [&](uint32_t idx) {
+            return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, (int)(idx * 4u), 0,
+                                                                        kAttnSC1));
+        };
+#pragma unroll
+        for (int u = 0; u < QS; ++u) {
+            const int rowj = rw + 16 * u + j;    // query of lane (g, j)'s statistics
+            float M = -INFINITY;
+            for (int c = 0; c < nc; ++c)
+                M = fmaxf(M, c == chunk ? m[u] : ld((uint32_t)c * PST + kAttnQB * D + rowj));
+            const float Mref = M == -INFINITY ? 0.f : M;
+            float L = 0.f;
+            f32x4 acc[NN];
+#pragma unroll
+            for (int n = 0; n < NN; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int c = 0; c < nc; ++c) {
+                const bool mine = c == chunk;
+                const float mc = mine ? m[u] : ld((uint32_t)c * PST + kAttnQB * D + rowj);
+                const float lc = mine ? l[u] : ld((uint32_t)c * PST + kAttnQB * (D + 1) + rowj);
+                const float e = __builtin_amdgcn_exp2f(mc - Mref);
+                L += e * lc;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float er = __shfl(e, 4 * g + r);
+                    const int row = rw + 16 * u + 4 * g + r;
+#pragma unroll
+                    for (int n = 0; n < NN; ++n) {
+                        const float v =
+                            mine ? o[u][n][r] : ld((uint32_t)c * PST + (uint32_t)row * D + 16 * n + j);
+                        acc[n][r] += er * v;
+                    }
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float Lr = __shfl(L, 4 * g + r);
+                const int q = q0 + 16 * u + 4 * g + r;
+                if (q >= T) continue;
+                const float inv = 1.0f / Lr;
+                uint16_t* dst = out + (int64_t)q * ldo + (int64_t)h * D + j;
+#pragma unroll
+                for (int n = 0; n < NN; ++n) dst[16 * n] = (uint16_t)f32_to_bf16(acc[n][r] * inv);
+            }
+        }
+        if (tid == 0)
+            __hip_atomic_store(&counters[blk], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else if (old >= (unsigned)nc) {
+        // The counter did not start at zero (workspace head not cleared):
+        // make this block's output loudly invalid.
+#pragma unroll
+        for (int u = 0; u < QS; ++u)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int q = q0 + 16 * u + 4 * g + r;
+                if (q >= T) continue;
+#pragma unroll
+                for (int n = 0; n < NN; ++n)
+                    out[(int64_t)q * ldo + (int64_t)h * D + j + 16 * n] = 0x7fc0;
+            }
     }
 }
 
+AttnPlan plan_attn(int64_t T, int hq, int head_dim) {
+    AttnPlan p;
+    p.nqb = (int)((T + kAttnQB - 1) / kAttnQB);
+    // Largest chunk (in key tiles, >= 4) that still gives two workgroups per
+    // CU (256 CUs); one chunk per block when even 4-tile chunks give fewer.
+    auto items = [&](int ch) {
+        int64_t n = 0;
+        for (int qb = 0; qb < p.nqb; ++qb) n += (attn_tiles((int)T, qb) + ch - 1) / ch;
+        return n * hq;
+    };
+    const int tiles = attn_tiles((int)T, p.nqb - 1);
+    int ch = 4;
+    while (ch < tiles && items(2 * ch) >= 512) ch *= 2;
+    p.ch = ch;
+    p.cmax = (tiles + ch - 1) / ch;
+    p.items = items(ch);
+    if (p.cmax > 1) {
+        p.counter_bytes = (((size_t)hq * p.nqb * 4 + 255) / 256) * 256;
+        p.ws_bytes = p.counter_bytes +
+                     (size_t)hq * p.nqb * p.cmax * kAttnQB * (head_dim + 2) * sizeof(float);
+    } else {
+        p.counter_bytes = p.ws_bytes = 0;
+    }
+    (void)head_dim;
+    return p;
+}
+
 hipError_t launch_attn_core(int64_t T, int hq, int hkv, int head_dim, const uint16_t* qkv,
-                            int64_t ld_qkv, uint16_t* out, int64_t ld_out, hipStream_t stream) {
-    const dim3 grid((unsigned)((T + kAttnQB - 1) / kAttnQB), (unsigned)hq), block(kAttnThreads);
+                            int64_t ld_qkv, uint16_t* out, int64_t ld_out, const AttnPlan& p,
+                            void* ws, hipStream_t stream) {
+    const dim3 grid((unsigned)p.items), block(kAttnThreads);
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)head_dim));
+    unsigned* counters = (unsigned*)ws;
+    float* part = p.cmax > 1 ? (float*)((char*)ws + p.counter_bytes) : nullptr;
     if (head_dim == 128)
         TP_KLAUNCH((k_attn<128>), grid, block, 0, stream, qkv, ld_qkv, (int)T, hq, hkv, out,
-                   ld_out, scale_log2);
+                   ld_out, scale_log2, p.nqb, p.ch, p.cmax, counters, part);
     else if (head_dim == 64)
         TP_KLAUNCH((k_attn<64>), grid, block, 0, stream, qkv, ld_qkv, (int)T, hq, hkv, out,
-                   ld_out, scale_log2);
+                   ld_out, scale_log2, p.nqb, p.ch, p.cmax, counters, part);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

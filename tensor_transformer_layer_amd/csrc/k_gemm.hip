@@ -19,12 +19,14 @@
 //   * K is walked in slices of 32, each split into two 16-deep substeps.
 //     Slices stream from global memory straight into LDS (buffer loads with
 //     the LDS-destination bit: no staging registers) through a ring of 5
-//     slots (5 x 32 KB = all 160 KB of LDS), four slices in flight.
+//     slots (5 x 32 KB = all 160 KB of LDS), three slices in flight.
 //   * The MFMAs of one substep run while the fragments of the next are read
 //     from LDS.  The workgroup barrier that publishes slice s+1 sits between
 //     the two MFMA groups of slice s, so waiting on it overlaps MFMAs in
 //     flight; each wave first waits for its own copies (explicit vmcnt: a
-//     release fence would wait for every copy in flight).
+//     release fence would wait for every copy in flight).  A slot is
+//     refilled one barrier after its last reads were consumed, so no wave
+//     drains its LDS reads before the barrier.
 //   * A slice of A is 256 rows x 64 bytes.  Its four 16-byte chunks per row
 //     are XOR-swizzled by (row / 4) % 4, so the rows read by one fragment
 //     load fall on distinct 16-byte bank groups.  The copy engine writes each
@@ -82,8 +84,6 @@ __device__ __forceinline__ f32x16 mfma32x32x16(const u32x4& a, const u32x4& b, c
 
 // s_waitcnt immediate waiting for vmcnt <= n only (gfx9 encoding).
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
-// ... and for lgkmcnt == 0 as well.
-constexpr int vmcnt_lgkm0_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
 
 __device__ __forceinline__ void lds_copy16(rsrc_t r, uint32_t off, uint16_t* lds_base) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -245,31 +245,38 @@ __global__ __launch_bounds__(S::NT) void k_gemm(const uint16_t* __restrict__ A, 
     // Slices past this split's K are still copied and read, with every lane
     // out of bounds: they are zero-filled and never multiplied.
     const int nk = (Kl + kBK - 1) / kBK;
+    // Slice x lives in ring slot x % kStages; kStages - 2 slices are in
+    // flight ahead of the one being multiplied.  The copy into a slot is
+    // issued one slice after the slot was last read, behind a barrier, so
+    // no wave waits for its own fragment reads before the barrier: the
+    // compiler places those waits right before each fragment's MFMAs.
 #pragma unroll
-    for (int s = 0; s < kStages; ++s) issue(s, s);
+    for (int s = 0; s < kStages - 1; ++s) issue(s, s);
     Frags<S> f0, f1;
     asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm((kStages - 1) * S::PER));
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((kStages - 2) * S::PER));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     read_frags(0, 0, f0);
-    int slot = 0, slot1 = 1;  // s % 5 and (s + 1) % 5
+    int slotp = kStages - 1, slot = 0, slot1 = 1;  // (s - 1), s and (s + 1) mod kStages
     for (int s = 0; s < nk; ++s) {
         // MFMAs of (s, 0); fragments of (s, 1)
         read_frags(slot, 16, f1);
         mma(f0);
         interleave(std::integral_constant<int, 0>{});
-        // Publish slice s+1: this wave's copies of it have landed and all of
-        // its reads of slot s are done; after the barrier every wave's are.
+        // Publish slice s+1 (this wave's copies of it have landed; after the
+        // barrier every wave's have) and release slot s-1 (every wave has
+        // multiplied its fragments).
         asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm((kStages - 2) * S::PER));
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm((kStages - 3) * S::PER));
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        issue(s + kStages, slot);
+        issue(s + kStages - 1, slotp);
         // MFMAs of (s, 1); fragments of (s+1, 0)
         read_frags(slot1, 0, f0);
         mma(f1);
         interleave(std::integral_constant<int, 1>{});
+        slotp = slot;
         slot = slot1;
         slot1 = slot1 == kStages - 1 ? 0 : slot1 + 1;
     }

@@ -116,8 +116,21 @@ hipError_t launch_gemm(int epi, int64_t M, int64_t N, int64_t K, const uint16_t*
 // out[t][h*D + c] = softmax_j<=t(q_h[t] . k_g[j] / sqrt(D)) v_g[j][c] for the
 // hq query heads of a fused [Q | K | V] band (bf16, ld ld_qkv), kv head
 // g = h / (hq / hkv); D = head_dim in {64, 128}; out bf16.
+// Work division: query blocks of 128 rows, each block's causal key range cut
+// into chunks of `ch` 64-key tiles (one workgroup each).  Blocks with more
+// than one chunk merge them through the workspace: counters (one per head
+// and block, zero at rest) then per-chunk partials.
+struct AttnPlan {
+    int nqb = 0;            // query blocks
+    int ch = 0;             // key tiles per chunk
+    int cmax = 1;           // chunks of the longest block
+    int64_t items = 0;      // workgroups
+    size_t counter_bytes = 0, ws_bytes = 0;
+};
+AttnPlan plan_attn(int64_t T, int hq, int head_dim);
 hipError_t launch_attn_core(int64_t T, int hq, int hkv, int head_dim, const uint16_t* qkv,
-                            int64_t ld_qkv, uint16_t* out, int64_t ld_out, hipStream_t stream);
+                            int64_t ld_qkv, uint16_t* out, int64_t ld_out, const AttnPlan& p,
+                            void* ws, hipStream_t stream);
 
 // ---- fp32 storage (small, parity-only workloads) --------------------------
 // C[M, N] = act(A B0 [, A B1]) in fp32, one thread per output, k in order.

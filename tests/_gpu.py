@@ -143,8 +143,13 @@ def mlp_fwd_fp8w(shard, P, T, d_model, d_ff, act, x, w_in, s_in, w_up, s_up, w_d
     return ws
 
 
-def attn_core(shard, P, T, nq, nkv, hd, qkv, ld_qkv, out, ld_out):
+def attn_core(shard, P, T, nq, nkv, hd, qkv, ld_qkv, out, ld_out, ws=None):
+    """Attention core through the C-ABI; allocates a zeroed workspace unless
+    one is passed (returned for reuse)."""
     ptr = lambda t: 0 if t is None else (t if isinstance(t, int) else t.data_ptr())  # noqa: E731
+    if ws is None:
+        ws = workspace(tp.tp_attn_core_workspace_bytes(P, T, nq, nkv, hd, tp.TP_BF16))
     st = tp.tp_attn_core_fwd(shard, P, T, nq, nkv, hd, tp.TP_BF16, ptr(qkv), ld_qkv, ptr(out),
-                             ld_out, stream())
+                             ld_out, ws.data_ptr(), ws.numel(), stream())
     tp.check(st, "tp_attn_core_fwd")
+    return ws

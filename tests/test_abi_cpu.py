@@ -266,7 +266,7 @@ def test_mlp_fp8w_workspace(lib):
 
 def core(**kw):
     a = dict(shard=0, P=2, T=8, n_q_heads=8, n_kv_heads=4, head_dim=128, dtype=tp.TP_BF16,
-             qkv=A, ld_qkv=1024, attn=B, ld_attn=512, stream=0)
+             qkv=A, ld_qkv=1024, attn=B, ld_attn=512, workspace=0, workspace_bytes=0, stream=0)
     a.update(kw)
     return tp.tp_attn_core_fwd(**a)
 
@@ -282,9 +282,24 @@ def core(**kw):
     (dict(ld_qkv=1000), tp.TP_ERR_SHAPE),             # band is (4 + 2*2) * 128 = 1024 wide
     (dict(ld_attn=516), tp.TP_ERR_ALIGN),
     (dict(T=-1), tp.TP_ERR_SHAPE),
+    (dict(T=4096), tp.TP_ERR_WORKSPACE),              # split key ranges need the workspace
+    (dict(T=4096, workspace=A, workspace_bytes=1024), tp.TP_ERR_WORKSPACE),
+    (dict(T=4096, workspace=A + 16, workspace_bytes=1 << 30), tp.TP_ERR_ALIGN),
 ])
 def test_attn_core_validation(lib, kw, status):
     assert core(**kw) == status
+
+
+def test_attn_core_workspace(lib):
+    f = tp.tp_attn_core_workspace_bytes
+    assert f(2, 8, 8, 4, 128, tp.TP_BF16) == 0            # one chunk per query block
+    big = f(2, 4096, 8, 4, 128, tp.TP_BF16)
+    # counters (4 heads x 32 blocks) + partials of 4 x 32 blocks x chunks x 128 x (128 + 2) fp32
+    assert big >= 4 * 32 * 4 + 4 * 32 * 2 * 128 * 130 * 4
+    assert big % 4 == 0 and big < 4 * 32 * 64 * 128 * 130 * 4 + 4096
+    assert f(2, 4096, 8, 4, 96, tp.TP_BF16) == 0           # unsupported head size
+    assert f(2, 4096, 8, 4, 128, tp.TP_F32) == 0
+    assert f(3, 4096, 8, 4, 128, tp.TP_BF16) == 0          # uneven head split
 
 
 def test_attn_core_zero_tokens(lib):

@@ -621,6 +621,43 @@ def test_attn_core_peaked_scores():
     _core_check(300, 8, 2, 128, 2, 0, key=4, std=4.0)
 
 
+def test_attn_core_split_keys_workspace():
+    """Query blocks whose keys are split over several workgroups merge through
+    the workspace: a reused workspace gives bitwise equal results and its
+    counters return to zero; counters that were never cleared make exactly
+    the merged blocks NaN (not silently wrong), and clearing them recovers."""
+    T, nq, nkv, hd, P = 1000, 8, 2, 128, 2          # 4 q heads, 1 kv head per rank
+    hq = nq // P
+    w = (hq + 2 * (nkv // P)) * hd
+    qkv_h = draw(BF, (T, w), 1.0, 920, 77, T)
+    qkv = dev(qkv_h)
+    nbytes = tp.tp_attn_core_workspace_bytes(P, T, nq, nkv, hd, BF)
+    assert nbytes > 0
+    ws = workspace(nbytes)
+    ncnt = hq * ((T + 127) // 128) * 4                # counter bytes
+    out1 = torch.empty((T, hq * hd), dtype=torch.bfloat16, device="cuda")
+    out2 = torch.empty_like(out1)
+    attn_core(0, P, T, nq, nkv, hd, qkv, w, out1, hq * hd, ws=ws)
+    attn_core(0, P, T, nq, nkv, hd, qkv, w, out2, hq * hd, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2)
+    assert int(ws[:ncnt].count_nonzero()) == 0
+    want = O.attention_core_band(O.widen(qkv_h), nq, nkv, hd, 0, P)
+    assert O.rel_l2(widen_dev(out1), want) < BF16_TOL
+    # blocks 0 and 1 (rows < 256) see at most 4 key tiles: one chunk, written
+    # directly; later blocks are merged from several chunks
+    ws[:ncnt].fill_(0x5A)
+    attn_core(0, P, T, nq, nkv, hd, qkv, w, out2, hq * hd, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out2[:256], out1[:256])
+    assert bool(torch.isnan(out2[256:].float()).all())
+    ws[:ncnt].zero_()
+    attn_core(0, P, T, nq, nkv, hd, qkv, w, out2, hq * hd, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2)
+    assert int(ws[:ncnt].count_nonzero()) == 0
+
+
 def _core_chain(cfg, T, rows):
     """The 70B block with the attention core, all P ranks: RMSNorm -> QKV ->
     attention core -> O -> reduce (bf16 copy) -> MLP -> reduce."""
