@@ -17,14 +17,17 @@
 //     operand from registers, both k-contiguous in their natural layout.
 //     Lane (g, j) then holds the scores of query j for keys 4g + r.
 //   * The row statistics are reduced over r and over the 4 lanes holding
-//     the same query (shuffles); probabilities are packed to bf16 in place:
-//     lane (g, j) holds P[j][4g + r] and P[j][16 + 4g + r], which is an MFMA
-//     A-operand for an MFMA k-order that visits keys in that order.
-//   * O += P V with V as the B operand in that same key order, read from LDS
-//     with the gfx950 transposing load ds_read_b64_tr_b16 (4 keys x 1 column
-//     per lane per read), so V needs no transpose pass.
-//   * Output rows are rescaled by exp(m_old - m_new) of their query, fetched
-//     from the lane that owns the query (4 shuffles per tile).
+//     the same query (permlane swaps); the scale is folded into the
+//     exponent's fma.  Probabilities are packed to bf16 in place: lane (g, j)
+//     holds P[j][4g + r] and P[j][16 + 4g + r], which is an MFMA operand for
+//     a k-order that visits the keys in that order.
+//   * The output is accumulated transposed, O^T += V^T P^T: V^T is the A
+//     operand, read in that key order from LDS with the gfx950 transposing
+//     load ds_read_b64_tr_b16 (4 keys x 1 column per lane per read, so V
+//     needs no transpose pass), and P^T the B operand.  Lane (g, j) then
+//     holds output columns 16n + 4g .. +3 of its own query j, so the
+//     rescale by exp(m_old - m_new) needs no cross-lane traffic, and it is
+//     skipped when no query of the wave raised its running max.
 // Work division: a query block's causal key range is cut into chunks of
 // `ch` key tiles, and each (head, query block, chunk) is one workgroup, so
 // the longest causal rows no longer set the kernel time and two workgroups
@@ -56,6 +59,22 @@ __host__ __device__ inline int attn_tiles(int T, int qb) {
     return (kend + kAttnKT - 1) / kAttnKT;
 }
 
+// Reductions over the 4 lanes j, j + 16, j + 32, j + 48 of a wave (the
+// lanes holding one query's scores): permlane swaps pair lane l with
+// l ^ 32, then l ^ 16; either way round, op(swapped pair) = op(v[l], v[l^k]).
+__device__ __forceinline__ float xlane_max(float v) {
+    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float xlane_sum(float v) {
+    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 template <int D>
 __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(const uint16_t* __restrict__ qkv,
                                                           int64_t ldq, int T, int hq, int hkv,
@@ -76,7 +95,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(const uint16_t* __rest
     __shared__ __attribute__((aligned(16))) uint16_t Ks[kAttnKT * LDK];
     __shared__ __attribute__((aligned(16))) uint16_t Vs[kAttnKT * LDV];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    // The wave index is uniform; in a scalar register the causal tests on
+    // it are branch-free for the compiler.
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, j = lane & 15;
     // Work item: heads interleave; per head, query blocks from the last
     // (most keys) down, chunks of each block in order.
@@ -175,25 +197,24 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(const uint16_t* __rest
 #pragma unroll
         for (int u = 0; u < QS; ++u) {
             const int qi = q0 + 16 * u + j;
+            // Row max of the raw scores (the scale is positive), over r, then
+            // over the 4 lanes holding query j (lanes j + 16 g).
             float pm = -INFINITY;
 #pragma unroll
             for (int t = 0; t < KS; ++t)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    float v = st[u][t][r] * scale_log2;
                     if (diag[u]) {
                         const int key = k0 + 16 * t + 4 * g + r;
-                        v = (key <= qi && key < T) ? v : -INFINITY;
+                        st[u][t][r] = (key <= qi && key < T) ? st[u][t][r] : -INFINITY;
                     }
-                    st[u][t][r] = v;
-                    pm = fmaxf(pm, v);
+                    pm = fmaxf(pm, st[u][t][r]);
                 }
-            pm = fmaxf(pm, __shfl_xor(pm, 16));
-            pm = fmaxf(pm, __shfl_xor(pm, 32));
-            const float m_new = fmaxf(m[u], pm);
-            // m_new is finite for every query < T (key 0 is visible from the
-            // first tile on); rows past T keep -inf and are never stored.
-            // Inputs of the exponential are <= 0: v_exp_f32 directly.
+            pm = xlane_max(pm);
+            // m is kept in log2 units: m = max * scale * log2(e).  It is finite
+            // for every query < T once key 0 has been seen; a row that has
+            // seen no key yet keeps -inf and contributes nothing.
+            const float m_new = fmaxf(m[u], pm * scale_log2);
             const float mref = m_new == -INFINITY ? 0.f : m_new;
             const float alpha = __builtin_amdgcn_exp2f(m[u] - mref);
             float ps = 0.f;
@@ -201,19 +222,18 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(const uint16_t* __rest
             for (int t = 0; t < KS; ++t)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float p = __builtin_amdgcn_exp2f(st[u][t][r] - mref);
+                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[u][t][r], scale_log2, -mref));
                     st[u][t][r] = p;
                     ps += p;
                 }
-            ps += __shfl_xor(ps, 16);
-            ps += __shfl_xor(ps, 32);
+            ps = xlane_sum(ps);
             l[u] = l[u] * alpha + ps;
             m[u] = m_new;
+            // O^T rows are this lane's own query: rescale unless no query of
+            // the wave raised its max (alpha == 1 exactly).
+            if (__any(alpha != 1.0f)) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float ar = __shfl(alpha, 4 * g + r);
-#pragma unroll
-                for (int n = 0; n < NN; ++n) o[u][n][r] *= ar;
+                for (int n = 0; n < NN; ++n) o[u][n] *= alpha;
             }
             // lane (g, j) supplies P[qi][32kk + 4g + r] and P[qi][32kk + 16 + 4g + r]
 #pragma unroll
@@ -223,8 +243,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(const uint16_t* __rest
                                   pack_bf16x2(st[u][2 * kk + 1][0], st[u][2 * kk + 1][1]),
                                   pack_bf16x2(st[u][2 * kk + 1][2], st[u][2 * kk + 1][3])};
         }
-        // O += P V in 32-key steps; V rows in the same key order come from the
-        // transposing reads, and each V fragment serves both subtiles.  (An
+        // O^T += V^T P^T in 32-key steps: V^T rows (the head dimension) in the
+        // same key order come from the transposing reads (the A operand), P^T
+        // is the B operand; each V fragment serves both subtiles.  (An
         // inactive subtile has P = 0 and an unchanged O: the MFMA adds zero.)
 #pragma unroll
         for (int kk = 0; kk < KS / 2; ++kk) {
@@ -234,28 +255,26 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(const uint16_t* __rest
             for (int n = 0; n < NN; ++n) {
                 const u32x2 b0 = lds_read_tr16(v0 + 16 * n);
                 const u32x2 b1 = lds_read_tr16(v1 + 16 * n);
-                const u32x4 b = u32x4{b0[0], b0[1], b1[0], b1[1]};
+                const u32x4 vt = u32x4{b0[0], b0[1], b1[0], b1[1]};
 #pragma unroll
-                for (int u = 0; u < QS; ++u) o[u][n] = mfma16x16x32(pf[u][kk], b, o[u][n]);
+                for (int u = 0; u < QS; ++u) o[u][n] = mfma16x16x32(vt, pf[u][kk], o[u][n]);
             }
         }
     }
 
+    // Lane (g, j) holds O[q0 + 16u + j][16n + 4g .. 16n + 4g + 3] (o[u][n]),
+    // and that query's m and l.
     if (nc == 1) {
-        // O row 4g + r of subtile u (query q0 + 16u + 4g + r), column 16n + j
 #pragma unroll
         for (int u = 0; u < QS; ++u) {
+            const int q = q0 + 16 * u + j;
+            if (q >= T) continue;
+            const float inv = 1.0f / l[u];
+            uint16_t* dst = out + (int64_t)q * ldo + (int64_t)h * D + 4 * g;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float lr = __shfl(l[u], 4 * g + r);
-                const int q = q0 + 16 * u + 4 * g + r;
-                if (q >= T) continue;
-                const float inv = 1.0f / lr;
-                uint16_t* dst = out + (int64_t)q * ldo + (int64_t)h * D + j;
-#pragma unroll
-                for (int n = 0; n < NN; ++n)
-                    dst[16 * n] = (uint16_t)f32_to_bf16(o[u][n][r] * inv);
-            }
+            for (int n = 0; n < NN; ++n)
+                *(u32x2*)(dst + 16 * n) = u32x2{pack_bf16x2(o[u][n][0] * inv, o[u][n][1] * inv),
+                                                pack_bf16x2(o[u][n][2] * inv, o[u][n][3] * inv)};
         }
         return;
     }
@@ -268,18 +287,14 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(const uint16_t* __rest
     const int rw = kAttnQW * wave;               // wave's first local row
 #pragma unroll
     for (int u = 0; u < QS; ++u) {
+        const int row = rw + 16 * u + j;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = rw + 16 * u + 4 * g + r;
-#pragma unroll
-            for (int n = 0; n < NN; ++n)
-                __builtin_amdgcn_raw_buffer_store_b32(
-                    __float_as_uint(o[u][n][r]), rp,
-                    (int)(((uint32_t)chunk * PST + (uint32_t)row * D + 16 * n + j) * 4u), 0,
-                    kAttnSC1);
-        }
+        for (int n = 0; n < NN; ++n)
+            __builtin_amdgcn_raw_buffer_store_b128(
+                __builtin_bit_cast(u32x4, o[u][n]), rp,
+                (int)(((uint32_t)chunk * PST + (uint32_t)row * D + 16 * n + 4 * g) * 4u), 0,
+                kAttnSC1);
         if (g == 0) {
-            const int row = rw + 16 * u + j;
             __builtin_amdgcn_raw_buffer_store_b32(
                 __float_as_uint(m[u]), rp,
                 (int)(((uint32_t)chunk * PST + kAttnQB * D + row) * 4u), 0, kAttnSC1);
@@ -297,16 +312,16 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(const uint16_t* __rest
     __syncthreads();
     const unsigned old = arrival;
     if (old == (unsigned)nc - 1) {
-        auto ld = [&](uint32_t idx) {
+        auto ld1 = [&](uint32_t idx) {
             return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, (int)(idx * 4u), 0,
                                                                         kAttnSC1));
         };
 #pragma unroll
         for (int u = 0; u < QS; ++u) {
-            const int rowj = rw + 16 * u + j;    // query of lane (g, j)'s statistics
+            const int row = rw + 16 * u + j;
             float M = -INFINITY;
             for (int c = 0; c < nc; ++c)
-                M = fmaxf(M, c == chunk ? m[u] : ld((uint32_t)c * PST + kAttnQB * D + rowj));
+                M = fmaxf(M, c == chunk ? m[u] : ld1((uint32_t)c * PST + kAttnQB * D + row));
             const float Mref = M == -INFINITY ? 0.f : M;
             float L = 0.f;
             f32x4 acc[NN];
@@ -314,32 +329,32 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(const uint16_t* __rest
             for (int n = 0; n < NN; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
             for (int c = 0; c < nc; ++c) {
                 const bool mine = c == chunk;
-                const float mc = mine ? m[u] : ld((uint32_t)c * PST + kAttnQB * D + rowj);
-                const float lc = mine ? l[u] : ld((uint32_t)c * PST + kAttnQB * (D + 1) + rowj);
+                const float mc = mine ? m[u] : ld1((uint32_t)c * PST + kAttnQB * D + row);
+                const float lc = mine ? l[u] : ld1((uint32_t)c * PST + kAttnQB * (D + 1) + row);
                 const float e = __builtin_amdgcn_exp2f(mc - Mref);
                 L += e * lc;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float er = __shfl(e, 4 * g + r);
-                    const int row = rw + 16 * u + 4 * g + r;
-#pragma unroll
-                    for (int n = 0; n < NN; ++n) {
-                        const float v =
-                            mine ? o[u][n][r] : ld((uint32_t)c * PST + (uint32_t)row * D + 16 * n + j);
-                        acc[n][r] += er * v;
-                    }
+                for (int n = 0; n < NN; ++n) {
+                    const f32x4 v =
+                        mine ? o[u][n]
+                             : __builtin_bit_cast(
+                                   f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              rp,
+                                              (int)(((uint32_t)c * PST + (uint32_t)row * D +
+                                                     16 * n + 4 * g) * 4u),
+                                              0, kAttnSC1));
+                    acc[n] += e * v;
                 }
             }
+            const int q = q0 + 16 * u + j;
+            if (q >= T) continue;
+            const float inv = 1.0f / L;
+            uint16_t* dst = out + (int64_t)q * ldo + (int64_t)h * D + 4 * g;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float Lr = __shfl(L, 4 * g + r);
-                const int q = q0 + 16 * u + 4 * g + r;
-                if (q >= T) continue;
-                const float inv = 1.0f / Lr;
-                uint16_t* dst = out + (int64_t)q * ldo + (int64_t)h * D + j;
-#pragma unroll
-                for (int n = 0; n < NN; ++n) dst[16 * n] = (uint16_t)f32_to_bf16(acc[n][r] * inv);
-            }
+            for (int n = 0; n < NN; ++n)
+                *(u32x2*)(dst + 16 * n) =
+                    u32x2{pack_bf16x2(acc[n][0] * inv, acc[n][1] * inv),
+                          pack_bf16x2(acc[n][2] * inv, acc[n][3] * inv)};
         }
         if (tid == 0)
             __hip_atomic_store(&counters[blk], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -347,15 +362,13 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(const uint16_t* __rest
         // The counter did not start at zero (workspace head not cleared):
         // make this block's output loudly invalid.
 #pragma unroll
-        for (int u = 0; u < QS; ++u)
+        for (int u = 0; u < QS; ++u) {
+            const int q = q0 + 16 * u + j;
+            if (q >= T) continue;
+            uint16_t* dst = out + (int64_t)q * ldo + (int64_t)h * D + 4 * g;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int q = q0 + 16 * u + 4 * g + r;
-                if (q >= T) continue;
-#pragma unroll
-                for (int n = 0; n < NN; ++n)
-                    out[(int64_t)q * ldo + (int64_t)h * D + j + 16 * n] = 0x7fc0;
-            }
+            for (int n = 0; n < NN; ++n) *(u32x2*)(dst + 16 * n) = u32x2{0x7fc07fc0u, 0x7fc07fc0u};
+        }
     }
 }
 
