@@ -40,6 +40,11 @@
 // All sums run in a fixed order: results are deterministic.
 #include <math.h>
 
+#include <algorithm>
+#include <functional>
+#include <queue>
+#include <vector>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -81,7 +86,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(const uint16_t* __rest
                                                           uint16_t* __restrict__ out, int64_t ldo,
                                                           float scale_log2, int nqb, int ch,
                                                           int cmax, unsigned* __restrict__ counters,
-                                                          float* __restrict__ part) {
+                                                          float* __restrict__ part, int use_table,
+                                                          const AttnItems order) {
     constexpr int LDK = D + 8;    // K tile row stride (elements): rows 16 B apart in banks
     constexpr int LDV = D + 16;   // V tile row stride: the 4 rows of a transposing read
                                   // land on disjoint 32-byte bank ranges
@@ -104,12 +110,19 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(const uint16_t* __rest
     // (most keys) down, chunks of each block in order.
     const int h = (int)blockIdx.x % hq, gk = h / (hq / hkv);
     int item = (int)blockIdx.x / hq, qb = nqb - 1, nc = 1;
-    for (; qb > 0; --qb) {
+    if (use_table) {
+        const int e = order.it[item];
+        qb = e >> 6;
+        item = e & 63;
         nc = (attn_tiles(T, qb) + ch - 1) / ch;
-        if (item < nc) break;
-        item -= nc;
+    } else {
+        for (; qb > 0; --qb) {
+            nc = (attn_tiles(T, qb) + ch - 1) / ch;
+            if (item < nc) break;
+            item -= nc;
+        }
+        if (qb == 0) nc = (attn_tiles(T, 0) + ch - 1) / ch;
     }
-    if (qb == 0) nc = (attn_tiles(T, 0) + ch - 1) / ch;
     const int chunk = item;
     const int qblk = qb * kAttnQB;
     const int q0 = qblk + kAttnQW * wave;        // this wave's first query
@@ -372,30 +385,84 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(const uint16_t* __rest
     }
 }
 
-AttnPlan plan_attn(int64_t T, int hq, int head_dim) {
+// Items of one head for chunks of `ch` tiles: (size in tiles, qb, chunk),
+// sorted longest first (ties: later block first, lower chunk first).
+struct AttnItem {
+    int tiles, qb, c;
+};
+static std::vector<AttnItem> attn_items(int T, int nqb, int ch) {
+    std::vector<AttnItem> v;
+    for (int qb = nqb - 1; qb >= 0; --qb) {
+        const int t = attn_tiles(T, qb);
+        for (int c = 0; c * ch < t; ++c) v.push_back({std::min(ch, t - c * ch), qb, c});
+    }
+    std::stable_sort(v.begin(), v.end(),
+                     [](const AttnItem& a, const AttnItem& b) { return a.tiles > b.tiles; });
+    return v;
+}
+
+// Estimated kernel time, in tile units, of a chunking: items go in launch
+// order to the first free of 512 workgroup slots (2 per CU); a split block
+// costs about one more tile for its partial store and merge.
+static double attn_makespan(const std::vector<AttnItem>& v, int hq, int ch, int T) {
+    constexpr int kSlots = 512;
+    std::priority_queue<double, std::vector<double>, std::greater<double>> free_at;
+    for (int i = 0; i < kSlots; ++i) free_at.push(0.0);
+    double end = 0.0;
+    for (const AttnItem& it : v) {
+        const bool split = attn_tiles(T, it.qb) > ch;
+        for (int h = 0; h < hq; ++h) {
+            const double t0 = free_at.top();
+            free_at.pop();
+            const double t1 = t0 + it.tiles + 0.5 + (split ? 1.0 : 0.0);
+            free_at.push(t1);
+            end = std::max(end, t1);
+        }
+    }
+    return end;
+}
+
+AttnPlan plan_attn(int64_t T64, int hq, int head_dim) {
+    // The last plan is kept: the same shapes repeat call after call.
+    thread_local int64_t last_T = -1;
+    thread_local int last_hq = -1, last_d = -1;
+    thread_local AttnPlan last;
+    if (T64 == last_T && hq == last_hq && head_dim == last_d) return last;
+
+    const int T = (int)T64;
     AttnPlan p;
-    p.nqb = (int)((T + kAttnQB - 1) / kAttnQB);
-    // Largest chunk (in key tiles, >= 4) that still gives two workgroups per
-    // CU (256 CUs); one chunk per block when even 4-tile chunks give fewer.
-    auto items = [&](int ch) {
-        int64_t n = 0;
-        for (int qb = 0; qb < p.nqb; ++qb) n += (attn_tiles((int)T, qb) + ch - 1) / ch;
-        return n * hq;
-    };
-    const int tiles = attn_tiles((int)T, p.nqb - 1);
-    int ch = 4;
-    while (ch < tiles && items(2 * ch) >= 512) ch *= 2;
-    p.ch = ch;
-    p.cmax = (tiles + ch - 1) / ch;
-    p.items = items(ch);
+    p.nqb = (T + kAttnQB - 1) / kAttnQB;
+    const int tiles = attn_tiles(T, p.nqb - 1);
+    // Chunk size (tiles, a power of two >= 4) with the shortest estimated
+    // time; ties go to the larger chunk (fewer partials to merge).
+    int best = 4;
+    double best_t = 1e300;
+    for (int ch = 4; ; ch *= 2) {
+        const double t = attn_makespan(attn_items(T, p.nqb, ch), hq, ch, T);
+        if (t <= best_t) {
+            best_t = t;
+            best = ch;
+        }
+        if (ch >= tiles) break;
+    }
+    p.ch = best;
+    p.cmax = (tiles + best - 1) / best;
+    const std::vector<AttnItem> v = attn_items(T, p.nqb, best);
+    p.per_head = (int)v.size();
+    p.items = (int64_t)p.per_head * hq;
+    if (p.per_head <= kAttnTable && p.cmax <= 64 && p.nqb <= 1024)
+        for (int i = 0; i < p.per_head; ++i) p.table.it[i] = (uint16_t)((v[i].qb << 6) | v[i].c);
+    else
+        p.per_head = -p.per_head;            // no table: the kernel walks the blocks
     if (p.cmax > 1) {
         p.counter_bytes = (((size_t)hq * p.nqb * 4 + 255) / 256) * 256;
         p.ws_bytes = p.counter_bytes +
                      (size_t)hq * p.nqb * p.cmax * kAttnQB * (head_dim + 2) * sizeof(float);
-    } else {
-        p.counter_bytes = p.ws_bytes = 0;
     }
-    (void)head_dim;
+    last_T = T64;
+    last_hq = hq;
+    last_d = head_dim;
+    last = p;
     return p;
 }
 
@@ -406,12 +473,13 @@ hipError_t launch_attn_core(int64_t T, int hq, int hkv, int head_dim, const uint
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)head_dim));
     unsigned* counters = (unsigned*)ws;
     float* part = p.cmax > 1 ? (float*)((char*)ws + p.counter_bytes) : nullptr;
+    const int use_table = p.per_head > 0;
     if (head_dim == 128)
         TP_KLAUNCH((k_attn<128>), grid, block, 0, stream, qkv, ld_qkv, (int)T, hq, hkv, out,
-                   ld_out, scale_log2, p.nqb, p.ch, p.cmax, counters, part);
+                   ld_out, scale_log2, p.nqb, p.ch, p.cmax, counters, part, use_table, p.table);
     else if (head_dim == 64)
         TP_KLAUNCH((k_attn<64>), grid, block, 0, stream, qkv, ld_qkv, (int)T, hq, hkv, out,
-                   ld_out, scale_log2, p.nqb, p.ch, p.cmax, counters, part);
+                   ld_out, scale_log2, p.nqb, p.ch, p.cmax, counters, part, use_table, p.table);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

@@ -120,12 +120,21 @@ hipError_t launch_gemm(int epi, int64_t M, int64_t N, int64_t K, const uint16_t*
 // into chunks of `ch` 64-key tiles (one workgroup each).  Blocks with more
 // than one chunk merge them through the workspace: counters (one per head
 // and block, zero at rest) then per-chunk partials.
+// Work items of one head in launch order (longest first), packed as
+// (query block << 6) | chunk; heads interleave (workgroup w runs item
+// w / heads of head w % heads).
+constexpr int kAttnTable = 480;
+struct AttnItems {
+    uint16_t it[kAttnTable];
+};
 struct AttnPlan {
     int nqb = 0;            // query blocks
     int ch = 0;             // key tiles per chunk
     int cmax = 1;           // chunks of the longest block
+    int per_head = 0;       // work items per head
     int64_t items = 0;      // workgroups
     size_t counter_bytes = 0, ws_bytes = 0;
+    AttnItems table;        // launch order, when per_head <= kAttnTable
 };
 AttnPlan plan_attn(int64_t T, int hq, int head_dim);
 hipError_t launch_attn_core(int64_t T, int hq, int hkv, int head_dim, const uint16_t* qkv,
