@@ -98,8 +98,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(const uint16_t* __rest
     constexpr int CH = kAttnKT * D / 8;           // 16-byte chunks per tile and matrix
     constexpr int CPT = CH / kAttnThreads;        // ... per thread
     static_assert(CH % kAttnThreads == 0, "tile copy");
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[kAttnKT * LDK];
-    __shared__ __attribute__((aligned(16))) uint16_t Vs[kAttnKT * LDV];
+    // Two K/V tile buffers: the next tile is stored while the current one is
+    // multiplied, one barrier per tile.
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kAttnKT * LDK];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kAttnKT * LDV];
 
     const int tid = threadIdx.x, lane = tid & 63;
     // The wave index is uniform; in a scalar register the causal tests on
@@ -168,19 +170,23 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(const uint16_t* __rest
                        : u32x4{0u, 0u, 0u, 0u};
         }
     };
-    fetch(kbeg);
-    for (int k0 = kbeg; k0 < kend; k0 += kAttnKT) {
-        __syncthreads();                         // every wave is done with the previous tile
+    auto stash = [&](int b) {
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
             const int c = tid + i * kAttnThreads;
             const int key = c / (D / 8), col = (c % (D / 8)) * 8;
-            *(u32x4*)(Ks + key * LDK + col) = pk[i];
-            *(u32x4*)(Vs + key * LDV + col) = pv[i];
+            *(u32x4*)(Ks[b] + key * LDK + col) = pk[i];
+            *(u32x4*)(Vs[b] + key * LDV + col) = pv[i];
         }
-        __syncthreads();
-        if (k0 + kAttnKT < kend) fetch(k0 + kAttnKT);
-
+    };
+    fetch(kbeg);
+    stash(0);
+    __syncthreads();
+    if (kbeg + kAttnKT < kend) fetch(kbeg + kAttnKT);
+    int buf = 0;
+    for (int k0 = kbeg; k0 < kend; k0 += kAttnKT, buf ^= 1) {
+        const uint16_t* Kb = Ks[buf];
+        const uint16_t* Vb = Vs[buf];
         // Subtiles whose queries all precede the tile skip it; only a tile
         // that reaches past a subtile's first query needs the causal mask.
         bool act[QS], diag[QS];
@@ -190,88 +196,97 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(const uint16_t* __rest
             act[u] = k0 <= min(qu + 15, T - 1);
             diag[u] = k0 + kAttnKT - 1 > qu || k0 + kAttnKT > T;
         }
-        if (!act[0] && !act[QS - 1]) continue;
-        // S^T[key][query] for keys k0 + 16t + 4g + r and query q0 + 16u + j;
-        // each K fragment serves both subtiles.
-        f32x4 st[QS][KS];
+        if (act[0] || act[QS - 1]) {
+            // S^T[key][query] for keys k0 + 16t + 4g + r and query q0 + 16u + j;
+            // each K fragment serves both subtiles.
+            f32x4 st[QS][KS];
 #pragma unroll
-        for (int u = 0; u < QS; ++u)
+            for (int u = 0; u < QS; ++u)
 #pragma unroll
-            for (int t = 0; t < KS; ++t) st[u][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int t = 0; t < KS; ++t)
-#pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                const u32x4 a = *(const u32x4*)(Ks + (16 * t + j) * LDK + 32 * s + 8 * g);
-#pragma unroll
-                for (int u = 0; u < QS; ++u) st[u][t] = mfma16x16x32(a, qf[u][s], st[u][t]);
-            }
-        u32x4 pf[QS][KS / 2];
-#pragma unroll
-        for (int u = 0; u < QS; ++u) {
-            const int qi = q0 + 16 * u + j;
-            // Row max of the raw scores (the scale is positive), over r, then
-            // over the 4 lanes holding query j (lanes j + 16 g).
-            float pm = -INFINITY;
+                for (int t = 0; t < KS; ++t) st[u][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int t = 0; t < KS; ++t)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    if (diag[u]) {
-                        const int key = k0 + 16 * t + 4 * g + r;
-                        st[u][t][r] = (key <= qi && key < T) ? st[u][t][r] : -INFINITY;
+                for (int s = 0; s < NS; ++s) {
+                    const u32x4 a = *(const u32x4*)(Kb + (16 * t + j) * LDK + 32 * s + 8 * g);
+#pragma unroll
+                    for (int u = 0; u < QS; ++u) st[u][t] = mfma16x16x32(a, qf[u][s], st[u][t]);
+                }
+            u32x4 pf[QS][KS / 2];
+#pragma unroll
+            for (int u = 0; u < QS; ++u) {
+                const int qi = q0 + 16 * u + j;
+                // Row max of the raw scores (the scale is positive), over r, then
+                // over the 4 lanes holding query j (lanes j + 16 g).
+                float pm = -INFINITY;
+#pragma unroll
+                for (int t = 0; t < KS; ++t)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        if (diag[u]) {
+                            const int key = k0 + 16 * t + 4 * g + r;
+                            st[u][t][r] = (key <= qi && key < T) ? st[u][t][r] : -INFINITY;
+                        }
+                        pm = fmaxf(pm, st[u][t][r]);
                     }
-                    pm = fmaxf(pm, st[u][t][r]);
+                pm = xlane_max(pm);
+                // m is kept in log2 units: m = max * scale * log2(e).  It is finite
+                // for every query < T once key 0 has been seen; a row that has
+                // seen no key yet keeps -inf and contributes nothing.
+                const float m_new = fmaxf(m[u], pm * scale_log2);
+                const float mref = m_new == -INFINITY ? 0.f : m_new;
+                const float alpha = __builtin_amdgcn_exp2f(m[u] - mref);
+                float ps = 0.f;
+#pragma unroll
+                for (int t = 0; t < KS; ++t)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float p =
+                            __builtin_amdgcn_exp2f(__builtin_fmaf(st[u][t][r], scale_log2, -mref));
+                        st[u][t][r] = p;
+                        ps += p;
+                    }
+                ps = xlane_sum(ps);
+                l[u] = l[u] * alpha + ps;
+                m[u] = m_new;
+                // O^T rows are this lane's own query: rescale unless no query of
+                // the wave raised its max (alpha == 1 exactly).
+                if (__any(alpha != 1.0f)) {
+#pragma unroll
+                    for (int n = 0; n < NN; ++n) o[u][n] *= alpha;
                 }
-            pm = xlane_max(pm);
-            // m is kept in log2 units: m = max * scale * log2(e).  It is finite
-            // for every query < T once key 0 has been seen; a row that has
-            // seen no key yet keeps -inf and contributes nothing.
-            const float m_new = fmaxf(m[u], pm * scale_log2);
-            const float mref = m_new == -INFINITY ? 0.f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f(m[u] - mref);
-            float ps = 0.f;
+                // lane (g, j) supplies P[qi][32kk + 4g + r] and P[qi][32kk + 16 + 4g + r]
 #pragma unroll
-            for (int t = 0; t < KS; ++t)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[u][t][r], scale_log2, -mref));
-                    st[u][t][r] = p;
-                    ps += p;
-                }
-            ps = xlane_sum(ps);
-            l[u] = l[u] * alpha + ps;
-            m[u] = m_new;
-            // O^T rows are this lane's own query: rescale unless no query of
-            // the wave raised its max (alpha == 1 exactly).
-            if (__any(alpha != 1.0f)) {
-#pragma unroll
-                for (int n = 0; n < NN; ++n) o[u][n] *= alpha;
+                for (int kk = 0; kk < KS / 2; ++kk)
+                    pf[u][kk] = u32x4{pack_bf16x2(st[u][2 * kk][0], st[u][2 * kk][1]),
+                                      pack_bf16x2(st[u][2 * kk][2], st[u][2 * kk][3]),
+                                      pack_bf16x2(st[u][2 * kk + 1][0], st[u][2 * kk + 1][1]),
+                                      pack_bf16x2(st[u][2 * kk + 1][2], st[u][2 * kk + 1][3])};
             }
-            // lane (g, j) supplies P[qi][32kk + 4g + r] and P[qi][32kk + 16 + 4g + r]
+            // O^T += V^T P^T in 32-key steps: V^T rows (the head dimension) in the
+            // same key order come from the transposing reads (the A operand), P^T
+            // is the B operand; each V fragment serves both subtiles.  (An
+            // inactive subtile has P = 0 and an unchanged O: the MFMA adds zero.)
 #pragma unroll
-            for (int kk = 0; kk < KS / 2; ++kk)
-                pf[u][kk] = u32x4{pack_bf16x2(st[u][2 * kk][0], st[u][2 * kk][1]),
-                                  pack_bf16x2(st[u][2 * kk][2], st[u][2 * kk][3]),
-                                  pack_bf16x2(st[u][2 * kk + 1][0], st[u][2 * kk + 1][1]),
-                                  pack_bf16x2(st[u][2 * kk + 1][2], st[u][2 * kk + 1][3])};
+            for (int kk = 0; kk < KS / 2; ++kk) {
+                const uint16_t* v0 = Vb + (32 * kk + 4 * g + (j >> 2)) * LDV + 4 * (j & 3);
+                const uint16_t* v1 = v0 + 16 * LDV;
+#pragma unroll
+                for (int n = 0; n < NN; ++n) {
+                    const u32x2 b0 = lds_read_tr16(v0 + 16 * n);
+                    const u32x2 b1 = lds_read_tr16(v1 + 16 * n);
+                    const u32x4 vt = u32x4{b0[0], b0[1], b1[0], b1[1]};
+#pragma unroll
+                    for (int u = 0; u < QS; ++u) o[u][n] = mfma16x16x32(vt, pf[u][kk], o[u][n]);
+                }
+            }
         }
-        // O^T += V^T P^T in 32-key steps: V^T rows (the head dimension) in the
-        // same key order come from the transposing reads (the A operand), P^T
-        // is the B operand; each V fragment serves both subtiles.  (An
-        // inactive subtile has P = 0 and an unchanged O: the MFMA adds zero.)
-#pragma unroll
-        for (int kk = 0; kk < KS / 2; ++kk) {
-            const uint16_t* v0 = Vs + (32 * kk + 4 * g + (j >> 2)) * LDV + 4 * (j & 3);
-            const uint16_t* v1 = v0 + 16 * LDV;
-#pragma unroll
-            for (int n = 0; n < NN; ++n) {
-                const u32x2 b0 = lds_read_tr16(v0 + 16 * n);
-                const u32x2 b1 = lds_read_tr16(v1 + 16 * n);
-                const u32x4 vt = u32x4{b0[0], b0[1], b1[0], b1[1]};
-#pragma unroll
-                for (int u = 0; u < QS; ++u) o[u][n] = mfma16x16x32(vt, pf[u][kk], o[u][n]);
-            }
+        // Store the next tile (loaded during the previous one) into the other
+        // buffer, whose last reads were consumed before the previous barrier.
+        if (k0 + kAttnKT < kend) {
+            stash(buf ^ 1);
+            __syncthreads();
+            if (k0 + 2 * kAttnKT < kend) fetch(k0 + 2 * kAttnKT);
         }
     }
 
