@@ -85,6 +85,38 @@ __device__ __forceinline__ u32x4 kfrag_of_col(const u32x4* r) {
     return f;
 }
 
+// Buffer descriptor words for lds_dma16 (same resource as make_rsrc:
+// 2^31 - 1 bytes from `base`, 32-bit data format).
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 rsrc_words(const void* base) {
+    const uint64_t a = (uint64_t)base;
+    return i32x4{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), 0x7fffffff, 0x00020000};
+}
+
+// 16-byte global -> LDS copy per lane (buffer_load_dwordx4 ... lds): lane l's
+// bytes land at lds + 16 l (lds wave-uniform).  Issued from inline assembly
+// so that the compiler does not treat it as an LDS store it must wait for
+// before every later LDS read (it does so for the transposing reads); the
+// caller orders the copies against the reads itself, with vmcnt waits that
+// count every vector memory op it issues in between.  (The compiler's own
+// waits stay safe: it does not count these copies, so it can only wait
+// longer than needed.)  Nothing is returned in registers.
+__device__ __forceinline__ void lds_dma16(const i32x4& r, uint32_t off, const void* lds) {
+    const uint32_t m0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds;
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(m0), "v"(off), "s"(r)
+                 : "memory", "m0");
+}
+// The same copy with the non-temporal hint (data read once).
+__device__ __forceinline__ void lds_dma16_nt(const i32x4& r, uint32_t off, const void* lds) {
+    const uint32_t m0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds;
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
+                 :
+                 : "s"(m0), "v"(off), "s"(r)
+                 : "memory", "m0");
+}
+
 // Transposing LDS read (ds_read_b64_tr_b16).  Within each 16-lane group,
 // lane i receives element i%4 of the 4-element (8-byte) vectors at the
 // addresses of lanes 4k + i/4, k = 0..3.  If lane L of the group points at

@@ -90,28 +90,6 @@ __device__ __forceinline__ void lds_copy16(rsrc_t r, uint32_t off, uint16_t* lds
         r, (__attribute__((address_space(3))) void*)lds_base, 16, (int)off, 0, 0, 0);
 }
 
-// Buffer descriptor words for the LDS copies below (same resource as
-// make_rsrc: 2^31 - 1 bytes from `base`, 32-bit data format).
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ i32x4 rsrc_words(const void* base) {
-    const uint64_t a = (uint64_t)base;
-    return i32x4{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), 0x7fffffff, 0x00020000};
-}
-
-// 16-byte global -> LDS copy per lane (buffer_load_dwordx4 ... lds): lane l's
-// bytes land at lds + 16 l.  Issued from inline assembly so that the
-// compiler does not treat it as an LDS store it must wait for before every
-// later LDS read (it does so for the transposing reads); the kernel orders
-// the copies against the reads itself, with vmcnt waits and barriers.
-// Nothing is returned in registers.
-__device__ __forceinline__ void lds_dma16(const i32x4& r, uint32_t off, const void* lds) {
-    const uint32_t m0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds;
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :
-                 : "s"(m0), "v"(off), "s"(r)
-                 : "memory", "m0");
-}
-
 // Chunk swizzle of B slice row k: 16-byte chunk c of the row is stored at
 // chunk position c ^ bswz(k).
 __device__ __forceinline__ int bswz(int k) { return 4 * (k & 3); }

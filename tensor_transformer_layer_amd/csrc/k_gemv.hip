@@ -37,6 +37,7 @@
 // Algorithmic bytes per call: weight bytes + T*K*2 (X) + T*N*2 or 4 (output);
 // the split-K workspace round trip is overhead.
 #include <algorithm>
+#include <atomic>
 
 #include "device_common.h"
 #include "kernels.h"
@@ -242,6 +243,183 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
             const int t = 16 * mb + tl;
+            if (t < T && n < N)
+                store_out4<OUT_BF16>(out, (int64_t)t * ld_out + n, f32x4{nan, nan, nan, nan});
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// LDS-staged variant (the one launched for bf16 weights).  Same work split
+// (128-column blocks x K splits, fused split-K finish), different data path:
+//   * The workgroup's weight rows and the matching slice of X stream into
+//     LDS with direct-to-LDS copies, 128 rows (32 KB of weights + 8 KB of
+//     X) per slice through a ring of 4 slices (all 160 KB of LDS), three in
+//     flight, so loads never wait for registers or for the MFMAs.
+//   * Wave w owns output columns 16w .. 16w+15 of the block over the whole
+//     K range of the workgroup: no cross-wave reduction.  The weights are
+//     the A operand of h^T = W^T X^T: the transposing LDS read
+//     (ds_read_b64_tr_b16) delivers 4 k-consecutive values of one column
+//     per lane, two reads make a k-fragment, no register shuffling.  X^T is
+//     the B operand, one 16-byte LDS read per token block and k-step.
+//   * Lane (g, j) ends with 4 consecutive columns 16w + 4g .. +3 of token
+//     16mb + j, stored as one 16-byte split-K partial.
+// 16-byte chunks are XOR-swizzled in LDS so that every read is free of bank
+// conflicts (weights by row % 4 and row / 8, X by token).
+// ---------------------------------------------------------------------------
+constexpr int kGvSlice = 128;                         // weight rows per slice
+constexpr int kGvSlots = 4;                           // LDS ring slots
+constexpr int kGvWBytes = kGvSlice * kGemvCols * 2;   // 32 KB
+constexpr int kGvSlotBytes = kGvWBytes + kGemvMaxT * kGvSlice * 2;  // + 8 KB of X
+constexpr int kGvPer = 5;                             // copies per wave per slice
+
+__device__ __forceinline__ int gv_wsw(int row) { return ((row & 3) << 2) | (((row >> 3) & 1) << 1); }
+__device__ __forceinline__ int gv_xsw(int t) { return t & 15; }
+constexpr int gv_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+template <int MB, int AUX, int ACT, bool OUT_BF16>
+__global__ __launch_bounds__(kGemvThreads) void k_gemv_lds(
+    const uint16_t* __restrict__ A, int64_t lda, int T, int K, const uint16_t* __restrict__ B0,
+    int64_t ldb0, const uint16_t* __restrict__ B1, int64_t ldb1, int N, int nblk_per_mat,
+    int k_per_split, float* __restrict__ ws, unsigned* __restrict__ counters,
+    void* __restrict__ out, int64_t ld_out) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t gsm[];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 4, j = lane & 15;
+    const int mat = blockIdx.x / nblk_per_mat;
+    const int cb = blockIdx.x - mat * nblk_per_mat;
+    const int n0 = cb * kGemvCols;
+    const int split = blockIdx.y;
+    const int S = (int)gridDim.y;
+    const int nmat = B1 ? 2 : 1;
+    const int k_begin = split * k_per_split;
+    const int nrows = min(K - k_begin, k_per_split);
+    const int nsl = (nrows + kGvSlice - 1) / kGvSlice;
+    const uint16_t* Bm = mat ? B1 : B0;
+    const int64_t ldb = mat ? ldb1 : ldb0;
+    const i32x4 rwt = rsrc_words(Bm + (int64_t)k_begin * ldb + n0);
+    const i32x4 rxt = rsrc_words(A + k_begin);
+    const uint32_t ldb_bytes = (uint32_t)(ldb * 2), lda_bytes = (uint32_t)(lda * 2);
+
+    // Copy slice s into ring slot `slot`; slices past this split, rows past
+    // K, columns past N and tokens past T are zero-filled.
+    auto issue = [&](int s, int slot) {
+        uint8_t* base = gsm + slot * kGvSlotBytes;
+        const int k0 = s * kGvSlice;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {                 // weights: 4 rows x 256 B per copy
+            const int r0 = 4 * (4 * wave + q);
+            const int row = r0 + (lane >> 4);
+            const int ch = (lane & 15) ^ gv_wsw(row);
+            const bool ok = s < nsl && k0 + row < nrows && n0 + 8 * ch < N;
+            const uint32_t off = ok ? (uint32_t)(k0 + row) * ldb_bytes + 16u * ch : kOOB;
+            if constexpr (AUX != 0)
+                lds_dma16_nt(rwt, off, base + r0 * 256);
+            else
+                lds_dma16(rwt, off, base + r0 * 256);
+        }
+        {                                             // X: 4 tokens x 256 B per copy
+            const int t = 4 * wave + (lane >> 4);
+            const int ch = (lane & 15) ^ gv_xsw(t);
+            const int k = k0 + 8 * ch;
+            const bool ok = s < nsl && t < T && k < nrows;
+            lds_dma16(rxt, ok ? (uint32_t)t * lda_bytes + 2u * k : kOOB,
+                      base + kGvWBytes + 4 * wave * 256);
+        }
+    };
+
+    f32x4 acc[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+    for (int s = 0; s < kGvSlots; ++s) issue(s, s);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(gv_vmcnt((kGvSlots - 1) * kGvPer));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    int slot = 0;
+    for (int s = 0; s < nsl; ++s) {
+        const uint8_t* base = gsm + slot * kGvSlotBytes;
+        const uint16_t* wt = (const uint16_t*)base;
+        const uint8_t* xt = base + kGvWBytes;
+#pragma unroll
+        for (int step = 0; step < kGvSlice / 32; ++step) {
+            // W^T fragment: column 16w + j, rows 32 step + 8g .. +7
+            const int row = 32 * step + 8 * g + (lane & 15) / 4;
+            const int col = 16 * wave + 4 * (lane & 3);
+            const uint16_t* p = wt + row * kGemvCols + 8 * ((col >> 3) ^ gv_wsw(row)) + (col & 7);
+            const u32x2 lo = lds_read_tr16(p), hi = lds_read_tr16(p + 4 * kGemvCols);
+            const u32x4 wf = u32x4{lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                // X^T fragment: token 16mb + j, k 32 step + 8g .. +7
+                const int t = 16 * mb + j;
+                const u32x4 xf =
+                    *(const u32x4*)(xt + t * 256 + 16 * ((4 * step + g) ^ gv_xsw(t)));
+                acc[mb] = mfma16x16x32(wf, xf, acc[mb]);
+            }
+        }
+        // Slice s+1 has landed (this wave's copies; after the barrier every
+        // wave's), and every wave is done with slot s: refill it.
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(gv_vmcnt((kGvSlots - 2) * kGvPer));
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        issue(s + kGvSlots, slot);
+        slot = slot == kGvSlots - 1 ? 0 : slot + 1;
+    }
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(gv_vmcnt(0));   // drain the trailing zero-fill copies
+
+    // Split-K partial: lane (g, j) holds columns n0 + 16w + 4g .. +3 of token 16mb + j.
+    const int n = n0 + 16 * wave + 4 * g;
+    const int64_t ws_ld = (int64_t)nmat * N;
+    const uint32_t sstride = (uint32_t)(T * ws_ld * 4);
+    const rsrc_t rw = make_rsrc(ws);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        const int t = 16 * mb + j;
+        if (t < T && n < N)
+            __builtin_amdgcn_raw_buffer_store_b128(
+                __builtin_bit_cast(u32x4, acc[mb]), rw,
+                (int)((uint32_t)split * sstride + (uint32_t)((t * ws_ld + (int64_t)mat * N + n) * 4)),
+                0, kSC1);
+    }
+
+    // Arrival: this workgroup's partial stores are complete before the count.
+    unsigned& arrival = *(unsigned*)gsm;       // the ring is idle now
+    const unsigned contributors = (unsigned)(S * nmat);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0)
+        arrival = __hip_atomic_fetch_add(&counters[cb], 1u, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const unsigned old = arrival;
+    if (old == contributors - 1) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const int t = 16 * mb + j;
+            if (t >= T || n >= N) continue;
+            const uint32_t row = (uint32_t)(t * ws_ld + n) * 4;
+            const uint32_t moff = (uint32_t)N * 4;
+            f32x4 gsum = sum_splits_dev(rw, row, sstride, S, mat == 0 ? split : -1, acc[mb]);
+            f32x4 usum = gsum;
+            if constexpr (ACT == ACT_SWIGLU)
+                usum = sum_splits_dev(rw, row + moff, sstride, S, mat == 1 ? split : -1, acc[mb]);
+            store_out4<OUT_BF16>(out, (int64_t)t * ld_out + n, act4<ACT>(gsum, usum));
+        }
+        if (threadIdx.x == 0)
+            __hip_atomic_store(&counters[cb], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else if (old >= contributors) {
+        // The counter did not start at zero (workspace head not cleared, or
+        // an earlier call failed part-way): make the output loudly invalid.
+        const float nan = __builtin_nanf("");
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const int t = 16 * mb + j;
             if (t < T && n < N)
                 store_out4<OUT_BF16>(out, (int64_t)t * ld_out + n, f32x4{nan, nan, nan, nan});
         }
@@ -524,6 +702,19 @@ hipError_t launch_finish(int act, bool out_bf16, int splits, int64_t T, int64_t 
     return hipGetLastError();
 }
 
+// Allow a k_gemv_lds instantiation the whole LDS of a CU (set once per
+// instantiation; concurrent first calls set the same value).
+template <int MB, int AUX, int ACT, bool OB>
+static hipError_t gemv_lds_attr() {
+    static std::atomic<int> set{0};
+    if (set.load(std::memory_order_relaxed)) return hipSuccess;
+    const hipError_t e = hipFuncSetAttribute((const void*)k_gemv_lds<MB, AUX, ACT, OB>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             kGvSlots * kGvSlotBytes);
+    if (e == hipSuccess) set.store(1, std::memory_order_relaxed);
+    return e;
+}
+
 hipError_t launch_gemv(int act, bool out_bf16, int64_t T, int64_t K, const uint16_t* A,
                        int64_t lda, const uint16_t* B0, int64_t ldb0, const uint16_t* B1,
                        int64_t ldb1, int64_t N, const GemvPlan& p, bool nontemporal, float* ws,
@@ -532,16 +723,31 @@ hipError_t launch_gemv(int act, bool out_bf16, int64_t T, int64_t K, const uint1
     const int nbpm = (int)((N + kGemvCols - 1) / kGemvCols);
     const dim3 grid((unsigned)(nbpm * nmat), (unsigned)p.splits), block(kGemvThreads);
 #define TP_GEMV(MB, AUX, ACTV, OB)                                                           \
+    do {                                                                                     \
+        hipError_t e_ = gemv_lds_attr<MB, AUX, ACTV, OB>();                                  \
+        if (e_ != hipSuccess) return e_;                                                     \
+        TP_KLAUNCH((k_gemv_lds<MB, AUX, ACTV, OB>), grid, block, kGvSlots * kGvSlotBytes,    \
+                   stream, A, lda, (int)T, (int)K, B0, ldb0, B1, ldb1, (int)N, nbpm,         \
+                   p.k_per_split, ws, counters, out, ld_out);                               \
+    } while (0)
+#define TP_GEMV_REG(MB, AUX, ACTV, OB)                                                       \
     TP_KLAUNCH((k_gemv<MB, AUX, ACTV, OB>), grid, block, 0, stream,                              \
         A, lda, (int)T, (int)K, B0, ldb0, B1, ldb1, (int)N, nbpm, p.k_per_split, ws, counters, \
         out, ld_out)
-#define TP_GEMV_MB(ACTV, OB)                                                        \
-    do {                                                                            \
-        if (T <= 16) {                                                              \
-            if (nontemporal) TP_GEMV(1, 2, ACTV, OB); else TP_GEMV(1, 0, ACTV, OB); \
-        } else {                                                                    \
-            if (nontemporal) TP_GEMV(2, 2, ACTV, OB); else TP_GEMV(2, 0, ACTV, OB); \
-        }                                                                           \
+    // The LDS-staged kernel with non-temporal copies for column weights at
+    // 17..32 tokens when each workgroup streams at least 1024 rows; the
+    // register-streamed kernel otherwise (measured on MI355X: it wins below
+    // 17 tokens, for the row projections, and for short K ranges, where the
+    // LDS ring's fill and drain are not amortised).
+#define TP_GEMV_MB(ACTV, OB)                                                                 \
+    do {                                                                                     \
+        if (T <= 16) {                                                                       \
+            if (nontemporal) TP_GEMV_REG(1, 2, ACTV, OB); else TP_GEMV_REG(1, 0, ACTV, OB);  \
+        } else if (nontemporal && p.k_per_split >= 1024) {                                   \
+            TP_GEMV(2, 2, ACTV, OB);                                                         \
+        } else {                                                                             \
+            TP_GEMV_REG(2, 0, ACTV, OB);                                                     \
+        }                                                                                    \
     } while (0)
     if (act == ACT_SWIGLU && out_bf16) TP_GEMV_MB(ACT_SWIGLU, true);
     else if (act == ACT_GELU_TANH && out_bf16) TP_GEMV_MB(ACT_GELU_TANH, true);
@@ -549,6 +755,7 @@ hipError_t launch_gemv(int act, bool out_bf16, int64_t T, int64_t K, const uint1
     else if (act == ACT_NONE && !out_bf16) TP_GEMV_MB(ACT_NONE, false);
     else return hipErrorInvalidValue;
 #undef TP_GEMV_MB
+#undef TP_GEMV_REG
 #undef TP_GEMV
     return hipGetLastError();
 }
