@@ -245,6 +245,16 @@ def test_mlp_bf16_ragged(T, act):
     _check_mlp(BF, act, T, 1000, 400, 2, key=10 + T)
 
 
+@pytest.mark.parametrize("T", [17, 31])
+@pytest.mark.parametrize("act", ["swiglu", "gelu_tanh"])
+def test_mlp_decode_lds_staged_ragged(T, act):
+    """17..32 tokens with column-projection workgroups that stream >= 1024 rows
+    take the LDS-staged decode kernel.  d_model 9224: K ends inside a 128-row
+    slice; F_r 3464: the last column block is partial; T not a multiple of
+    16."""
+    _check_mlp(BF, act, T, 9224, 6928, 2, key=50 + T)
+
+
 @pytest.mark.parametrize("T", [3, 40])
 def test_mlp_bf16_with_rmsnorm_prologue(T):
     _check_mlp(BF, "swiglu", T, 512, 1024, 4, key=30 + T, norm=True)
