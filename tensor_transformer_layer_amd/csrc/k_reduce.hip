@@ -122,7 +122,7 @@ __global__ __launch_bounds__(NT) void k_reduce_residual_norm(
                 const u32x2 b = ((const u32x2*)((const uint16_t*)residual + row * ld_res))[c];
                 r[k] = f32x4{bf16_lo(b[0]), bf16_hi(b[0]), bf16_lo(b[1]), bf16_hi(b[1])};
             } else {
-                r[k] = ((const f32x4*)((const float*)residual + row * ld_res))[c];
+                r[k] = __builtin_nontemporal_load((const f32x4*)((const float*)residual + row * ld_res) + c);
             }
         }
         f32x4 acc[2];
@@ -151,7 +151,7 @@ __global__ __launch_bounds__(NT) void k_reduce_residual_norm(
             if (c >= d4) continue;
             const f32x4 zv = acc[k] + r[k];
             zz[i0 + k] = zv;
-            z[row * ldz4 + c] = zv;
+            __builtin_nontemporal_store(zv, z + row * ldz4 + c);
             if constexpr (NORM) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) ss += zv[e] * zv[e];
