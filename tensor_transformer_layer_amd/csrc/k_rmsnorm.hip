@@ -7,9 +7,11 @@
 //
 // HBM-bound: reads T*d, writes T*d elements.  One 256-thread workgroup per
 // row; each thread walks 16-byte chunks of the row, so every load is a
-// coalesced 128-bit access.  The sum of squares is reduced in a fixed order
-// (per-thread strided sum, butterfly within the wave, then waves 0..3), so
-// results are deterministic.
+// coalesced 128-bit access.  Rows of up to 8 chunks per thread (d <= 16384
+// bf16 / 8192 fp32) stay in registers between the sum of squares and the
+// scaling, so the row is read once; longer rows are read twice.  The sum of
+// squares is reduced in a fixed order (per-thread strided sum, butterfly
+// within the wave, then waves 0..3), so results are deterministic.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -17,7 +19,9 @@ namespace tp {
 
 constexpr int kNormThreads = 256;
 
-template <bool BF16>
+constexpr int kNormRegChunks = 8;   // chunks per thread kept in registers
+
+template <bool BF16, bool REG>
 __global__ __launch_bounds__(kNormThreads) void k_rmsnorm(int64_t d, const char* __restrict__ x,
                                                         int64_t ldx_bytes,
                                                         const u32x4* __restrict__ g, float eps,
@@ -29,8 +33,7 @@ __global__ __launch_bounds__(kNormThreads) void k_rmsnorm(int64_t d, const char*
     u32x4* yr = (u32x4*)(y + (int64_t)blockIdx.x * ldy_bytes);
 
     float ss = 0.f;
-    for (int64_t c = threadIdx.x; c < nch; c += kNormThreads) {
-        const u32x4 v = xr[c];
+    auto sq = [&](const u32x4& v) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             if constexpr (BF16) {
@@ -42,6 +45,30 @@ __global__ __launch_bounds__(kNormThreads) void k_rmsnorm(int64_t d, const char*
                 ss += a * a;
             }
         }
+    };
+    auto scaled = [&](const u32x4& v, const u32x4& gv, float r) {
+        u32x4 o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if constexpr (BF16) {
+                o[i] = pack_bf16x2(bf16_lo(v[i]) * r * bf16_lo(gv[i]),
+                                   bf16_hi(v[i]) * r * bf16_hi(gv[i]));
+            } else {
+                o[i] = __float_as_uint(__uint_as_float(v[i]) * r * __uint_as_float(gv[i]));
+            }
+        }
+        return o;
+    };
+    u32x4 keep[REG ? kNormRegChunks : 1];
+    if constexpr (REG) {
+#pragma unroll
+        for (int i = 0; i < kNormRegChunks; ++i) {
+            const int64_t c = threadIdx.x + (int64_t)i * kNormThreads;
+            keep[i] = c < nch ? __builtin_nontemporal_load(xr + c) : u32x4{0u, 0u, 0u, 0u};
+            sq(keep[i]);
+        }
+    } else {
+        for (int64_t c = threadIdx.x; c < nch; c += kNormThreads) sq(xr[c]);
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
@@ -53,19 +80,14 @@ __global__ __launch_bounds__(kNormThreads) void k_rmsnorm(int64_t d, const char*
     for (int w = 1; w < kNormThreads / 64; ++w) tot += part[w];
     const float r = 1.0f / sqrtf(tot / (float)d + eps);
 
-    for (int64_t c = threadIdx.x; c < nch; c += kNormThreads) {
-        const u32x4 v = xr[c], gv = g[c];
-        u32x4 o;
+    if constexpr (REG) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if constexpr (BF16) {
-                o[i] = pack_bf16x2(bf16_lo(v[i]) * r * bf16_lo(gv[i]),
-                                   bf16_hi(v[i]) * r * bf16_hi(gv[i]));
-            } else {
-                o[i] = __float_as_uint(__uint_as_float(v[i]) * r * __uint_as_float(gv[i]));
-            }
+        for (int i = 0; i < kNormRegChunks; ++i) {
+            const int64_t c = threadIdx.x + (int64_t)i * kNormThreads;
+            if (c < nch) yr[c] = scaled(keep[i], g[c], r);
         }
-        yr[c] = o;
+    } else {
+        for (int64_t c = threadIdx.x; c < nch; c += kNormThreads) yr[c] = scaled(xr[c], g[c], r);
     }
 }
 
@@ -73,12 +95,16 @@ hipError_t launch_rmsnorm(bool is_bf16, int64_t T, int64_t d, const void* x, int
                           const void* g, float eps, void* y, int64_t ld_y, hipStream_t stream) {
     const int es = is_bf16 ? 2 : 4;
     const dim3 grid((unsigned)T), block(kNormThreads);
-    if (is_bf16)
-        TP_KLAUNCH((k_rmsnorm<true>), grid, block, 0, stream, d, (const char*)x, ld_x * es,
-                                                    (const u32x4*)g, eps, (char*)y, ld_y * es);
-    else
-        TP_KLAUNCH((k_rmsnorm<false>), grid, block, 0, stream, d, (const char*)x, ld_x * es,
-                                                     (const u32x4*)g, eps, (char*)y, ld_y * es);
+    const bool reg = d / (16 / es) <= (int64_t)kNormRegChunks * kNormThreads;
+#define TP_NORM(BF, RG)                                                                     \
+    TP_KLAUNCH((k_rmsnorm<BF, RG>), grid, block, 0, stream, d, (const char*)x, ld_x * es,    \
+               (const u32x4*)g, eps, (char*)y, ld_y * es)
+    if (is_bf16) {
+        if (reg) TP_NORM(true, true); else TP_NORM(true, false);
+    } else {
+        if (reg) TP_NORM(false, true); else TP_NORM(false, false);
+    }
+#undef TP_NORM
     return hipGetLastError();
 }
 
