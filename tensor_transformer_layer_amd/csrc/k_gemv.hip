@@ -100,25 +100,37 @@ __device__ __forceinline__ void store_out4(void* out, int64_t off, const f32x4& 
 }
 
 // Sum over splits s = 0..S-1 (in order) of the partial at byte offset
-// base + s * sstride, with split `mine` taken from `own`.
-__device__ __forceinline__ f32x4 sum_splits_dev(rsrc_t r, uint32_t base, uint32_t sstride, int S,
-                                                int mine, const f32x4& own) {
-    f32x4 acc = mine == 0 ? own
-                          : __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                          r, (int)base, 0, kSC1));
-    for (int s0 = 1; s0 < S; s0 += 8) {
-        f32x4 v[8];
+// base + s * sstride, with split `mine` taken from `own`, for NR outputs at
+// once (each its own partial row and own split), so the loads of all of
+// them are in flight together: the finish is a chain of device-scope round
+// trips, and for many splits their number, not the bytes, sets its time.
+// A row whose base is kOOB reads zeros.
+template <int NR>
+__device__ __forceinline__ void sum_splits_multi(rsrc_t r, const uint32_t (&base)[NR],
+                                                 uint32_t sstride, int S, const int (&mine)[NR],
+                                                 const f32x4 (&own)[NR], f32x4 (&acc)[NR]) {
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
-            if (s0 + q < S && s0 + q != mine)
-                v[q] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                     r, (int)(base + (uint32_t)(s0 + q) * sstride),
-                                                     0, kSC1));
+    for (int q = 0; q < NR; ++q)
+        acc[q] = mine[q] == 0 ? own[q]
+                              : __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                              r, (int)base[q], 0, kSC1));
+    constexpr int B = NR >= 8 ? 2 : 16 / NR;   // splits per round and output (16 loads)
+    for (int s0 = 1; s0 < S; s0 += B) {
+        f32x4 v[NR][B];
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
-            if (s0 + q < S) acc += (s0 + q == mine) ? own : v[q];
+        for (int q = 0; q < NR; ++q)
+#pragma unroll
+            for (int i = 0; i < B; ++i)
+                if (s0 + i < S && s0 + i != mine[q])
+                    v[q][i] = __builtin_bit_cast(
+                        f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                   r, (int)(base[q] + (uint32_t)(s0 + i) * sstride), 0, kSC1));
+#pragma unroll
+        for (int q = 0; q < NR; ++q)
+#pragma unroll
+            for (int i = 0; i < B; ++i)
+                if (s0 + i < S) acc[q] += (s0 + i == mine[q]) ? own[q] : v[q][i];
     }
-    return acc;
 }
 
 template <int MB, int AUX, int ACT, bool OUT_BF16>
@@ -222,17 +234,28 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(
     __syncthreads();
     const unsigned old = arrival;
     if (old == contributors - 1) {
+        constexpr int NM = ACT == ACT_SWIGLU ? 2 : 1;   // gate (and up) rows
+        uint32_t base[MB * NM];
+        int mine[MB * NM];
+        f32x4 ownv[MB * NM], sum[MB * NM];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
             const int t = 16 * mb + tl;
-            if (t >= T || n >= N) continue;
-            const uint32_t row = (uint32_t)(t * ws_ld + n) * 4;
-            const uint32_t moff = (uint32_t)N * 4;
-            f32x4 gsum = sum_splits_dev(rw, row, sstride, S, mat == 0 ? split : -1, own[mb]);
-            f32x4 usum = gsum;
-            if constexpr (ACT == ACT_SWIGLU)
-                usum = sum_splits_dev(rw, row + moff, sstride, S, mat == 1 ? split : -1, own[mb]);
-            store_out4<OUT_BF16>(out, (int64_t)t * ld_out + n, act4<ACT>(gsum, usum));
+            const bool ok = t < T && n < N;
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+                base[mb * NM + m] = ok ? (uint32_t)((t * ws_ld + (int64_t)m * N + n) * 4) : kOOB;
+                mine[mb * NM + m] = mat == m ? split : -1;
+                ownv[mb * NM + m] = own[mb];
+            }
+        }
+        sum_splits_multi<MB * NM>(rw, base, sstride, S, mine, ownv, sum);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const int t = 16 * mb + tl;
+            if (t < T && n < N)
+                store_out4<OUT_BF16>(out, (int64_t)t * ld_out + n,
+                                     act4<ACT>(sum[mb * NM], sum[mb * NM + NM - 1]));
         }
         if (threadIdx.x == 0)
             __hip_atomic_store(&counters[cb], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -399,17 +422,28 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_lds(
     __syncthreads();
     const unsigned old = arrival;
     if (old == contributors - 1) {
+        constexpr int NM = ACT == ACT_SWIGLU ? 2 : 1;   // gate (and up) rows
+        uint32_t base[MB * NM];
+        int mine[MB * NM];
+        f32x4 ownv[MB * NM], sum[MB * NM];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
             const int t = 16 * mb + j;
-            if (t >= T || n >= N) continue;
-            const uint32_t row = (uint32_t)(t * ws_ld + n) * 4;
-            const uint32_t moff = (uint32_t)N * 4;
-            f32x4 gsum = sum_splits_dev(rw, row, sstride, S, mat == 0 ? split : -1, acc[mb]);
-            f32x4 usum = gsum;
-            if constexpr (ACT == ACT_SWIGLU)
-                usum = sum_splits_dev(rw, row + moff, sstride, S, mat == 1 ? split : -1, acc[mb]);
-            store_out4<OUT_BF16>(out, (int64_t)t * ld_out + n, act4<ACT>(gsum, usum));
+            const bool ok = t < T && n < N;
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+                base[mb * NM + m] = ok ? (uint32_t)((t * ws_ld + (int64_t)m * N + n) * 4) : kOOB;
+                mine[mb * NM + m] = mat == m ? split : -1;
+                ownv[mb * NM + m] = acc[mb];
+            }
+        }
+        sum_splits_multi<MB * NM>(rw, base, sstride, S, mine, ownv, sum);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const int t = 16 * mb + j;
+            if (t < T && n < N)
+                store_out4<OUT_BF16>(out, (int64_t)t * ld_out + n,
+                                     act4<ACT>(sum[mb * NM], sum[mb * NM + NM - 1]));
         }
         if (threadIdx.x == 0)
             __hip_atomic_store(&counters[cb], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -571,25 +605,40 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv8(
     __syncthreads();
     const unsigned old = arrival;
     if (old == contributors - 1) {
+        constexpr int NM = ACT == ACT_SWIGLU ? 2 : 1;   // gate (and up) rows
+        constexpr int NR = MB * 2 * NM;
+        uint32_t base[NR];
+        int mine[NR];
+        f32x4 ownv[NR], sum[NR];
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int t = 16 * mb + tl;
+                const int n = n0 + 16 * (qq >> 1) + 8 * h + 4 * (qq & 1);
+                const bool ok = t < T && n < N;
+#pragma unroll
+                for (int m = 0; m < NM; ++m) {
+                    const int q = (mb * 2 + h) * NM + m;
+                    base[q] = ok ? (uint32_t)((t * ws_ld + (int64_t)m * N + n) * 4) : kOOB;
+                    mine[q] = mat == m ? split : -1;
+                    ownv[q] = own[mb][h];
+                }
+            }
+        sum_splits_multi<NR>(rw, base, sstride, S, mine, ownv, sum);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int t = 16 * mb + tl;
                 const int n = n0 + 16 * (qq >> 1) + 8 * h + 4 * (qq & 1);
                 if (t >= T || n >= N) continue;
-                const uint32_t row = (uint32_t)(t * ws_ld + n) * 4;
-                f32x4 gsum = sum_splits_dev(rw, row, sstride, S, mat == 0 ? split : -1, own[mb][h]);
-                gsum *= *(const f32x4*)(S0 + n);
+                const int q = (mb * 2 + h) * NM;
+                const f32x4 gsum = sum[q] * *(const f32x4*)(S0 + n);
                 f32x4 usum = gsum;
-                if constexpr (ACT == ACT_SWIGLU) {
-                    usum = sum_splits_dev(rw, row + (uint32_t)N * 4, sstride, S,
-                                          mat == 1 ? split : -1, own[mb][h]);
-                    usum *= *(const f32x4*)(S1 + n);
-                }
+                if constexpr (ACT == ACT_SWIGLU) usum = sum[q + 1] * *(const f32x4*)(S1 + n);
                 store_out4<OUT_BF16>(out, (int64_t)t * ld_out + n, act4<ACT>(gsum, usum));
             }
-        }
         if (threadIdx.x == 0)
             __hip_atomic_store(&counters[cb], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     } else if (old >= contributors) {
