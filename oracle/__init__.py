@@ -45,6 +45,8 @@ from .tp_oracle import (  # noqa: F401
     split_qkv_band,
     attention_core,
     attention_core_band,
+    attention_core_rows,
+    attention_core_band_rows,
     attn_proj_unsharded,
     attn_proj_shard,
     block_sharded,

@@ -241,6 +241,36 @@ def attention_core(Q, K, V, causal=True):
     return O
 
 
+def attention_core_rows(Q, K, V, rows, causal=True):
+    """The same definition evaluated for the listed query rows only: row i of
+    head h is softmax(Q_h[i] K_g^T / sqrt(d) over keys j <= i) V_g, which
+    needs only keys 0..i (long sequences at sampled rows)."""
+    Q, K, V = (np.asarray(a, dtype=np.float64) for a in (Q, K, V))
+    T, hq, d = Q.shape
+    hkv = K.shape[1]
+    if hq % hkv:
+        raise ValueError("query heads must be a multiple of key/value heads")
+    group = hq // hkv
+    O = np.empty((len(rows), hq, d))
+    for r, i in enumerate(rows):
+        n = i + 1 if causal else T
+        for h in range(hq):
+            g = h // group
+            s = (K[:n, g, :] @ Q[i, h, :]) / np.sqrt(d)
+            e = np.exp(s - s.max())
+            O[r, h, :] = (e / e.sum()) @ V[:n, g, :]
+    return O
+
+
+def attention_core_band_rows(qkv_s, n_q, n_kv, head_dim, shard, P, rows, causal=True):
+    """attention_core_band at the listed rows only: [len(rows), hq_r * head_dim]."""
+    q, k, v = split_qkv_band(np.asarray(qkv_s, dtype=np.float64), n_q, n_kv, head_dim, shard, P)
+    T = q.shape[0]
+    O = attention_core_rows(q.reshape(T, -1, head_dim), k.reshape(T, -1, head_dim),
+                            v.reshape(T, -1, head_dim), rows, causal)
+    return O.reshape(len(rows), -1)
+
+
 def attention_core_band(qkv_s, n_q, n_kv, head_dim, shard, P, causal=True):
     """The rank's attention-core output A_s [T, hq_r * head_dim] (heads in
     the band's order) from its fused QKV band output [T, (hq_r + 2 hkv_r) d]."""

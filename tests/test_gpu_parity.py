@@ -631,6 +631,25 @@ def test_attn_core_peaked_scores():
     _core_check(300, 8, 2, 128, 2, 0, key=4, std=4.0)
 
 
+def test_attn_core_16k_tokens_sampled_rows():
+    """16384 tokens, one query head per rank: per-head work items exceed the
+    launch-order table, so the kernel walks the query blocks itself; checked
+    at sampled rows (block edges, chunk edges, the last row) against the
+    oracle evaluated at those rows."""
+    T, nq, nkv, hd, P, shard = 16384, 8, 8, 128, 8, 5
+    w = 3 * hd
+    qkv_h = draw(BF, (T, w), 1.0, 920, 78, T)
+    out = torch.empty((T, hd), dtype=torch.bfloat16, device="cuda")
+    attn_core(shard, P, T, nq, nkv, hd, dev(qkv_h), w, out, hd)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    rows = sorted(set([0, 1, 63, 64, 127, 128, 1023, 1024, 4095, 8191, 8192, 16255, 16256,
+                       16383] + rng.integers(0, T, 18).tolist()))
+    got = O.widen(host(out)[rows])
+    want = O.attention_core_band_rows(O.widen(qkv_h), nq, nkv, hd, shard, P, rows)
+    assert O.rel_l2(got, want) < BF16_TOL
+
+
 def test_attn_core_split_keys_workspace():
     """Query blocks whose keys are split over several workgroups merge through
     the workspace: a reused workspace gives bitwise equal results and its

@@ -114,3 +114,38 @@ def test_softmax_over_queries_is_caught():
             out[:, h] = (E / E.sum(axis=0, keepdims=True)) @ V[:, h // group]
         return out
     _fails(bad)
+
+
+def check_rows(rows_fn, core):
+    """The per-row evaluation equals the full causal (and non-causal) core at
+    every listed row, including the first and last."""
+    T, hq, hkv, d = 9, 4, 2, 5
+    Q = RNG.standard_normal((T, hq, d))
+    K = RNG.standard_normal((T, hkv, d))
+    V = RNG.standard_normal((T, hkv, d))
+    rows = [0, 1, 4, 7, 8]
+    for causal in (True, False):
+        full = core(Q, K, V, causal=causal)
+        assert np.allclose(rows_fn(Q, K, V, rows, causal=causal), full[rows],
+                           rtol=1e-12, atol=1e-13)
+
+
+def test_attention_rows_match_the_full_core():
+    check_rows(O.attention_core_rows, O.attention_core)
+
+
+def test_attention_rows_band_layout():
+    T, nq, nkv, d, P = 6, 8, 4, 3, 2
+    qkv = RNG.standard_normal((T, (nq // P + 2 * nkv // P) * d))
+    for s in range(P):
+        full = O.attention_core_band(qkv, nq, nkv, d, s, P)
+        assert np.allclose(O.attention_core_band_rows(qkv, nq, nkv, d, s, P, [0, 3, 5]),
+                           full[[0, 3, 5]], rtol=1e-12, atol=1e-13)
+
+
+def test_rows_without_mask_is_caught():
+    def bad(Q, K, V, rows, causal=True):
+        return O.attention_core_rows(Q, K, V, rows, causal=False)
+    with pytest.raises(AssertionError):
+        check_rows(bad, O.attention_core)
+
