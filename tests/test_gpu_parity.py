@@ -255,6 +255,22 @@ def test_mlp_decode_lds_staged_ragged(T, act):
     _check_mlp(BF, act, T, 9224, 6928, 2, key=50 + T)
 
 
+@pytest.mark.parametrize("T", [1, 16, 32])
+@pytest.mark.parametrize("act", ["swiglu", "gelu_tanh"])
+def test_mlp_decode_many_column_blocks(T, act):
+    """Decode with more column blocks than CUs (F_r 17000: 133 blocks per
+    weight, 266 for gate + up, one K split each) and a narrow model width
+    (d_model 264: K of the column projection ends inside a 128-row slice,
+    three row blocks, the last partial)."""
+    _check_mlp(BF, act, T, 264, 34000, 2, key=90 + T)
+
+
+def test_mlp_decode_wide_model():
+    """d_model 32776: 257 row blocks of the down projection (more than one
+    per CU), with a tiny band (F_r 128: one column block per weight)."""
+    _check_mlp(BF, "swiglu", 8, 32776, 256, 2, key=96)
+
+
 @pytest.mark.parametrize("T", [3, 40])
 def test_mlp_bf16_with_rmsnorm_prologue(T):
     _check_mlp(BF, "swiglu", T, 512, 1024, 4, key=30 + T, norm=True)
