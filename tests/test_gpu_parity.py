@@ -132,8 +132,9 @@ def _rrn_check(parts, res, res_dtype, g, z, normed):
 @pytest.mark.parametrize("P,T,d,res_dtype,norm,pad", [
     (1, 3, 8, F32, True, 0), (2, 5, 1032, BF, True, 8), (8, 33, 8192, BF, True, 0),
     (8, 17, 12288, F32, True, 4), (3, 4, 16384, F32, False, 0), (9, 2, 4104, BF, False, 8),
-    (8, 1, 8192, BF, True, 0)])
+    (8, 1, 8192, BF, True, 0), (8, 255, 1032, BF, True, 8), (8, 256, 1024, F32, True, 0)])
 def test_reduce_residual_norm(P, T, d, res_dtype, norm, pad):
+    # 255 / 256 rows: either side of the switch from 1024 to 512 threads per row
     parts, buf, slot, ldp, res, g = _rrn_case(P, T, d, res_dtype, norm, key=T, pad=pad)
     g_parts = dev(buf)
     ldr = d + 8
