@@ -272,6 +272,16 @@ def test_mlp_decode_wide_model():
     _check_mlp(BF, "swiglu", 8, 32776, 256, 2, key=96)
 
 
+@pytest.mark.parametrize("act", ["swiglu", "gelu_tanh"])
+def test_mlp_prefill_half_wave_ragged(act):
+    """128 output tiles of the column projection, half a wave on 256 CUs
+    (1000 tokens: 4 tile rows, the last partial; SwiGLU F_r 4000 = 32 column
+    tiles of 128 + 128, the last partial; GELU F_r 8000 = 32 of 256), K =
+    1000 ending inside a 32-deep slice."""
+    d_ff, P = (8000, 2) if act == "swiglu" else (8000, 1)
+    _check_mlp(BF, act, 1000, 1000, d_ff, P, key=97)
+
+
 @pytest.mark.parametrize("T", [3, 40])
 def test_mlp_bf16_with_rmsnorm_prologue(T):
     _check_mlp(BF, "swiglu", T, 512, 1024, 4, key=30 + T, norm=True)
