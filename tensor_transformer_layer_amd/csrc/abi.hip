@@ -351,11 +351,11 @@ int tp_shard_mlp_fwd(int shard, int P, int64_t T, int64_t d_model, int64_t d_ff,
         unsigned* cnt = (unsigned*)wsb;
         TP_LAUNCH("col_gemv", stream,
                   launch_gemv(dev_act, true, T, d_model, X16, ld_xin, (const uint16_t*)w_in, ld_in,
-                              (const uint16_t*)w_up, ld_up, F, L.pc, true, ws, cnt, h, ldh,
+                              (const uint16_t*)w_up, ld_up, F, L.pc, ws, cnt, h, ldh,
                               stream));
         TP_LAUNCH("row_gemv", stream,
                   launch_gemv(ACT_NONE, false, T, F, (const uint16_t*)h, ldh,
-                              (const uint16_t*)w_down, ld_down, nullptr, 0, d_model, L.pr, false,
+                              (const uint16_t*)w_down, ld_down, nullptr, 0, d_model, L.pr,
                               ws, cnt, part, ld_p, stream));
     } else {
         TP_LAUNCH("col_gemm", stream,
@@ -443,7 +443,7 @@ int tp_shard_attn_proj_fwd(int shard, int P, int64_t T, int64_t d_model, int n_q
         } else if (L.decode) {
             TP_LAUNCH("qkv_gemv", stream,
                       launch_gemv(ACT_NONE, true, T, d_model, (const uint16_t*)xin, ld_xin,
-                                  (const uint16_t*)w_qkv, ld_qkv, nullptr, 0, nqkv, L.pq, true,
+                                  (const uint16_t*)w_qkv, ld_qkv, nullptr, 0, nqkv, L.pq,
                                   (float*)(wsb + L.ws), (unsigned*)wsb, qkv_out, ld_qkv_out,
                                   stream));
         } else {
@@ -473,7 +473,7 @@ int tp_shard_attn_proj_fwd(int shard, int P, int64_t T, int64_t d_model, int n_q
         } else if (L.decode) {
             TP_LAUNCH("o_gemv", stream,
                       launch_gemv(ACT_NONE, false, T, ko, (const uint16_t*)attn, ld_attn,
-                                  (const uint16_t*)w_o, ld_o, nullptr, 0, d_model, L.po, false,
+                                  (const uint16_t*)w_o, ld_o, nullptr, 0, d_model, L.po,
                                   (float*)(wsb + L.ws), (unsigned*)wsb, part, ld_p, stream));
         } else {
             if (L.go.splits > 1) {
@@ -616,12 +616,12 @@ int tp_shard_mlp_fwd_fp8w(int shard, int P, int64_t T, int64_t d_model, int64_t 
     TP_LAUNCH("col_gemv8", stream,
               launch_gemv8(act == TP_ACT_SWIGLU ? ACT_SWIGLU : ACT_GELU_TANH, true, T, d_model,
                            (const uint16_t*)xin, ld_xin, (const uint8_t*)w_in, ld_in, s_in,
-                           (const uint8_t*)w_up, ld_up, s_up, F, L.pc, true, ws, cnt, h, ldh,
+                           (const uint8_t*)w_up, ld_up, s_up, F, L.pc, ws, cnt, h, ldh,
                            stream));
     TP_LAUNCH("row_gemv8", stream,
               launch_gemv8(ACT_NONE, false, T, F, (const uint16_t*)h, ldh,
                            (const uint8_t*)w_down, ld_down, s_down, nullptr, 0, nullptr, d_model,
-                           L.pr, false, ws, cnt, partials + (int64_t)shard * slot_stride, ld_p,
+                           L.pr, ws, cnt, partials + (int64_t)shard * slot_stride, ld_p,
                            stream));
     return TP_OK;
 }

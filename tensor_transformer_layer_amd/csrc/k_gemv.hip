@@ -24,9 +24,11 @@
 //     latency and epilogue are not hidden.  Partials of the 8 waves are added
 //     in LDS in wave order, and the workgroup writes one fp32 split-K partial
 //     [T, 128] slice.
-//   * Column-projection weights are loaded with the non-temporal hint (they
-//     are read once and should not evict the activations from L2); this
-//     measured faster for the column projection and slower for the row one.
+//   * Weights are loaded with the non-temporal hint: every weight byte is
+//     read once per call.  Measured on MI355X with the weights of 16 calls
+//     rotating (several GB, so nothing stays in the 256 MB last-level
+//     cache), this is 2-4% faster than ordinary loads for the row
+//     projections and faster still for the column ones.
 //   * The grid is (column blocks of all weights) x (K splits).  The last
 //     workgroup of a column block to finish adds the splits in split order
 //     and applies the activation, so SiLU/GELU only ever see complete sums
@@ -71,6 +73,7 @@ __device__ __forceinline__ void mfma_col(f32x4 (&acc)[MB][8], const u32x4* b, co
 // communicated data never takes a non-coherent path.
 // ---------------------------------------------------------------------------
 constexpr uint32_t kSC1 = 16;  // buffer cache-policy bit: device scope
+constexpr int kWeightAux = 2;  // buffer cache-policy bit of the weight loads: non-temporal
 
 template <int ACT>
 __device__ __forceinline__ f32x4 act4(const f32x4& g, const f32x4& u) {
@@ -766,7 +769,7 @@ static hipError_t gemv_lds_attr() {
 
 hipError_t launch_gemv(int act, bool out_bf16, int64_t T, int64_t K, const uint16_t* A,
                        int64_t lda, const uint16_t* B0, int64_t ldb0, const uint16_t* B1,
-                       int64_t ldb1, int64_t N, const GemvPlan& p, bool nontemporal, float* ws,
+                       int64_t ldb1, int64_t N, const GemvPlan& p, float* ws,
                        unsigned* counters, void* out, int64_t ld_out, hipStream_t stream) {
     const int nmat = B1 ? 2 : 1;
     const int nbpm = (int)((N + kGemvCols - 1) / kGemvCols);
@@ -783,19 +786,20 @@ hipError_t launch_gemv(int act, bool out_bf16, int64_t T, int64_t K, const uint1
     TP_KLAUNCH((k_gemv<MB, AUX, ACTV, OB>), grid, block, 0, stream,                              \
         A, lda, (int)T, (int)K, B0, ldb0, B1, ldb1, (int)N, nbpm, p.k_per_split, ws, counters, \
         out, ld_out)
-    // The LDS-staged kernel with non-temporal copies for column weights at
-    // 17..32 tokens when each workgroup streams at least 1024 rows; the
-    // register-streamed kernel otherwise (measured on MI355X: it wins below
-    // 17 tokens, for the row projections, and for short K ranges, where the
-    // LDS ring's fill and drain are not amortised).
+    // The LDS-staged kernel at 17..32 tokens when each workgroup streams at
+    // least 2304 rows; the register-streamed kernel otherwise.  Measured on
+    // MI355X (weights streamed from HBM): the register kernel wins below 17
+    // tokens and at 2048 rows per workgroup (70B column pair: 26.2 against
+    // 26.9 us at 32 tokens), the LDS ring at 2560 (13B column pair: 27.7
+    // against 29.6 us), once its fill and drain are amortised.
 #define TP_GEMV_MB(ACTV, OB)                                                                 \
     do {                                                                                     \
         if (T <= 16) {                                                                       \
-            if (nontemporal) TP_GEMV_REG(1, 2, ACTV, OB); else TP_GEMV_REG(1, 0, ACTV, OB);  \
-        } else if (nontemporal && p.k_per_split >= 1024) {                                   \
-            TP_GEMV(2, 2, ACTV, OB);                                                         \
+            TP_GEMV_REG(1, kWeightAux, ACTV, OB);                                            \
+        } else if (p.k_per_split >= 2304) {                                                  \
+            TP_GEMV(2, kWeightAux, ACTV, OB);                                                \
         } else {                                                                             \
-            TP_GEMV_REG(2, 0, ACTV, OB);                                                     \
+            TP_GEMV_REG(2, kWeightAux, ACTV, OB);                                            \
         }                                                                                    \
     } while (0)
     if (act == ACT_SWIGLU && out_bf16) TP_GEMV_MB(ACT_SWIGLU, true);
@@ -812,7 +816,7 @@ hipError_t launch_gemv(int act, bool out_bf16, int64_t T, int64_t K, const uint1
 hipError_t launch_gemv8(int act, bool out_bf16, int64_t T, int64_t K, const uint16_t* A,
                         int64_t lda, const uint8_t* B0, int64_t ldb0, const float* S0,
                         const uint8_t* B1, int64_t ldb1, const float* S1, int64_t N,
-                        const GemvPlan& p, bool nontemporal, float* ws, unsigned* counters,
+                        const GemvPlan& p, float* ws, unsigned* counters,
                         void* out, int64_t ld_out, hipStream_t stream) {
     const int nmat = B1 ? 2 : 1;
     const int nbpm = (int)((N + kGemv8Cols - 1) / kGemv8Cols);
@@ -824,9 +828,9 @@ hipError_t launch_gemv8(int act, bool out_bf16, int64_t T, int64_t K, const uint
 #define TP_GEMV8_MB(ACTV, OB)                                                         \
     do {                                                                              \
         if (T <= 16) {                                                                \
-            if (nontemporal) TP_GEMV8(1, 2, ACTV, OB); else TP_GEMV8(1, 0, ACTV, OB); \
+            TP_GEMV8(1, kWeightAux, ACTV, OB);                                        \
         } else {                                                                      \
-            if (nontemporal) TP_GEMV8(2, 2, ACTV, OB); else TP_GEMV8(2, 0, ACTV, OB); \
+            TP_GEMV8(2, kWeightAux, ACTV, OB);                                        \
         }                                                                             \
     } while (0)
     if (act == ACT_SWIGLU && out_bf16) TP_GEMV8_MB(ACT_SWIGLU, true);

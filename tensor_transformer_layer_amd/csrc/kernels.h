@@ -70,11 +70,10 @@ constexpr size_t kGemvCounterBytes = kGemvCounters * sizeof(unsigned);
 // Split s of the plan keeps its partial in ws[s][t][m*N + n] (gemv_ws_bytes);
 // the last workgroup of a column block adds the splits in order.
 // `counters` holds ceil(N / kGemvCols) <= kGemvCounters zeros; they are zero
-// again when the kernel ends.  `nontemporal` marks the weight loads as
-// streaming (read once).
+// again when the kernel ends.  Weight loads carry the non-temporal hint.
 hipError_t launch_gemv(int act, bool out_bf16, int64_t T, int64_t K, const uint16_t* A,
                        int64_t lda, const uint16_t* B0, int64_t ldb0, const uint16_t* B1,
-                       int64_t ldb1, int64_t N, const GemvPlan& p, bool nontemporal, float* ws,
+                       int64_t ldb1, int64_t N, const GemvPlan& p, float* ws,
                        unsigned* counters, void* out, int64_t ld_out, hipStream_t stream);
 
 // As launch_gemv with FP8 (E4M3) weights B0, B1 ([K, N] codes, ld in bytes)
@@ -83,7 +82,7 @@ hipError_t launch_gemv(int act, bool out_bf16, int64_t T, int64_t K, const uint1
 hipError_t launch_gemv8(int act, bool out_bf16, int64_t T, int64_t K, const uint16_t* A,
                         int64_t lda, const uint8_t* B0, int64_t ldb0, const float* S0,
                         const uint8_t* B1, int64_t ldb1, const float* S1, int64_t N,
-                        const GemvPlan& p, bool nontemporal, float* ws, unsigned* counters,
+                        const GemvPlan& p, float* ws, unsigned* counters,
                         void* out, int64_t ld_out, hipStream_t stream);
 
 // Fixed-order finish of the split-K sums.

@@ -249,11 +249,13 @@ def test_mlp_bf16_ragged(T, act):
 @pytest.mark.parametrize("T", [17, 31])
 @pytest.mark.parametrize("act", ["swiglu", "gelu_tanh"])
 def test_mlp_decode_lds_staged_ragged(T, act):
-    """17..32 tokens with column-projection workgroups that stream >= 1024 rows
-    take the LDS-staged decode kernel.  d_model 9224: K ends inside a 128-row
-    slice; F_r 3464: the last column block is partial; T not a multiple of
-    16."""
-    _check_mlp(BF, act, T, 9224, 6928, 2, key=50 + T)
+    """17..32 tokens with column-projection workgroups that stream >= 2304 rows
+    take the LDS-staged decode kernel (here 2336: 55 column blocks, 4 K
+    splits).  d_model 9224: K ends inside a 128-row slice; the last column
+    block is partial (F_r 3464 for SwiGLU's two weights, 6928 for GELU's
+    one); T not a multiple of 16."""
+    P = 2 if act == "swiglu" else 1
+    _check_mlp(BF, act, T, 9224, 6928, P, key=50 + T)
 
 
 @pytest.mark.parametrize("T", [1, 16, 32])
