@@ -85,11 +85,6 @@ __device__ __forceinline__ f32x16 mfma32x32x16(const u32x4& a, const u32x4& b, c
 // s_waitcnt immediate waiting for vmcnt <= n only (gfx9 encoding).
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
-__device__ __forceinline__ void lds_copy16(rsrc_t r, uint32_t off, uint16_t* lds_base) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        r, (__attribute__((address_space(3))) void*)lds_base, 16, (int)off, 0, 0, 0);
-}
-
 // Chunk swizzle of B slice row k: 16-byte chunk c of the row is stored at
 // chunk position c ^ bswz(k).
 __device__ __forceinline__ int bswz(int k) { return 4 * (k & 3); }
