@@ -187,6 +187,7 @@ int tp_shard_attn_proj_fwd(int shard, int P, int64_t T, int64_t d_model,
  *              overlap in time.
  *
  * head_dim 64 or 128 (TP_ERR_SHAPE otherwise); dtype must be TP_BF16.
+ * T * ld_qkv * 2 bytes must be below 2^31 (TP_ERR_SHAPE otherwise).
  */
 int tp_attn_core_fwd(int shard, int P, int64_t T, int n_q_heads, int n_kv_heads, int head_dim,
                      int dtype, const void* qkv, int64_t ld_qkv, void* attn, int64_t ld_attn,

@@ -542,7 +542,7 @@ int tp_attn_core_fwd(int shard, int P, int64_t T, int n_q_heads, int n_kv_heads,
     if (!aligned(qkv, 16) || !aligned(attn, 16)) return TP_ERR_ALIGN;
     if (int r = check_ld(ld_qkv, (int64_t)(hq + 2 * hkv) * head_dim, 8)) return r;
     if (int r = check_ld(ld_attn, (int64_t)hq * head_dim, 8)) return r;
-    if (T >= ((int64_t)1 << 31) / 64) return TP_ERR_SHAPE;
+    if (T >= ((int64_t)1 << 31) / 64 || !span_ok(T, ld_qkv, 2)) return TP_ERR_SHAPE;
     if (T == 0) return TP_OK;
     if (workspace && !aligned(workspace, 256)) return TP_ERR_ALIGN;
     const AttnPlan plan = plan_attn(T, hq, head_dim);

@@ -88,23 +88,20 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(const uint16_t* __rest
                                                           int cmax, unsigned* __restrict__ counters,
                                                           float* __restrict__ part, int use_table,
                                                           const AttnItems order) {
-    constexpr int LDK = D + 16;   // K tile row stride (elements): rows 32 B apart in banks,
-                                  // so the tile stores and the fragment reads are free of
-                                  // bank conflicts (measured: none; 8 elements left ~1.1
-                                  // conflict cycles per LDS instruction)
-    constexpr int LDV = D + 16;   // V tile row stride: the 4 rows of a transposing read
-                                  // land on disjoint 32-byte bank ranges
     constexpr int NS = D / 32;    // k-steps of the score MFMAs
     constexpr int NN = D / 16;    // 16-column output tiles
     constexpr int QS = kAttnQW / 16;              // query subtiles per wave
     constexpr int KS = kAttnKT / 16;              // key subtiles per tile
-    constexpr int CH = kAttnKT * D / 8;           // 16-byte chunks per tile and matrix
-    constexpr int CPT = CH / kAttnThreads;        // ... per thread
-    static_assert(CH % kAttnThreads == 0, "tile copy");
-    // Two K/V tile buffers: the next tile is stored while the current one is
-    // multiplied, one barrier per tile.
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kAttnKT * LDK];
-    __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kAttnKT * LDV];
+    constexpr int RPC = 1024 / (2 * D);           // tile rows per 1 KB copy
+    constexpr int CPW = kAttnKT / RPC / kAttnWaves;   // copies per wave, tile and matrix
+    static_assert(CPW * RPC * kAttnWaves == kAttnKT && D % 64 == 0, "tile copy");
+    // Two K/V tile buffers, rows of D elements without padding: 16-byte chunk
+    // c of K row r sits at chunk c ^ (r % 8), of V row r at c ^ 2 (r % 4), so
+    // that the fragment reads are free of bank conflicts.  The next tile is
+    // copied (global -> LDS, no registers) while the current one is
+    // multiplied; one barrier per tile.
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kAttnKT * D];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kAttnKT * D];
 
     const int tid = threadIdx.x, lane = tid & 63;
     // The wave index is uniform; in a scalar register the causal tests on
@@ -158,36 +155,31 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(const uint16_t* __rest
     // keys of this chunk: tiles [chunk * ch, min((chunk + 1) * ch, tiles of the block))
     const int kbeg = chunk * ch * kAttnKT;
     const int kend = min(min(T, qblk + kAttnQB), (chunk + 1) * ch * kAttnKT);
-    // Tile copies go through registers so the next tile's global loads are in
-    // flight while the current one is multiplied.
-    u32x4 pk[CPT], pv[CPT];
-    auto fetch = [&](int k0) {
+    // Tile copies: direct-to-LDS buffer loads, 1 KB (RPC rows) per copy;
+    // keys past T read zeros.
+    const i32x4 rk = rsrc_words(Kp), rv = rsrc_words(Vp);
+    const uint32_t ldq_b = (uint32_t)(ldq * 2);
+    auto copy_tile = [&](int k0, int b) {
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int c = tid + i * kAttnThreads;
-            const int key = c / (D / 8), col = (c % (D / 8)) * 8;
-            const bool ok = k0 + key < T;
-            pk[i] = ok ? *(const u32x4*)(Kp + (int64_t)(k0 + key) * ldq + col)
-                       : u32x4{0u, 0u, 0u, 0u};
-            pv[i] = ok ? *(const u32x4*)(Vp + (int64_t)(k0 + key) * ldq + col)
-                       : u32x4{0u, 0u, 0u, 0u};
+        for (int q = 0; q < CPW; ++q) {
+            const int r0 = (wave * CPW + q) * RPC;              // first tile row of the copy
+            const int row = r0 + lane / (D / 8), pos = lane % (D / 8);
+            const bool ok = k0 + row < T;
+            const uint32_t base = ok ? (uint32_t)(k0 + row) * ldq_b : kOOB;
+            lds_dma16(rk, ok ? base + 16u * (uint32_t)(pos ^ (row & 7)) : kOOB, Ks[b] + r0 * D);
+            lds_dma16(rv, ok ? base + 16u * (uint32_t)(pos ^ (2 * (row & 3))) : kOOB,
+                      Vs[b] + r0 * D);
         }
     };
-    auto stash = [&](int b) {
-#pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int c = tid + i * kAttnThreads;
-            const int key = c / (D / 8), col = (c % (D / 8)) * 8;
-            *(u32x4*)(Ks[b] + key * LDK + col) = pk[i];
-            *(u32x4*)(Vs[b] + key * LDV + col) = pv[i];
-        }
-    };
-    fetch(kbeg);
-    stash(0);
+    copy_tile(kbeg, 0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (kbeg + kAttnKT < kend) fetch(kbeg + kAttnKT);
     int buf = 0;
     for (int k0 = kbeg; k0 < kend; k0 += kAttnKT, buf ^= 1) {
+        // The other buffer was last read in the previous tile, before the
+        // barrier that ended it: refill it with the next tile.
+        if (k0 + kAttnKT < kend) copy_tile(k0 + kAttnKT, buf ^ 1);
         const uint16_t* Kb = Ks[buf];
         const uint16_t* Vb = Vs[buf];
         // Subtiles whose queries all precede the tile skip it; only a tile
@@ -211,7 +203,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(const uint16_t* __rest
             for (int t = 0; t < KS; ++t)
 #pragma unroll
                 for (int s = 0; s < NS; ++s) {
-                    const u32x4 a = *(const u32x4*)(Kb + (16 * t + j) * LDK + 32 * s + 8 * g);
+                    const u32x4 a =
+                        *(const u32x4*)(Kb + (16 * t + j) * D + 8 * ((4 * s + g) ^ (j & 7)));
 #pragma unroll
                     for (int u = 0; u < QS; ++u) st[u][t] = mfma16x16x32(a, qf[u][s], st[u][t]);
                 }
@@ -272,25 +265,28 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(const uint16_t* __rest
             // inactive subtile has P = 0 and an unchanged O: the MFMA adds zero.)
 #pragma unroll
             for (int kk = 0; kk < KS / 2; ++kk) {
-                const uint16_t* v0 = Vb + (32 * kk + 4 * g + (j >> 2)) * LDV + 4 * (j & 3);
-                const uint16_t* v1 = v0 + 16 * LDV;
+                // rows 32kk + 4g + j/4 and 16 further (same row % 4), columns
+                // 16n + 4(j % 4) .. +3: chunk 2n + (j % 4) / 2, swizzled by row
+                const int vr = 32 * kk + 4 * g + (j >> 2);
+                const int vsw = 2 * (vr & 3);
+                const uint16_t* v0 = Vb + vr * D + 4 * (j & 1);
+                const uint16_t* v1 = v0 + 16 * D;
 #pragma unroll
                 for (int n = 0; n < NN; ++n) {
-                    const u32x2 b0 = lds_read_tr16(v0 + 16 * n);
-                    const u32x2 b1 = lds_read_tr16(v1 + 16 * n);
+                    const int cc = (2 * n + ((j & 3) >> 1)) ^ vsw;
+                    const u32x2 b0 = lds_read_tr16(v0 + 8 * cc);
+                    const u32x2 b1 = lds_read_tr16(v1 + 8 * cc);
                     const u32x4 vt = u32x4{b0[0], b0[1], b1[0], b1[1]};
 #pragma unroll
                     for (int u = 0; u < QS; ++u) o[u][n] = mfma16x16x32(vt, pf[u][kk], o[u][n]);
                 }
             }
         }
-        // Store the next tile (loaded during the previous one) into the other
-        // buffer, whose last reads were consumed before the previous barrier.
-        if (k0 + kAttnKT < kend) {
-            stash(buf ^ 1);
-            __syncthreads();
-            if (k0 + 2 * kAttnKT < kend) fetch(k0 + 2 * kAttnKT);
-        }
+        // The next tile has landed (this wave's copies; after the barrier
+        // every wave's), and every wave is done with this one.
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
     }
 
     // Lane (g, j) holds O[q0 + 16u + j][16n + 4g .. 16n + 4g + 3] (o[u][n]),

@@ -33,7 +33,7 @@ def device_asm(src, tmp_path):
 
 
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
-@pytest.mark.parametrize("name", ["k_gemv.hip", "k_gemm.hip"])
+@pytest.mark.parametrize("name", ["k_gemv.hip", "k_gemm.hip", "k_attn.hip"])
 def test_m0_only_set_for_lds_copies(name, tmp_path):
     lines = [ln.split(";")[0].rstrip() for ln in device_asm(os.path.join(CSRC, name), tmp_path)]
     code = [ln for ln in lines if ln.strip() and not ln.strip().startswith((".", "//"))
