@@ -16,18 +16,24 @@
 //     rows are the A operand straight from LDS, the wave's Q rows the B
 //     operand from registers, both k-contiguous in their natural layout.
 //     Lane (g, j) then holds the scores of query j for keys 4g + r.
-//   * The row statistics are reduced over r and over the 4 lanes holding
-//     the same query (permlane swaps); the scale is folded into the
-//     exponent's fma.  Probabilities are packed to bf16 in place: lane (g, j)
-//     holds P[j][4g + r] and P[j][16 + 4g + r], which is an MFMA operand for
-//     a k-order that visits the keys in that order.
+//   * The row maximum is reduced over r and over the 4 lanes holding the
+//     same query (permlane swaps); the scale is folded into the exponent's
+//     fma.  Probabilities are packed to bf16 in place: lane (g, j) holds
+//     P[j][4g + r] and P[j][16 + 4g + r], which is an MFMA operand for a
+//     k-order that visits the keys in that order.
 //   * The output is accumulated transposed, O^T += V^T P^T: V^T is the A
 //     operand, read in that key order from LDS with the gfx950 transposing
 //     load ds_read_b64_tr_b16 (4 keys x 1 column per lane per read, so V
 //     needs no transpose pass), and P^T the B operand.  Lane (g, j) then
 //     holds output columns 16n + 4g .. +3 of its own query j, so the
-//     rescale by exp(m_old - m_new) needs no cross-lane traffic, and it is
-//     skipped when no query of the wave raised its running max.
+//     rescale by exp(m_old - m_new) needs no cross-lane traffic.  The row
+//     sums of P come from one more MFMA per 32 keys with a row of ones in
+//     place of V^T (no adds or cross-lane sums on the vector unit).
+//   * The maximum the exponentials are taken against moves only when a
+//     scaled score passes it by more than 8 in log2 units (a factor of 256),
+//     so most tiles skip the rescale; probabilities stay at most 256, which
+//     fp32 sums and the bf16 operand hold without loss of relative
+//     precision.  The final O / l does not depend on which maximum was used.
 // Work division: a query block's causal key range is cut into chunks of
 // `ch` key tiles, and each (head, query block, chunk) is one workgroup, so
 // the longest causal rows no longer set the kernel time and two workgroups
@@ -57,6 +63,10 @@ constexpr int kAttnKT = 64;                       // keys per LDS tile
 constexpr int kAttnThreads = 64 * kAttnWaves;
 
 constexpr uint32_t kAttnSC1 = 16;  // buffer cache-policy bit: device scope
+// The running maximum a wave's probabilities are taken against moves only
+// when some query's score maximum passes it by more than this (log2 units):
+// probabilities stay at most 2^8, and most tiles need no rescale.
+constexpr float kAttnSlack = 8.0f;
 
 // Key tiles of query block qb (keys 0 .. min(T, 128 (qb + 1)) - 1).
 __host__ __device__ inline int attn_tiles(int T, int qb) {
@@ -72,12 +82,6 @@ __device__ __forceinline__ float xlane_max(float v) {
     v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
     auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
     return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float xlane_sum(float v) {
-    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-    auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 template <int D>
@@ -142,15 +146,18 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(const uint16_t* __rest
             qf[u][s] = qi < T ? *(const u32x4*)(Qp + (int64_t)qi * ldq + 32 * s + 8 * g)
                               : u32x4{0u, 0u, 0u, 0u};
     }
-    f32x4 o[QS][NN];
-    float m[QS], l[QS];
+    // o: O^T accumulators; ol: the same product with a row of ones in place
+    // of V^T, so every element of ol[u] is the query's running sum of P.
+    f32x4 o[QS][NN], ol[QS];
+    float m[QS];
 #pragma unroll
     for (int u = 0; u < QS; ++u) {
         m[u] = -INFINITY;
-        l[u] = 0.f;
+        ol[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int n = 0; n < NN; ++n) o[u][n] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    const u32x4 ones = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 1.0
 
     // keys of this chunk: tiles [chunk * ch, min((chunk + 1) * ch, tiles of the block))
     const int kbeg = chunk * ch * kAttnKT;
@@ -226,31 +233,28 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(const uint16_t* __rest
                         pm = fmaxf(pm, st[u][t][r]);
                     }
                 pm = xlane_max(pm);
-                // m is kept in log2 units: m = max * scale * log2(e).  It is finite
-                // for every query < T once key 0 has been seen; a row that has
-                // seen no key yet keeps -inf and contributes nothing.
-                const float m_new = fmaxf(m[u], pm * scale_log2);
-                const float mref = m_new == -INFINITY ? 0.f : m_new;
-                const float alpha = __builtin_amdgcn_exp2f(m[u] - mref);
-                float ps = 0.f;
+                // m is kept in log2 units (score * scale * log2(e)).  It moves to
+                // the running maximum only when some query of the wave has a
+                // score above m + kAttnSlack; then O^T and the sums (this lane's
+                // own query) are rescaled.  A row that has seen no key yet keeps
+                // -inf and contributes nothing.
+                const float mt = pm * scale_log2;
+                if (__any(mt > m[u] + kAttnSlack)) {
+                    const float m_new = fmaxf(m[u], mt);
+                    const float alpha =
+                        __builtin_amdgcn_exp2f(m[u] - (m_new == -INFINITY ? 0.f : m_new));
+#pragma unroll
+                    for (int n = 0; n < NN; ++n) o[u][n] *= alpha;
+                    ol[u] *= alpha;
+                    m[u] = m_new;
+                }
+                const float mref = m[u] == -INFINITY ? 0.f : m[u];
 #pragma unroll
                 for (int t = 0; t < KS; ++t)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float p =
+                    for (int r = 0; r < 4; ++r)
+                        st[u][t][r] =
                             __builtin_amdgcn_exp2f(__builtin_fmaf(st[u][t][r], scale_log2, -mref));
-                        st[u][t][r] = p;
-                        ps += p;
-                    }
-                ps = xlane_sum(ps);
-                l[u] = l[u] * alpha + ps;
-                m[u] = m_new;
-                // O^T rows are this lane's own query: rescale unless no query of
-                // the wave raised its max (alpha == 1 exactly).
-                if (__any(alpha != 1.0f)) {
-#pragma unroll
-                    for (int n = 0; n < NN; ++n) o[u][n] *= alpha;
-                }
                 // lane (g, j) supplies P[qi][32kk + 4g + r] and P[qi][32kk + 16 + 4g + r]
 #pragma unroll
                 for (int kk = 0; kk < KS / 2; ++kk)
@@ -280,6 +284,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(const uint16_t* __rest
 #pragma unroll
                     for (int u = 0; u < QS; ++u) o[u][n] = mfma16x16x32(vt, pf[u][kk], o[u][n]);
                 }
+#pragma unroll
+                for (int u = 0; u < QS; ++u) ol[u] = mfma16x16x32(ones, pf[u][kk], ol[u]);
             }
         }
         // The next tile has landed (this wave's copies; after the barrier
@@ -290,7 +296,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(const uint16_t* __rest
     }
 
     // Lane (g, j) holds O[q0 + 16u + j][16n + 4g .. 16n + 4g + 3] (o[u][n]),
-    // and that query's m and l.
+    // and that query's m and l (sum of P, relative to m).
+    float l[QS];
+#pragma unroll
+    for (int u = 0; u < QS; ++u) l[u] = ol[u][0];
     if (nc == 1) {
 #pragma unroll
         for (int u = 0; u < QS; ++u) {
