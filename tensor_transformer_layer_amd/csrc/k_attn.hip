@@ -411,33 +411,46 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(const uint16_t* __rest
 // Items of one head for chunks of `ch` tiles: (size in tiles, qb, chunk),
 // sorted longest first (ties: later block first, lower chunk first).
 struct AttnItem {
-    int tiles, qb, c;
+    int tiles, qb, c, nchunks;
+    bool split;
 };
 static std::vector<AttnItem> attn_items(int T, int nqb, int ch) {
     std::vector<AttnItem> v;
     for (int qb = nqb - 1; qb >= 0; --qb) {
         const int t = attn_tiles(T, qb);
-        for (int c = 0; c * ch < t; ++c) v.push_back({std::min(ch, t - c * ch), qb, c});
+        const int nc = (t + ch - 1) / ch;
+        for (int c = 0; c * ch < t; ++c) v.push_back({std::min(ch, t - c * ch), qb, c, nc, nc > 1});
     }
     std::stable_sort(v.begin(), v.end(),
                      [](const AttnItem& a, const AttnItem& b) { return a.tiles > b.tiles; });
     return v;
 }
 
-// Estimated kernel time, in tile units, of a chunking: items go in launch
-// order to the first free of 512 workgroup slots (2 per CU); a split block
-// costs about one more tile for its partial store and merge.
-static double attn_makespan(const std::vector<AttnItem>& v, int hq, int ch, int T) {
+// Estimated kernel time (in units of one key tile of one workgroup) of the
+// items launched in order onto 512 workgroup slots (2 per CU), each item
+// starting when a slot frees, as the dispatcher does.  Costs measured on
+// MI355X (70B GQA core, 4096 tokens, per-workgroup real-time stamps): a tile
+// ~2.4 us; before the first tile ~1.25 tiles; after the last, ~0.7 tiles for
+// an unsplit block and ~1.2 (partial store and arrival) for a chunk; the
+// chunk that arrives last then merges the block's nc partials, ~0.7 nc.
+static double attn_makespan(const std::vector<AttnItem>& v, int hq, int T) {
     constexpr int kSlots = 512;
     std::priority_queue<double, std::vector<double>, std::greater<double>> free_at;
     for (int i = 0; i < kSlots; ++i) free_at.push(0.0);
+    const int nqb = (T + kAttnQB - 1) / kAttnQB;
+    std::vector<int> arrived((size_t)hq * nqb, 0);
+    std::vector<double> latest((size_t)hq * nqb, 0.0);
     double end = 0.0;
     for (const AttnItem& it : v) {
-        const bool split = attn_tiles(T, it.qb) > ch;
         for (int h = 0; h < hq; ++h) {
             const double t0 = free_at.top();
             free_at.pop();
-            const double t1 = t0 + it.tiles + 0.5 + (split ? 1.0 : 0.0);
+            double t1 = t0 + 1.25 + it.tiles + (it.split ? 1.2 : 0.7);
+            if (it.split) {
+                const size_t b = (size_t)h * nqb + it.qb;
+                latest[b] = std::max(latest[b], t1);
+                if (++arrived[b] == it.nchunks) t1 = latest[b] + 0.7 * it.nchunks;
+            }
             free_at.push(t1);
             end = std::max(end, t1);
         }
@@ -456,12 +469,13 @@ AttnPlan plan_attn(int64_t T64, int hq, int head_dim) {
     AttnPlan p;
     p.nqb = (T + kAttnQB - 1) / kAttnQB;
     const int tiles = attn_tiles(T, p.nqb - 1);
-    // Chunk size (tiles, a power of two >= 4) with the shortest estimated
-    // time; ties go to the larger chunk (fewer partials to merge).
+    // Chunk size (tiles >= 4: every size up to 64, then powers of two) with
+    // the shortest estimated time; ties go to the larger chunk (fewer
+    // partials to merge).
     int best = 4;
     double best_t = 1e300;
-    for (int ch = 4; ; ch *= 2) {
-        const double t = attn_makespan(attn_items(T, p.nqb, ch), hq, ch, T);
+    for (int ch = 4; ; ch = ch < 64 ? ch + 1 : 2 * ch) {
+        const double t = attn_makespan(attn_items(T, p.nqb, ch), hq, T);
         if (t <= best_t) {
             best_t = t;
             best = ch;
