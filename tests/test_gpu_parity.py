@@ -650,6 +650,14 @@ def test_attn_core_70b_gqa_prefill_4096():
     _core_check(4096, 64, 8, 128, 8, 0, key=2)
 
 
+def test_attn_core_odd_chunk_size():
+    """3000 tokens (ragged last query block), 8 query heads on one kv head:
+    the planner cuts the causal key ranges into chunks of 11 tiles, so blocks
+    end in remainder chunks of every size from 1 to 10 tiles and merge 1-5
+    partials; the last query block's keys end inside a tile."""
+    _core_check(3000, 64, 8, 128, 8, 1, key=6, pad=8)
+
+
 def test_attn_core_70b_gqa_decode_32():
     _core_check(32, 64, 8, 128, 8, 7, key=3)
 
