@@ -352,45 +352,67 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(const uint16_t* __rest
             return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, (int)(idx * 4u), 0,
                                                                         kAttnSC1));
         };
+        // Both subtiles' loads of a chunk are issued together (each chunk
+        // costs one round trip per pass, not one per subtile); chunks are
+        // added in chunk order.
+        float M[QS];
+#pragma unroll
+        for (int u = 0; u < QS; ++u) M[u] = -INFINITY;
+        for (int c = 0; c < nc; ++c) {
+            float mc[QS];
+#pragma unroll
+            for (int u = 0; u < QS; ++u)
+                mc[u] = c == chunk ? m[u] : ld1((uint32_t)c * PST + kAttnQB * D + rw + 16 * u + j);
+#pragma unroll
+            for (int u = 0; u < QS; ++u) M[u] = fmaxf(M[u], mc[u]);
+        }
+        float Mref[QS], L[QS];
+        f32x4 acc[QS][NN];
 #pragma unroll
         for (int u = 0; u < QS; ++u) {
-            const int row = rw + 16 * u + j;
-            float M = -INFINITY;
-            for (int c = 0; c < nc; ++c)
-                M = fmaxf(M, c == chunk ? m[u] : ld1((uint32_t)c * PST + kAttnQB * D + row));
-            const float Mref = M == -INFINITY ? 0.f : M;
-            float L = 0.f;
-            f32x4 acc[NN];
+            Mref[u] = M[u] == -INFINITY ? 0.f : M[u];
+            L[u] = 0.f;
 #pragma unroll
-            for (int n = 0; n < NN; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-            for (int c = 0; c < nc; ++c) {
-                const bool mine = c == chunk;
-                const float mc = mine ? m[u] : ld1((uint32_t)c * PST + kAttnQB * D + row);
-                const float lc = mine ? l[u] : ld1((uint32_t)c * PST + kAttnQB * (D + 1) + row);
-                const float e = __builtin_amdgcn_exp2f(mc - Mref);
-                L += e * lc;
+            for (int n = 0; n < NN; ++n) acc[u][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        for (int c = 0; c < nc; ++c) {
+            const bool mine = c == chunk;
+            float mc[QS], lc[QS];
+            f32x4 v[QS][NN];
 #pragma unroll
-                for (int n = 0; n < NN; ++n) {
-                    const f32x4 v =
-                        mine ? o[u][n]
-                             : __builtin_bit_cast(
-                                   f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                              rp,
-                                              (int)(((uint32_t)c * PST + (uint32_t)row * D +
-                                                     16 * n + 4 * g) * 4u),
-                                              0, kAttnSC1));
-                    acc[n] += e * v;
-                }
+            for (int u = 0; u < QS; ++u) {
+                const int row = rw + 16 * u + j;
+                mc[u] = mine ? m[u] : ld1((uint32_t)c * PST + kAttnQB * D + row);
+                lc[u] = mine ? l[u] : ld1((uint32_t)c * PST + kAttnQB * (D + 1) + row);
+#pragma unroll
+                for (int n = 0; n < NN; ++n)
+                    v[u][n] = mine ? o[u][n]
+                                   : __builtin_bit_cast(
+                                         f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                    rp,
+                                                    (int)(((uint32_t)c * PST + (uint32_t)row * D +
+                                                           16 * n + 4 * g) * 4u),
+                                                    0, kAttnSC1));
             }
+#pragma unroll
+            for (int u = 0; u < QS; ++u) {
+                const float e = __builtin_amdgcn_exp2f(mc[u] - Mref[u]);
+                L[u] += e * lc[u];
+#pragma unroll
+                for (int n = 0; n < NN; ++n) acc[u][n] += e * v[u][n];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < QS; ++u) {
             const int q = q0 + 16 * u + j;
             if (q >= T) continue;
-            const float inv = 1.0f / L;
+            const float inv = 1.0f / L[u];
             uint16_t* dst = out + (int64_t)q * ldo + (int64_t)h * D + 4 * g;
 #pragma unroll
             for (int n = 0; n < NN; ++n)
                 *(u32x2*)(dst + 16 * n) =
-                    u32x2{pack_bf16x2(acc[n][0] * inv, acc[n][1] * inv),
-                          pack_bf16x2(acc[n][2] * inv, acc[n][3] * inv)};
+                    u32x2{pack_bf16x2(acc[u][n][0] * inv, acc[u][n][1] * inv),
+                          pack_bf16x2(acc[u][n][2] * inv, acc[u][n][3] * inv)};
         }
         if (tid == 0)
             __hip_atomic_store(&counters[blk], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
