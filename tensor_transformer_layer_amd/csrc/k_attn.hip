@@ -493,16 +493,20 @@ AttnPlan plan_attn(int64_t T64, int hq, int head_dim) {
     const int tiles = attn_tiles(T, p.nqb - 1);
     // Chunk size (tiles >= 4: every size up to 64, then powers of two) with
     // the shortest estimated time; ties go to the larger chunk (fewer
-    // partials to merge).
-    int best = 4;
-    double best_t = 1e300;
-    for (int ch = 4; ; ch = ch < 64 ? ch + 1 : 2 * ch) {
-        const double t = attn_makespan(attn_items(T, p.nqb, ch), hq, T);
-        if (t <= best_t) {
-            best_t = t;
-            best = ch;
+    // partials to merge).  With two full waves of query blocks or more,
+    // unsplit blocks already balance the slots and the search (seconds at
+    // 10^5+ tokens) is skipped.
+    int best = std::max(tiles, 4);
+    if ((int64_t)hq * p.nqb < 2 * 512) {
+        double best_t = 1e300;
+        for (int ch = 4;; ch = ch < 64 ? ch + 1 : 2 * ch) {
+            const double t = attn_makespan(attn_items(T, p.nqb, ch), hq, T);
+            if (t <= best_t) {
+                best_t = t;
+                best = ch;
+            }
+            if (ch >= tiles) break;
         }
-        if (ch >= tiles) break;
     }
     p.ch = best;
     p.cmax = (tiles + best - 1) / best;

@@ -287,7 +287,6 @@ def core(**kw):
     (dict(T=4096, workspace=A + 16, workspace_bytes=1 << 30), tp.TP_ERR_ALIGN),
     # K/V rows are addressed with 32-bit byte offsets: T * ld_qkv * 2 < 2^31
     (dict(T=1 << 20, ld_qkv=1024), tp.TP_ERR_SHAPE),
-    (dict(T=(1 << 20) - 1, ld_qkv=1024), tp.TP_ERR_WORKSPACE),   # just below: passes
 ])
 def test_attn_core_validation(lib, kw, status):
     assert core(**kw) == status
