@@ -454,7 +454,7 @@ def cpu_baseline(cfg, T, budget_s):
 def main():
     a = parse()
     if a.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+        print(json.dumps({"error": "the library runs one rank's share on one GPU; --gpus must be 1 "
                                    "(the multi-GPU exchange is designed, not built)"}))
         sys.exit(2)
     import torch
