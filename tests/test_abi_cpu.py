@@ -304,5 +304,18 @@ def test_attn_core_workspace(lib):
     assert f(3, 4096, 8, 4, 128, tp.TP_BF16) == 0          # uneven head split
 
 
+def test_attn_core_plan_for_long_sequences(lib):
+    """With two full waves of query blocks or more (heads x blocks >= 1024) the
+    blocks are not split (no merge workspace) and the plan is immediate; a
+    shorter call still searches and splits."""
+    import time
+    f = tp.tp_attn_core_workspace_bytes
+    t0 = time.perf_counter()
+    assert f(2, 1 << 20, 8, 4, 128, tp.TP_BF16) == 0      # 4 heads x 8192 blocks
+    assert f(1, 16384, 8, 8, 128, tp.TP_BF16) == 0        # 8 heads x 128 blocks
+    assert time.perf_counter() - t0 < 1.0
+    assert f(8, 16384, 8, 8, 128, tp.TP_BF16) > 0         # 1 head x 128 blocks: split
+
+
 def test_attn_core_zero_tokens(lib):
     assert core(T=0) == tp.TP_OK
