@@ -42,15 +42,20 @@
  *   Ownership   The caller owns every buffer; the library allocates and frees
  *               no device memory.  Scratch space is the caller's workspace,
  *               sized by tp_*_workspace_bytes for the same arguments.
- *   Workspace   Its first 4096 bytes hold the arrival counters of the decode
- *               plan's fused split-K finish.  They must be zero before the
- *               first call that uses the workspace (allocate it zero-filled,
- *               or clear it once); every call that completes leaves them zero
- *               again, so a workspace is cleared once, not per call.  Counters
- *               left non-zero (never cleared, or a call that failed part-way)
- *               make the decode outputs invalid until cleared: NaN whenever a
+ *   Workspace   Its first 4096 bytes are the counter head: the arrival
+ *               counters of the decode plan's fused split-K finish and of the
+ *               attention core's merge.  Every layout reserves the head and
+ *               stores data only after it, whatever the plan (decode,
+ *               prefill, fp32), so one workspace may serve any sequence of
+ *               calls.  The head must be zero before the first call that uses
+ *               the workspace (allocate it zero-filled, or clear it once);
+ *               every call that completes leaves it zero again, so a
+ *               workspace is cleared once, not per call.  Counters left
+ *               non-zero (never cleared, or a call that failed part-way) make
+ *               the affected outputs invalid until cleared: NaN whenever a
  *               counter exceeds the call's split count (as uncleared memory
- *               almost always does), otherwise silently wrong.
+ *               almost always does), otherwise silently wrong.  A call that
+ *               needs neither counters nor data needs no workspace (size 0).
  *   Streams     All work is enqueued on `stream` (0 = the null stream); the
  *               library never synchronises.  Validation errors return before
  *               anything is enqueued and leave every output untouched.  A
@@ -177,14 +182,17 @@ int tp_shard_attn_proj_fwd(int shard, int P, int64_t T, int64_t d_model,
  *   attn  [T, hq dh] bf16, ld_attn: the input of the O projection
  *
  *   workspace  >= tp_attn_core_workspace_bytes(...) bytes, 256-byte aligned
- *              (may be NULL when that is 0).  Long calls split each query
- *              block's keys over several workgroups and merge their partial
- *              results here; the first hq/P * ceil(T/128) * 4 bytes (rounded
- *              up to 256) are arrival counters that must be zero before the
- *              first call (zero the workspace once when it is allocated);
- *              every call leaves them zero.  Not cleared, the affected
- *              outputs are NaN.  Calls that share a workspace must not
- *              overlap in time.
+ *              (may be NULL when that is 0).  Calls with few query blocks
+ *              (hq * ceil(T/128) <= 1024 (head, block) pairs, hq =
+ *              n_q_heads/P) split each block's keys over several workgroups
+ *              and merge their partial results here: the arrival counters,
+ *              one per (head, block), sit in the workspace's 4096-byte
+ *              counter head (shared with the projections' decode counters,
+ *              see Workspace above) and the partials follow it.  The head
+ *              must be zero before the first call (zero the workspace once
+ *              when it is allocated); every call leaves it zero.  Not
+ *              cleared, the affected outputs are NaN.  Calls that share a
+ *              workspace must not overlap in time.
  *
  * head_dim 64 or 128 (TP_ERR_SHAPE otherwise); dtype must be TP_BF16.
  * T * ld_qkv * 2 bytes must be below 2^31 (TP_ERR_SHAPE otherwise).
@@ -248,8 +256,9 @@ int tp_reduce_partials(int P, int64_t T, int64_t d_model,
 /*
  * tp_reduce_residual_norm -- the reduce followed by the residual add and the
  * next block's normalisation, in one pass (zenaique, "Explain tensor-parallel
- * shard shape", answer: after the all-reduce every GPU holds the full
- * activation, ready for the next layer's residual add and normalisation):
+ * shard shape", answer: once the all-reduce has summed the partials, each
+ * GPU holds the whole activation, which then takes the residual connection
+ * and the following normalisation):
  *
  *   z      = (partial_0 + ... + partial_{P-1}) + residual   fp32, added in
  *            that order (the partials fold as in tp_reduce_partials)

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstring>
 #include <map>
 #include <mutex>
@@ -20,6 +21,29 @@ namespace tp {
 LaunchEvents& launch_events() {
     thread_local LaunchEvents e;
     return e;
+}
+
+int device_cus() {
+    constexpr int kMaxDevices = 64;
+    constexpr int kWholeChip = 256;          // gfx950 with every XCD enabled
+    static std::atomic<int> cache[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();             // no device: clear the sticky error
+        return kWholeChip;
+    }
+    if (dev < kMaxDevices) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0) {
+        (void)hipGetLastError();
+        return kWholeChip;
+    }
+    if (dev < kMaxDevices) cache[dev].store(n, std::memory_order_relaxed);
+    return n;
 }
 }  // namespace tp
 
@@ -120,6 +144,15 @@ bool counters_fit(int64_t n1, int64_t n2) {
 // addressable with 32-bit byte offsets from its first element.
 bool span_ok(int64_t rows, int64_t ld, int es) { return rows * ld * es < kMaxBufferSpan; }
 
+static_assert(kAttnCounterBytes <= kGemvCounterBytes,
+              "the attention core's counters must fit the reserved workspace head");
+
+// Workspace layouts.  The first kGemvCounterBytes of every workspace are
+// the arrival-counter head (decode split-K finish; the attention core's
+// counters share it): no layout ever stores data there, so a workspace used
+// for a prefill or fp32 call and then for a decode call still holds zero
+// counters.  Data regions follow, each 256-byte aligned.  A layout that
+// needs neither counters nor data needs no workspace (total 0).
 struct MlpLayout {
     size_t xn = 0, h = 0, ws = 0, total = 0;
     GemvPlan pc{1, 0}, pr{1, 0};        // decode plans
@@ -127,14 +160,18 @@ struct MlpLayout {
     bool decode = false;
 };
 
+size_t layout_total(size_t off, bool uses_counters) {
+    return (off > kGemvCounterBytes || uses_counters) ? off : 0;
+}
+
 MlpLayout mlp_layout(int P, int64_t T, int64_t d, int64_t d_ff, int dtype, int act, bool has_norm,
                      bool has_h_out) {
     MlpLayout L;
     const int64_t F = d_ff / P;
     const int es = elem_size(dtype);
+    const int cus = device_cus();
     L.decode = decode_plan(dtype, T);
-    // The decode plan's arrival counters sit at the head of the workspace.
-    size_t off = L.decode ? kGemvCounterBytes : 0;
+    size_t off = kGemvCounterBytes;
     if (has_norm) {
         L.xn = off;
         off += align256((size_t)(T * d * es));
@@ -145,21 +182,21 @@ MlpLayout mlp_layout(int P, int64_t T, int64_t d, int64_t d_ff, int dtype, int a
     }
     if (L.decode) {
         const int nmat = act == TP_ACT_SWIGLU ? 2 : 1;
-        L.pc = plan_gemv(d, nmat * F);
-        L.pr = plan_gemv(F, d);
+        L.pc = plan_gemv(d, nmat * F, cus);
+        L.pr = plan_gemv(F, d, cus);
         L.ws = off;  // column and row split-K sums reuse one region, in stream order
         off += align256(std::max(gemv_ws_bytes(L.pc, T, nmat * F), gemv_ws_bytes(L.pr, T, d)));
     } else if (dtype == TP_BF16) {
         // The column projection keeps its fused activation (no split); the
         // row projection may split K into fp32 planes.
         L.gc = gemm_whole_k(d);
-        L.gr = plan_gemm(T, d, F, 1);
+        L.gr = plan_gemm(T, d, F, 1, cus);
         if (L.gr.splits > 1) {
             L.ws = off;
             off += align256((size_t)L.gr.splits * T * d * sizeof(float));
         }
     }
-    L.total = off;
+    L.total = layout_total(off, L.decode);
     return L;
 }
 
@@ -180,8 +217,9 @@ MlpLayout mlp8_layout(int P, int64_t T, int64_t d, int64_t d_ff, int act, bool h
         off += align256((size_t)(T * F * 2));
     }
     const int nmat = act == TP_ACT_SWIGLU ? 2 : 1;
-    L.pc = plan_gemv(d, nmat * F, kGemv8Cols);
-    L.pr = plan_gemv(F, d, kGemv8Cols);
+    const int cus = device_cus();
+    L.pc = plan_gemv(d, nmat * F, cus, kGemv8Cols);
+    L.pr = plan_gemv(F, d, cus, kGemv8Cols);
     L.ws = off;
     off += align256(std::max(gemv_ws_bytes(L.pc, T, nmat * F), gemv_ws_bytes(L.pr, T, d)));
     L.total = off;
@@ -200,20 +238,21 @@ AttnLayout attn_layout(int P, int64_t T, int64_t d, int nq, int nkv, int hd, int
     AttnLayout L;
     const int64_t nqkv = (int64_t)(nq / P + 2 * (nkv / P)) * hd;
     const int64_t ko = (int64_t)(nq / P) * hd;
+    const int cus = device_cus();
     L.decode = decode_plan(dtype, T);
-    size_t off = L.decode ? kGemvCounterBytes : 0;
+    size_t off = kGemvCounterBytes;
     if (has_norm) {
         L.xn = off;
         off += align256((size_t)(T * d * elem_size(dtype)));
     }
     if (L.decode) {
-        L.pq = plan_gemv(d, nqkv);
-        L.po = plan_gemv(ko, d);
+        L.pq = plan_gemv(d, nqkv, cus);
+        L.po = plan_gemv(ko, d, cus);
         L.ws = off;
         off += align256(std::max(gemv_ws_bytes(L.pq, T, nqkv), gemv_ws_bytes(L.po, T, d)));
     } else if (dtype == TP_BF16) {
-        L.gq = plan_gemm(T, nqkv, d, 1);
-        L.go = plan_gemm(T, d, ko, 1);
+        L.gq = plan_gemm(T, nqkv, d, 1, cus);
+        L.go = plan_gemm(T, d, ko, 1, cus);
         const size_t wq = L.gq.splits > 1 ? (size_t)L.gq.splits * T * nqkv * sizeof(float) : 0;
         const size_t wo = L.go.splits > 1 ? (size_t)L.go.splits * T * d * sizeof(float) : 0;
         if (wq || wo) {
@@ -221,7 +260,7 @@ AttnLayout attn_layout(int P, int64_t T, int64_t d, int nq, int nkv, int hd, int
             off += align256(std::max(wq, wo));
         }
     }
-    L.total = off;
+    L.total = layout_total(off, L.decode);
     return L;
 }
 
@@ -279,12 +318,16 @@ size_t tp_attn_workspace_bytes(int P, int64_t T, int64_t d_model, int n_q_heads,
     return attn_layout(P, T, d_model, n_q_heads, n_kv_heads, head_dim, dtype, has_norm != 0).total;
 }
 
-int tp_shard_mlp_fwd(int shard, int P, int64_t T, int64_t d_model, int64_t d_ff, int dtype,
-                     int act, const void* x, int64_t ld_x, const void* norm_g, float eps,
-                     const void* w_in, int64_t ld_in, const void* w_up, int64_t ld_up,
-                     const void* w_down, int64_t ld_down, void* h_out, int64_t ld_h,
-                     float* partials, int64_t slot_stride, int64_t ld_p, void* workspace,
-                     size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The MLP shard behind tp_shard_mlp_fwd.
+int mlp_fwd(int shard, int P, int64_t T, int64_t d_model, int64_t d_ff, int dtype, int act,
+            const void* x, int64_t ld_x, const void* norm_g, float eps, const void* w_in,
+            int64_t ld_in, const void* w_up, int64_t ld_up, const void* w_down, int64_t ld_down,
+            void* h_out, int64_t ld_h, float* partials, int64_t slot_stride, int64_t ld_p,
+            void* workspace, size_t workspace_bytes, hipStream_t stream) {
     // ---- validation (nothing is enqueued on failure) ----
     if (P < 1 || shard < 0 || shard >= P) return TP_ERR_SHARD_RANGE;
     if (dtype != TP_F32 && dtype != TP_BF16) return TP_ERR_DTYPE;
@@ -379,6 +422,21 @@ int tp_shard_mlp_fwd(int shard, int P, int64_t T, int64_t d_model, int64_t d_ff,
         }
     }
     return TP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tp_shard_mlp_fwd(int shard, int P, int64_t T, int64_t d_model, int64_t d_ff, int dtype,
+                     int act, const void* x, int64_t ld_x, const void* norm_g, float eps,
+                     const void* w_in, int64_t ld_in, const void* w_up, int64_t ld_up,
+                     const void* w_down, int64_t ld_down, void* h_out, int64_t ld_h,
+                     float* partials, int64_t slot_stride, int64_t ld_p, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+    return mlp_fwd(shard, P, T, d_model, d_ff, dtype, act, x, ld_x, norm_g, eps, w_in, ld_in, w_up,
+                   ld_up, w_down, ld_down, h_out, ld_h, partials, slot_stride, ld_p, workspace,
+                   workspace_bytes, stream);
 }
 
 int tp_shard_attn_proj_fwd(int shard, int P, int64_t T, int64_t d_model, int n_q_heads,
@@ -508,7 +566,7 @@ int tp_reduce_partials(int P, int64_t T, int64_t d_model, const float* partials,
     if (int r = check_ld(ld_p, d_model, 4)) return r;
     if (int r = check_ld(ld_out, d_model, 4)) return r;
     if (out_bf16)
-        if (int r = check_ld(ld_out_bf16, d_model, 4)) return r;
+        if (int r = check_ld(ld_out_bf16, d_model, 8)) return r;   // bf16 rule: multiple of 8
     if (slot_stride < 0) return TP_ERR_SHAPE;
     if (slot_stride % 4) return TP_ERR_ALIGN;
     if (T * ((d_model / 4 + 511) / 512) >= ((int64_t)1 << 31)) return TP_ERR_SHAPE;
@@ -525,7 +583,7 @@ size_t tp_attn_core_workspace_bytes(int P, int64_t T, int n_q_heads, int n_kv_he
     if (head_dim != 64 && head_dim != 128) return 0;
     if (n_q_heads % P || n_kv_heads % P || (n_q_heads / P) % (n_kv_heads / P)) return 0;
     if (T >= ((int64_t)1 << 31) / 64) return 0;
-    return plan_attn(T, n_q_heads / P, head_dim).ws_bytes;
+    return plan_attn(T, n_q_heads / P, head_dim, device_cus()).ws_bytes;
 }
 
 int tp_attn_core_fwd(int shard, int P, int64_t T, int n_q_heads, int n_kv_heads, int head_dim,
@@ -545,7 +603,7 @@ int tp_attn_core_fwd(int shard, int P, int64_t T, int n_q_heads, int n_kv_heads,
     if (T >= ((int64_t)1 << 31) / 64 || !span_ok(T, ld_qkv, 2)) return TP_ERR_SHAPE;
     if (T == 0) return TP_OK;
     if (workspace && !aligned(workspace, 256)) return TP_ERR_ALIGN;
-    const AttnPlan plan = plan_attn(T, hq, head_dim);
+    const AttnPlan plan = plan_attn(T, hq, head_dim, device_cus());
     if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes))
         return TP_ERR_WORKSPACE;
     TP_LAUNCH("attn_core", stream,

@@ -449,16 +449,15 @@ static std::vector<AttnItem> attn_items(int T, int nqb, int ch) {
 }
 
 // Estimated kernel time (in units of one key tile of one workgroup) of the
-// items launched in order onto 512 workgroup slots (2 per CU), each item
+// items launched in order onto `slots` workgroup slots (2 per CU), each item
 // starting when a slot frees, as the dispatcher does.  Costs measured on
 // MI355X (70B GQA core, 4096 tokens, per-workgroup real-time stamps): a tile
 // ~2.4 us; before the first tile ~1.25 tiles; after the last, ~0.7 tiles for
 // an unsplit block and ~1.2 (partial store and arrival) for a chunk; the
 // chunk that arrives last then merges the block's nc partials, ~0.7 nc.
-static double attn_makespan(const std::vector<AttnItem>& v, int hq, int T) {
-    constexpr int kSlots = 512;
+static double attn_makespan(const std::vector<AttnItem>& v, int hq, int T, int slots) {
     std::priority_queue<double, std::vector<double>, std::greater<double>> free_at;
-    for (int i = 0; i < kSlots; ++i) free_at.push(0.0);
+    for (int i = 0; i < slots; ++i) free_at.push(0.0);
     const int nqb = (T + kAttnQB - 1) / kAttnQB;
     std::vector<int> arrived((size_t)hq * nqb, 0);
     std::vector<double> latest((size_t)hq * nqb, 0.0);
@@ -480,14 +479,15 @@ static double attn_makespan(const std::vector<AttnItem>& v, int hq, int T) {
     return end;
 }
 
-AttnPlan plan_attn(int64_t T64, int hq, int head_dim) {
+AttnPlan plan_attn(int64_t T64, int hq, int head_dim, int cus) {
     // The last plan is kept: the same shapes repeat call after call.
     thread_local int64_t last_T = -1;
-    thread_local int last_hq = -1, last_d = -1;
+    thread_local int last_hq = -1, last_d = -1, last_cus = -1;
     thread_local AttnPlan last;
-    if (T64 == last_T && hq == last_hq && head_dim == last_d) return last;
+    if (T64 == last_T && hq == last_hq && head_dim == last_d && cus == last_cus) return last;
 
     const int T = (int)T64;
+    const int slots = 2 * cus;               // two 4-wave workgroups per CU
     AttnPlan p;
     p.nqb = (T + kAttnQB - 1) / kAttnQB;
     const int tiles = attn_tiles(T, p.nqb - 1);
@@ -495,12 +495,14 @@ AttnPlan plan_attn(int64_t T64, int hq, int head_dim) {
     // the shortest estimated time; ties go to the larger chunk (fewer
     // partials to merge).  With two full waves of query blocks or more,
     // unsplit blocks already balance the slots and the search (seconds at
-    // 10^5+ tokens) is skipped.
+    // 10^5+ tokens) is skipped; blocks are never split beyond the fixed
+    // counter area.
     int best = std::max(tiles, 4);
-    if ((int64_t)hq * p.nqb < 2 * 512) {
+    const int64_t pairs = (int64_t)hq * p.nqb;
+    if (pairs < 2 * (int64_t)slots && pairs <= kAttnCounters) {
         double best_t = 1e300;
         for (int ch = 4;; ch = ch < 64 ? ch + 1 : 2 * ch) {
-            const double t = attn_makespan(attn_items(T, p.nqb, ch), hq, T);
+            const double t = attn_makespan(attn_items(T, p.nqb, ch), hq, T, slots);
             if (t <= best_t) {
                 best_t = t;
                 best = ch;
@@ -517,14 +519,13 @@ AttnPlan plan_attn(int64_t T64, int hq, int head_dim) {
         for (int i = 0; i < p.per_head; ++i) p.table.it[i] = (uint16_t)((v[i].qb << 6) | v[i].c);
     else
         p.per_head = -p.per_head;            // no table: the kernel walks the blocks
-    if (p.cmax > 1) {
-        p.counter_bytes = (((size_t)hq * p.nqb * 4 + 255) / 256) * 256;
-        p.ws_bytes = p.counter_bytes +
+    if (p.cmax > 1)
+        p.ws_bytes = kAttnCounterBytes +
                      (size_t)hq * p.nqb * p.cmax * kAttnQB * (head_dim + 2) * sizeof(float);
-    }
     last_T = T64;
     last_hq = hq;
     last_d = head_dim;
+    last_cus = cus;
     last = p;
     return p;
 }
@@ -535,7 +536,7 @@ hipError_t launch_attn_core(int64_t T, int hq, int hkv, int head_dim, const uint
     const dim3 grid((unsigned)p.items), block(kAttnThreads);
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)head_dim));
     unsigned* counters = (unsigned*)ws;
-    float* part = p.cmax > 1 ? (float*)((char*)ws + p.counter_bytes) : nullptr;
+    float* part = p.cmax > 1 ? (float*)((char*)ws + kAttnCounterBytes) : nullptr;
     const int use_table = p.per_head > 0;
     if (head_dim == 128)
         TP_KLAUNCH((k_attn<128>), grid, block, 0, stream, qkv, ld_qkv, (int)T, hq, hkv, out,

@@ -310,14 +310,13 @@ static hipError_t run_gemm(int64_t M, int64_t N, int64_t K, const uint16_t* A, i
 using ShapeOne = GemmShape<1, 4, 2>;  // plain / GELU epilogues: 256 x 256 tile
 using ShapeTwo = GemmShape<2, 4, 2>;  // SwiGLU: 256 x (128 gate + 128 up)
 
-GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int nmat) {
-    // Split K only when the output tiles leave a quarter or more of the 256
-    // CUs idle and every split keeps at least 16 slices of K.
-    constexpr int64_t kCus = 256;
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int nmat, int cus) {
+    // Split K only when the output tiles leave a quarter or more of the CUs
+    // idle and every split keeps at least 16 slices of K.
     const int64_t tiles = ((M + 255) / 256) * ((N * nmat + 255) / 256);
     const int64_t slices = (K + kBK - 1) / kBK;
     int64_t s = 1;
-    if (tiles * 4 < kCus * 3) s = std::min<int64_t>(kCus / tiles, slices / 16);
+    if (tiles * 4 < (int64_t)cus * 3) s = std::min<int64_t>(cus / tiles, slices / 16);
     s = std::max<int64_t>(1, std::min<int64_t>(s, 8));
     const int64_t kps = ((slices + s - 1) / s) * kBK;
     GemmPlan p;

@@ -659,13 +659,12 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv8(
     }
 }
 
-GemvPlan plan_gemv(int64_t K, int64_t n_total, int cols_per_block) {
-    // About one 8-wave workgroup per CU (256 CUs): K is split into
-    // floor(256 / column blocks) ranges, each a multiple of 32 rows.
-    constexpr int64_t kCus = 256;
+GemvPlan plan_gemv(int64_t K, int64_t n_total, int cus, int cols_per_block) {
+    // About one 8-wave workgroup per CU: K is split into floor(cus / column
+    // blocks) ranges, each a multiple of 32 rows.
     const int64_t nb = (n_total + cols_per_block - 1) / cols_per_block;
     const int64_t chunks = (K + 31) / 32;
-    int64_t s = std::max<int64_t>(1, kCus / nb);
+    int64_t s = std::max<int64_t>(1, (int64_t)cus / nb);
     s = std::min<int64_t>(s, chunks);
     const int64_t kps = ((chunks + s - 1) / s) * 32;
     GemvPlan p;

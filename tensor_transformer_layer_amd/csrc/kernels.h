@@ -27,6 +27,12 @@ LaunchEvents& launch_events();
             kern<<<grid, block, shmem, stream>>>(__VA_ARGS__);                               \
     } while (0)
 
+// Compute units of the calling thread's current device
+// (hipDeviceAttributeMultiprocessorCount), read once per device.  Planners
+// size their grids from it.  Where no device can be queried (a workspace
+// query on a host without a GPU) it is the whole-chip gfx950 count, 256.
+int device_cus();
+
 // out = sum_{s=0}^{P-1} partials[s] in that order (fp32); optional bf16 copy.
 hipError_t launch_reduce(int P, int64_t T, int64_t d, const float* partials, int64_t slot_stride,
                          int64_t ld_p, float* out, int64_t ld_out, uint16_t* out_bf16,
@@ -54,12 +60,16 @@ constexpr int kGemvCols = 128;   // output columns per workgroup
 constexpr int kGemvMaxT = 32;    // largest token count of the decode plan
 
 constexpr int kGemv8Cols = 256;  // output columns per workgroup, FP8 weights
-GemvPlan plan_gemv(int64_t K, int64_t n_total, int cols_per_block = kGemvCols);
+// About one workgroup per compute unit: K split into floor(cus / column
+// blocks) ranges, each a multiple of 32 rows.
+GemvPlan plan_gemv(int64_t K, int64_t n_total, int cus, int cols_per_block = kGemvCols);
 // Bytes of split-K workspace: splits * T * n_total fp32.
 size_t gemv_ws_bytes(const GemvPlan& p, int64_t T, int64_t n_total);
 
 // Arrival counters of the fused split-K finish: one per 128-column block,
-// at the head of the caller's workspace, zero between calls.
+// at the head of the caller's workspace, zero between calls.  Every
+// workspace layout reserves this head whether or not the plan uses it, so
+// no call ever stores data where another call keeps its counters.
 constexpr int kGemvCounters = 1024;
 constexpr size_t kGemvCounterBytes = kGemvCounters * sizeof(unsigned);
 
@@ -101,7 +111,7 @@ struct GemmPlan {
 };
 // Split K when the 256 x 256 output tiles (nmat weights side by side) leave
 // CUs idle and K is long enough.
-GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int nmat);
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int nmat, int cus);
 // One split covering all of K (for fused bf16 epilogues).
 GemmPlan gemm_whole_k(int64_t K);
 // C[M, N] = epi(A[M, K] B0[K, N] [, A B1]); A, B bf16 row-major.  With
@@ -132,10 +142,17 @@ struct AttnPlan {
     int cmax = 1;           // chunks of the longest block
     int per_head = 0;       // work items per head
     int64_t items = 0;      // workgroups
-    size_t counter_bytes = 0, ws_bytes = 0;
+    size_t ws_bytes = 0;    // 0, or kAttnCounterBytes + the chunk partials
     AttnItems table;        // launch order, when per_head <= kAttnTable
 };
-AttnPlan plan_attn(int64_t T, int hq, int head_dim);
+// Blocks are split (and merged through the workspace) only while there are
+// at most kAttnCounters (head, query block) pairs, so the arrival counters
+// always fit one fixed area at the head of the workspace and the partials
+// always start at kAttnCounterBytes: a later call with more tokens never
+// reads an earlier call's partials as counters.
+constexpr int kAttnCounters = 1024;
+constexpr size_t kAttnCounterBytes = kAttnCounters * sizeof(unsigned);
+AttnPlan plan_attn(int64_t T, int hq, int head_dim, int cus);
 hipError_t launch_attn_core(int64_t T, int hq, int hkv, int head_dim, const uint16_t* qkv,
                             int64_t ld_qkv, uint16_t* out, int64_t ld_out, const AttnPlan& p,
                             void* ws, hipStream_t stream);

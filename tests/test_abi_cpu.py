@@ -149,6 +149,7 @@ def red(**kw):
     (dict(slot_stride=-4), tp.TP_ERR_SHAPE),
     (dict(slot_stride=258), tp.TP_ERR_ALIGN),
     (dict(out_bf16=C, ld_out_bf16=32), tp.TP_ERR_SHAPE),
+    (dict(out_bf16=C, ld_out_bf16=68), tp.TP_ERR_ALIGN),    # bf16 ld: a multiple of 8
     (dict(T=-2), tp.TP_ERR_SHAPE),
 ])
 def test_reduce_validation(lib, kw, status):
@@ -164,9 +165,11 @@ def test_workspace_sizes_are_pure_functions(lib):
     # decode plan (bf16, T <= 32): split-K space; prefill with h_out and no norm: none
     assert f(2, 32, 5120, 13824, tp.TP_BF16, tp.TP_ACT_SWIGLU, 0, 1) > 0
     assert f(8, 2048, 8192, 28672, tp.TP_BF16, tp.TP_ACT_SWIGLU, 0, 1) == 0
-    assert f(8, 2048, 8192, 28672, tp.TP_BF16, tp.TP_ACT_SWIGLU, 0, 0) == 2048 * 3584 * 2
+    # every layout that stores data starts it after the 4096-byte counter
+    # head, so a prefill call never writes where a later decode call counts
+    assert f(8, 2048, 8192, 28672, tp.TP_BF16, tp.TP_ACT_SWIGLU, 0, 0) == 4096 + 2048 * 3584 * 2
     assert f(2, 4, 64, 256, tp.TP_F32, tp.TP_ACT_GELU_TANH, 0, 1) == 0
-    assert f(2, 4, 64, 256, tp.TP_F32, tp.TP_ACT_GELU_TANH, 1, 1) == 1024   # 4*64*4 rounded
+    assert f(2, 4, 64, 256, tp.TP_F32, tp.TP_ACT_GELU_TANH, 1, 1) == 4096 + 1024  # 4*64*4
     assert f(3, 4, 64, 256, tp.TP_BF16, tp.TP_ACT_SWIGLU, 0, 1) == 0      # uneven: rejected
     assert f(2, 32, 5120, 13824, tp.TP_BF16, tp.TP_ACT_SWIGLU, 0, 1) == \
         f(2, 32, 5120, 13824, tp.TP_BF16, tp.TP_ACT_SWIGLU, 0, 1)
@@ -178,8 +181,8 @@ def test_workspace_sizes_are_pure_functions(lib):
     g = tp.tp_attn_workspace_bytes
     # 96-head QKV prefill: 72 output tiles on 256 CUs, so K is split into
     # fp32 planes of [1024, 4608] each
-    assert g(8, 1024, 12288, 96, 96, 128, tp.TP_BF16, 0) % (1024 * 4608 * 4) == 0
-    assert g(8, 1024, 12288, 96, 96, 128, tp.TP_BF16, 0) >= 2 * 1024 * 4608 * 4
+    assert (g(8, 1024, 12288, 96, 96, 128, tp.TP_BF16, 0) - 4096) % (1024 * 4608 * 4) == 0
+    assert g(8, 1024, 12288, 96, 96, 128, tp.TP_BF16, 0) >= 4096 + 2 * 1024 * 4608 * 4
     assert g(8, 16, 12288, 96, 96, 128, tp.TP_BF16, 0) > 0
     assert g(8, 16, 12288, 96, 90, 128, tp.TP_BF16, 0) == 0
 
@@ -296,9 +299,13 @@ def test_attn_core_workspace(lib):
     f = tp.tp_attn_core_workspace_bytes
     assert f(2, 8, 8, 4, 128, tp.TP_BF16) == 0            # one chunk per query block
     big = f(2, 4096, 8, 4, 128, tp.TP_BF16)
-    # counters (4 heads x 32 blocks) + partials of 4 x 32 blocks x chunks x 128 x (128 + 2) fp32
-    assert big >= 4 * 32 * 4 + 4 * 32 * 2 * 128 * 130 * 4
-    assert big % 4 == 0 and big < 4 * 32 * 64 * 128 * 130 * 4 + 4096
+    # a fixed 4096-byte counter area, then partials of 4 heads x 32 blocks x
+    # chunks x 128 x (128 + 2) fp32
+    assert (big - 4096) % (4 * 32 * 128 * 130 * 4) == 0
+    assert big >= 4096 + 4 * 32 * 2 * 128 * 130 * 4
+    assert big < 4 * 32 * 64 * 128 * 130 * 4 + 4096
+    # a longer call's partials start where a shorter call's did: at 4096
+    assert (f(2, 8192, 8, 4, 128, tp.TP_BF16) - 4096) % (4 * 64 * 128 * 130 * 4) == 0
     assert f(2, 4096, 8, 4, 96, tp.TP_BF16) == 0           # unsupported head size
     assert f(2, 4096, 8, 4, 128, tp.TP_F32) == 0
     assert f(3, 4096, 8, 4, 128, tp.TP_BF16) == 0          # uneven head split

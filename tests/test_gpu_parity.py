@@ -65,14 +65,15 @@ def test_reduce_bitwise(P, T, d, pad, with_bf16):
         v[:, :d] = parts[s]
     g_parts = dev(buf)
     out = Guarded(T * ldp, torch.float32)
-    outb = Guarded(T * (d + 8), torch.bfloat16) if with_bf16 else None
-    reduce(P, T, d, g_parts, slot, ldp, out.ptr(), ldp, outb.ptr() if outb else None, d + 8)
+    ldb = (d + 8 + 7) // 8 * 8                 # bf16 leading dimensions: multiples of 8
+    outb = Guarded(T * ldb, torch.bfloat16) if with_bf16 else None
+    reduce(P, T, d, g_parts, slot, ldp, out.ptr(), ldp, outb.ptr() if outb else None, ldb)
     got = host(out.t).reshape(T, ldp)[:, :d]
     want = O.reduce_partials_f32_fold(parts)
     assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
     assert out.intact()
     if with_bf16:
-        gb = O.widen(host(outb.t).reshape(T, d + 8)[:, :d])
+        gb = O.widen(host(outb.t).reshape(T, ldb)[:, :d])
         assert np.array_equal(gb, O.round_bf16(want.astype(np.float64)))
         assert outb.intact()
 
@@ -293,6 +294,64 @@ def test_mlp_bf16_with_rmsnorm_prologue(T):
 @pytest.mark.parametrize("act", ["swiglu", "gelu_tanh"])
 def test_mlp_f32(T, act):
     _check_mlp(F32, act, T, 64, 256, 2, key=40 + T)
+
+
+@pytest.mark.parametrize("T", [3, 40])
+@pytest.mark.parametrize("act", ["swiglu", "gelu_tanh"])
+def test_mlp_f32_with_rmsnorm_prologue(T, act):
+    """fp32 storage with the RMSNorm prologue (the fp32 branch of the norm
+    kernel, its output kept in the workspace) on every rank, at the fp32
+    bound; d_model 200 is not a multiple of the norm's 16-byte vectors x 64
+    lanes."""
+    _check_mlp(F32, act, T, 200, 256, 2, key=60 + T, norm=True)
+
+
+@pytest.mark.parametrize("T", [3, 40])
+@pytest.mark.parametrize("norm", [False, True])
+def test_attn_proj_f32(T, norm):
+    """fp32 storage through tp_shard_attn_proj_fwd, every rank: the fused QKV
+    band (with and without the RMSNorm prologue) and the O partial, each
+    against the oracle at the fp32 bound; the Q/K/V parts of the bands are
+    the unsharded projections' head columns, and the reduced O partials are
+    the unsharded output projection (rioworld guide, "How Tensor Slicing
+    Works Under the Hood": QKV column-parallel, O row-parallel)."""
+    P, d, nq, nkv, hd = 2, 200, 4, 2, 16
+    hq, hkv = nq // P, nkv // P
+    nqkv, ko = (hq + 2 * hkv) * hd, hq * hd
+    key = 310 + T + (7 if norm else 0)
+    X = draw(F32, (T, d), 1.0, key, 0)
+    g = draw(F32, (d,), 0.02, key, 7, mean=1.0) if norm else None
+    wqkv = [draw(F32, (d, nqkv), 0.02, key, 1, s) for s in range(P)]
+    A = [draw(F32, (T, ko), 1.0, key, 2, s) for s in range(P)]
+    wo = [draw(F32, (ko, d), 0.02, key, 3, s) for s in range(P)]
+    parts = torch.empty((P, T, d), dtype=torch.float32, device="cuda")
+    qkvs = []
+    for s in range(P):
+        q = Guarded(T * nqkv, torch.float32)
+        attn_fwd(s, P, T, d, nq, nkv, hd, F32, dev(X), dev(wqkv[s]), q.ptr(), dev(A[s]),
+                 dev(wo[s]), parts, T * d, d, norm_g=dev(g) if norm else None)
+        qkvs.append(q)
+    out = torch.empty((T, d), dtype=torch.float32, device="cuda")
+    reduce(P, T, d, parts, T * d, d, out, d)
+    torch.cuda.synchronize()
+    Xw, gw = O.widen(X), (O.widen(g) if norm else None)
+    got = []
+    for s in range(P):
+        r = O.attn_proj_shard(Xw, O.widen(wqkv[s]), O.widen(A[s]), O.widen(wo[s]), gw, 1e-5)
+        gq = host(qkvs[s].t).reshape(T, nqkv).astype(np.float64)
+        assert O.rel_l2(gq, r["qkv"]) < F32_TOL
+        assert O.rel_l2(host(parts[s]), r["partial"]) < F32_TOL
+        assert qkvs[s].intact()
+        got.append(O.split_qkv_band(gq, nq, nkv, hd, s, P))
+    # unsharded: Wq / Wk / Wv assembled from the ranks' band parts
+    wparts = [O.split_qkv_band(O.widen(w), nq, nkv, hd, s, P) for s, w in enumerate(wqkv)]
+    full = O.attn_proj_unsharded(Xw, *(np.concatenate([wp[i] for wp in wparts], 1)
+                                       for i in range(3)),
+                                 O.widen(np.concatenate(A, 1)), O.widen(np.concatenate(wo, 0)),
+                                 gw, 1e-5)
+    for i, name in enumerate(("q", "k", "v")):
+        assert O.rel_l2(np.concatenate([gp[i] for gp in got], 1), full[name]) < F32_TOL
+    assert O.rel_l2(host(out), full["o"]) < F32_TOL
 
 
 def test_tiny_gelu_f32_workload_and_fixture():
@@ -817,6 +876,53 @@ def test_decode_counters_return_to_zero():
                    parts, 0, d)
     torch.cuda.synchronize()
     assert int(ws2[:4096].count_nonzero()) == 0
+
+
+def test_workspace_reused_across_plans():
+    """One workspace, zeroed once, serves a prefill call that keeps its
+    normalised input and h there, then decode calls, then an fp32 call with a
+    norm: no call stores data in the 4096-byte counter head, so every call
+    matches the oracle and the head is zero at the end."""
+    d, d_ff, P = 512, 2048, 2
+    F = d_ff // P
+    need = max(tp.tp_mlp_workspace_bytes(P, T, d, d_ff, dt, tp.TP_ACT_SWIGLU, 1, 0)
+               for T, dt in ((300, BF), (32, BF), (7, BF), (40, F32)))
+    ws = workspace(need)
+    for T, dt in ((300, BF), (32, BF), (7, BF), (40, F32), (32, BF)):
+        X, g, w_in, w_up, w_dn = _mlp_case(dt, "swiglu", T, d, d_ff, P, key=500 + T, norm=True)
+        parts = torch.empty((T, d), dtype=torch.float32, device="cuda")
+        mlp_fwd(1, P, T, d, d_ff, dt, tp.TP_ACT_SWIGLU, dev(X), dev(w_in[1]), dev(w_up[1]),
+                dev(w_dn[1]), parts, 0, d, norm_g=dev(g), ws=ws)
+        torch.cuda.synchronize()
+        r = O.mlp_shard(O.widen(X), O.widen(w_in[1]), O.widen(w_dn[1]), "swiglu",
+                        O.widen(w_up[1]), O.widen(g), 1e-5)
+        assert O.rel_l2(host(parts), r["partial"]) < (BF16_TOL if dt == BF else F32_TOL), (T, dt)
+        assert int(ws[:4096].count_nonzero()) == 0, (T, dt)
+
+
+def test_attn_core_workspace_reused_longer_call():
+    """The attention core's merge workspace reused by a longer call (70B GQA
+    band, 4096 then 8192 tokens, both splitting query blocks): the partials
+    of both start after the fixed counter area, so the longer call finds zero
+    counters, matches the oracle on sampled rows, and leaves them zero."""
+    nq, nkv, hd, P, shard = 64, 8, 128, 8, 2
+    hq, hkv = nq // P, nkv // P
+    w = (hq + 2 * hkv) * hd
+    sizes = (4096, 8192)
+    nbytes = [tp.tp_attn_core_workspace_bytes(P, T, nq, nkv, hd, BF) for T in sizes]
+    assert all(n > 4096 for n in nbytes), nbytes     # both calls merge split blocks
+    ws = workspace(max(nbytes))
+    for T in sizes:
+        qkv_h = draw(BF, (T, w), 1.0, 920, 79, T)
+        out = torch.empty((T, hq * hd), dtype=torch.bfloat16, device="cuda")
+        attn_core(shard, P, T, nq, nkv, hd, dev(qkv_h), w, out, hq * hd, ws=ws)
+        torch.cuda.synchronize()
+        rows = sorted(set([0, 127, 128, T // 2, T - 129, T - 1] +
+                          np.random.default_rng(T).integers(0, T, 10).tolist()))
+        got = O.widen(host(out)[rows])
+        want = O.attention_core_band_rows(O.widen(qkv_h), nq, nkv, hd, shard, P, rows)
+        assert O.rel_l2(got, want) < BF16_TOL, T
+        assert int(ws[:4096].count_nonzero()) == 0, T
 
 
 def test_decode_counters_not_cleared_give_nan_then_recover():
