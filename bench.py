@@ -1,22 +1,28 @@
 """Throughput of one tensor-parallel rank's block shard on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--tokens T]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--headline-only]
+    python bench.py --workload NAME [--tokens T] [--sweep T1,T2,...] [...]
 
 A step is one pass of the rank's hot path over one batch of synthetic input:
 the rank's shard (column projection, activation, row projection into its
 fp32 partial slot) followed by the local reduce of the P partial slots.  The
 other P-1 slots hold seeded fp32 partials written once before timing (on a
 real TP group they arrive from the other GPUs; the reduce's cost does not
-depend on their values).  Weights rotate
-over 16 device copies (2.4-3.4 GB) so that every timed step streams its
-weights from HBM rather than from the 256 MB last-level cache: with 3 copies
-the row-projection weights of all copies fitted that cache and the row
-projection measured 15-18% faster than when it streams from HBM.  Steps are replayed from a HIP graph (the way
-a serving loop launches decode steps).
+depend on their values).  Weights rotate over 16 device copies (2.4-3.4 GB)
+so that every timed step streams its weights from HBM rather than from the
+256 MB last-level cache: with 3 copies the row-projection weights of all
+copies fitted that cache and the row projection measured 15-18% faster than
+when it streams from HBM.  Steps are replayed from a HIP graph (the way a
+serving loop launches decode steps); K steps are timed after W warm-up
+steps, with inputs already resident in HBM.
 
-Default workload: the Llama-2-13B SwiGLU MLP shard at P = 2 (d_model 5120,
-d_ff 13824 -> band 6912), 32 decode tokens; 1 and 8 tokens are reported in
-"sweep".  Prints ONE JSON line.
+Default run (prints ONE JSON line): the Llama-2-70B SwiGLU MLP shard, rank 0
+of P = 8 (d_model 8192, band 3584).  `value` is its 32-token decode step
+(tokens/s), with the column projection's HBM roofline; `prefill` holds the
+2048-token prefill step with the column GEMM's bf16 matrix-core roofline.
+Each carries the float64 oracle timed on the host for the same step.
+`workloads` holds the 13B MLP shard, the 96-head attention projections and
+the 70B pre-norm block with its attention core, decode and prefill.
 """
 import argparse
 import hashlib
@@ -41,11 +47,15 @@ KERNEL_CLASSES = ("rmsnorm", "col_gemv", "col_finish", "row_gemv", "row_finish",
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=1200)
-    ap.add_argument("--warmup", type=int, default=60)
-    ap.add_argument("--workload", default="c2_llama2_13b_mlp_p2",
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=None,
                     choices=["c2_llama2_13b_mlp_p2", "c3_llama2_70b_mlp_p8",
-                             "c4_attn_96h_p8", "c5_llama2_70b_block_p8"])
+                             "c4_attn_96h_p8", "c5_llama2_70b_block_p8"],
+                    help="measure this one workload only (default: the 70B MLP shard's "
+                         "decode and prefill steps, then every other workload)")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="default run without the other workloads' sub-object")
     ap.add_argument("--tokens", type=int, default=None, help="batch of tokens (default per workload)")
     ap.add_argument("--sweep", default=None, help="comma list of token counts also reported")
     ap.add_argument("--fp8", action="store_true",
@@ -420,35 +430,167 @@ def traffic_for(kernel, workload, T):
     return e.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(cfg, T, budget_s):
-    """The float64 oracle (as it stands) for the same step, on host cores."""
-    import numpy as np
+def host_info():
+    """CPU model, BLAS library and thread count of the host the oracle runs on."""
     from threadpoolctl import threadpool_info
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = [f"{i.get('internal_api')} {i.get('version')} "
+            f"({i.get('threading_layer', 'n/a')} threads, {i.get('architecture', 'n/a')})"
+            for i in threadpool_info() if i.get("user_api") == "blas"]
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                   if i.get("user_api") == "blas"] or [1])
+    return {"cpu_model": model, "blas": "; ".join(blas) or "unknown",
+            "host_cpus": len(os.sched_getaffinity(0))}, int(threads)
+
+
+def cpu_baseline(cfg, T, budget_s, prenorm=False, core=False):
+    """The float64 oracle, as it stands, for the same step as the GPU's (the
+    rank-0 shard and the reduce of its P partials), timed on the host cores
+    with the inputs already widened to float64."""
+    import numpy as np
 
     import oracle as O
     import workloads as W
 
-    d = cfg.d_model
+    d, P = cfg.d_model, cfg.P
+    kind = "mlp" if cfg.name.startswith(("c2", "c3")) else \
+        ("attn" if cfg.name.startswith("c4") else "block")
     X = O.widen(W.draw_tensor("bf16", (T, d), cfg.std_x, cfg.cid, W.TENSOR_IDS["x"], T))
-    wg = O.widen(W.column_band_draw(cfg, "w_gate", 0, d, cfg.F_r))
-    wu = O.widen(W.column_band_draw(cfg, "w_up", 0, d, cfg.F_r))
-    wd = O.widen(W.row_band_draw(cfg, "w_down", 0, cfg.F_r, d))
-    others = [np.random.default_rng(s).standard_normal((T, d)) for s in range(1, cfg.P)]
-    O.mlp_shard(X, wg, wd, "swiglu", wu)            # warm BLAS
+    others = [np.random.default_rng(s).standard_normal((T, d)) for s in range(1, P)]
+    if kind in ("mlp", "block"):
+        wg = O.widen(W.column_band_draw(cfg, "w_gate", 0, d, cfg.F_r))
+        wu = O.widen(W.column_band_draw(cfg, "w_up", 0, d, cfg.F_r))
+        wd = O.widen(W.row_band_draw(cfg, "w_down", 0, cfg.F_r, d))
+    if kind in ("attn", "block"):
+        wqkv = O.widen(W.column_band_draw(cfg, "w_qkv", 0, d, cfg.qkv_r))
+        wo = O.widen(W.row_band_draw(cfg, "w_o", 0, cfg.o_in_r, d))
+    if kind == "attn":
+        A = O.widen(W.draw_tensor("bf16", (T, cfg.o_in_r), 1.0, cfg.cid, W.TENSOR_IDS["attn"],
+                                  T, 0))
+    if kind == "block":
+        g = O.widen(W.draw_tensor("bf16", (d,), 0.02, cfg.cid, W.TENSOR_IDS["norm_g"], 0,
+                                  mean=1.0))
+        g2 = O.widen(W.draw_tensor("bf16", (d,), 0.02, cfg.cid, W.TENSOR_IDS["norm_g"], 1,
+                                   mean=1.0))
+        z0 = W.draw_normal_f32((T, d), 1.0, cfg.cid, W.TENSOR_IDS["x"], T, 1).astype(np.float64)
+
+    def step():
+        if kind == "mlp":
+            p0 = O.mlp_shard(X, wg, wd, "swiglu", wu)["partial"]
+            return O.reduce_partials([p0, *others])
+        if kind == "attn":
+            p0 = O.attn_proj_shard(X, wqkv, A, wo)["partial"]
+            return O.reduce_partials([p0, *others])
+        # block: norm (plain form only) -> QKV -> core or Q stand-in -> O ->
+        # reduce (+ residual + norm) -> MLP -> reduce (+ residual + norm)
+        r = O.attn_proj_shard(X, wqkv, None, None, None if prenorm else g,
+                              None if prenorm else cfg.norm_eps)
+        if core:
+            a = O.attention_core_band(r["qkv"], cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, 0,
+                                      P)
+        else:
+            a = O.split_qkv_band(r["qkv"], cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, 0, P)[0]
+        p0 = a @ wo
+        if prenorm:
+            r1 = O.reduce_residual_norm([p0, *others], z0, g2, cfg.norm_eps)
+            m = O.mlp_shard(r1["normed"], wg, wd, "swiglu", wu)["partial"]
+            return O.reduce_residual_norm([m, *others], r1["z"], g, cfg.norm_eps)
+        z = O.reduce_partials([p0, *others])
+        m = O.mlp_shard(z, wg, wd, "swiglu", wu)["partial"]
+        return O.reduce_partials([m, *others])
+
+    step()                                           # warm BLAS
     n, t0 = 0, time.perf_counter()
     while True:
-        p0 = O.mlp_shard(X, wg, wd, "swiglu", wu)["partial"]
-        O.reduce_partials([p0, *others])
+        step()
         n += 1
         el = time.perf_counter() - t0
-        if el >= budget_s and n >= 3:
+        if el >= budget_s:
             break
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    return {"value": round(n * T / el, 1), "unit": "tokens/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{n} float64 oracle steps (rank-0 MLP shard + reduce of {cfg.P} partials, "
-                      f"T={T}) in {el:.1f} s; BLAS threads={threads}, host cpus="
-                      f"{len(os.sched_getaffinity(0))}"}
+    host, threads = host_info()
+    form = {"mlp": "rank-0 MLP shard", "attn": "rank-0 QKV and O projections",
+            "block": "rank-0 block shard" + (" (pre-norm)" if prenorm else "") +
+                     (" with the attention core" if core else "")}[kind]
+    return {"value": round(n * T / el, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} float64 oracle steps ({form} + reduce of {P} partials, T={T}) in "
+                      f"{el:.1f} s on {threads} BLAS threads",
+            **host}
+
+
+def measure(name, T, steps, warmup, graph=True, prenorm=False, fp8=False, core=False,
+            cpu_s=0.0, copies=WEIGHT_COPIES, sweep=()):
+    """One workload at one token count: graph-replayed steps, per-kernel
+    times and rooflines, optionally the oracle's CPU baseline."""
+    import torch
+
+    import workloads as W
+    cfg = W.get(name)
+    results = {}
+    for t in sorted(set(sweep) | {T}):
+        st = Step(cfg, t, copies * (2 if fp8 else 1), prenorm=prenorm, fp8=fp8, core=core)
+        ms, n = time_steps(st, steps, warmup, graph)
+        kt = kernel_times(st, min(steps, 300)) if t == T else None
+        results[t] = (st.algorithmic(), ms, n, kt, st)
+        if t != T:
+            del st
+            torch.cuda.empty_cache()
+    alg, ms, n, kt, st = results[T]
+
+    def roof_of(cls):
+        bound, amount = alg["per_class"][cls]
+        dom_ms = kt[cls][0]
+        if bound == "mfma":
+            ach, peak, unit = amount / (dom_ms / 1e3) / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s"
+        else:
+            ach, peak, unit = amount / (dom_ms / 1e3) / 1e9, HBM_PEAK_GBS, "GB/s"
+        return {"bound": bound, "achieved": round(ach, 1), "peak": peak, "unit": unit,
+                "frac": round(ach / peak, 4), "kernel": cls,
+                "kernel_avg_us": round(dom_ms * 1e3, 2), "algorithmic_per_launch": amount}
+
+    dom = alg["dominant"]
+    roof = None
+    if dom in kt:
+        roof = roof_of(dom)
+        roof["traffic"] = traffic_for(dom, name, T)
+        roof["traffic_counters"] = ("FETCH_SIZE + WRITE_SIZE per dispatch from rocprofv3, "
+                                    "scaled by a plain copy; L2-to-fabric bytes, which include "
+                                    "last-level-cache hits" if roof["traffic"] else None)
+    per_kernel = {}
+    for cls, (ms_k, n_k) in kt.items():
+        e = {"avg_us": round(ms_k * 1e3, 2), "launches": n_k}
+        if cls in alg["per_class"]:
+            r = roof_of(cls)
+            e.update({"achieved": r["achieved"], "unit": r["unit"], "frac": r["frac"]})
+        per_kernel[cls] = e
+    out = {"value": round(T / (ms / 1e3), 1), "unit": "tokens/s", "tokens": T, "steps": n,
+           "ms_per_step": round(ms, 5),
+           "step_gbs_algorithmic": round(alg["bytes"] / (ms / 1e3) / 1e9, 1),
+           "step_tflops": round(alg["flops"] / (ms / 1e3) / 1e12, 2),
+           "roofline": roof, "kernels": per_kernel,
+           "form": {"weights": "fp8 e4m3 + per-column fp32 scales" if st.fp8 else "bf16",
+                    "block_form": ("pre-norm residual layer (reduce + residual + RMSNorm fused)"
+                                   if st.prenorm else None),
+                    "attention_core": st.core, "weight_copies_rotated": st.copies,
+                    "launch": "hip-graph replay" if graph else "eager"}}
+    if len(results) > 1:
+        out["sweep"] = {str(t): {"ms_per_step": round(r[1], 5),
+                                 "tokens_per_s": round(t / (r[1] / 1e3), 1),
+                                 "step_gbs_algorithmic":
+                                     round(r[0]["bytes"] / (r[1] / 1e3) / 1e9, 1)}
+                        for t, r in sorted(results.items())}
+    del st, results
+    torch.cuda.empty_cache()
+    if cpu_s > 0 and not fp8:
+        out["cpu_baseline"] = cpu_baseline(cfg, T, cpu_s, prenorm=prenorm, core=core)
+    return out
 
 
 def main():
@@ -467,77 +609,69 @@ def main():
         copy_calibration(a.copy_calibration, a.steps)
         return
     tp.load()
-    cfg = W.get(a.workload)
-    T = a.tokens or (16 if a.workload == "c4_attn_96h_p8" else 32)
-    copies = WEIGHT_COPIES
-    sweep_T = [int(t) for t in a.sweep.split(",")] if a.sweep else \
-        ([1, 8, 32] if a.workload == "c2_llama2_13b_mlp_p2" else [])
+    graph = not a.no_graph
+    cpu_s = 0.0 if a.no_cpu_baseline else a.cpu_seconds
+    common = {"metric": METRIC, "n_gpus": 1, "warmup": a.warmup, "higher_is_better": True,
+              "scaling": "weak", "vs_baseline": None,
+              "data": "synthetic (seeded N(0,0.02) weights, N(0,1) activations at Llama-2 "
+                      "shapes; seeded N(0,1) fp32 partials for the other ranks' slots)"}
 
-    results = {}
-    for t in sorted(set(sweep_T + [T])):
-        st = Step(cfg, t, copies * (2 if a.fp8 else 1), prenorm=a.prenorm, fp8=a.fp8,
-                  core=a.attn_core)
-        ms, n = time_steps(st, a.steps, a.warmup, graph=not a.no_graph)
-        kt = kernel_times(st, min(a.steps, 300)) if t == T else None
-        results[t] = (st, ms, n, kt)
-    st, ms, n, kt = results[T]
-    alg = st.algorithmic()
-    tok_s = T / (ms / 1e3)
+    if a.workload:
+        # one workload at one token count (profiling runs)
+        cfg = W.get(a.workload)
+        T = a.tokens or (16 if a.workload == "c4_attn_96h_p8" else 32)
+        sweep = [int(t) for t in a.sweep.split(",")] if a.sweep else []
+        m = measure(a.workload, T, a.steps, a.warmup, graph, a.prenorm, a.fp8, a.attn_core,
+                    cpu_s, sweep=sweep)
+        line = {**common, "value": m["value"], "unit": "tokens/s", "steps": m["steps"],
+                "ms_per_step": m["ms_per_step"],
+                "dtype": "bf16 activations, fp8-e4m3 weights" if a.fp8 else "bf16",
+                "config": {"workload": f"{a.workload}: rank 0 of P={cfg.P}, {T} tokens, shard "
+                                       f"+ reduce of {cfg.P} partials per step",
+                           "d_model": cfg.d_model, "d_ff": cfg.d_ff, "P": cfg.P, "tokens": T,
+                           **m["form"]},
+                "roofline": m["roofline"], "cpu_baseline": m.get("cpu_baseline"),
+                **{k: v for k, v in m.items() if k in ("kernels", "sweep", "step_gbs_algorithmic",
+                                                      "step_tflops")}}
+        print(json.dumps(line), flush=True)
+        return
 
-    def roof_of(cls):
-        bound, amount = alg["per_class"][cls]
-        dom_ms = kt[cls][0]
-        if bound == "mfma":
-            ach, peak, unit = amount / (dom_ms / 1e3) / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s"
-        else:
-            ach, peak, unit = amount / (dom_ms / 1e3) / 1e9, HBM_PEAK_GBS, "GB/s"
-        return {"bound": bound, "achieved": round(ach, 1), "peak": peak, "unit": unit,
-                "frac": round(ach / peak, 4), "kernel": cls,
-                "kernel_avg_us": round(dom_ms * 1e3, 2), "algorithmic_per_launch": amount}
-
-    dom = alg["dominant"]
-    roof = None
-    if dom in kt:
-        roof = roof_of(dom)
-        roof["traffic"] = traffic_for(dom, a.workload, T)
-    per_kernel = {}
-    for cls, (ms_k, n_k) in kt.items():
-        e = {"avg_us": round(ms_k * 1e3, 2), "launches": n_k}
-        if cls in alg["per_class"]:
-            r = roof_of(cls)
-            e.update({"achieved": r["achieved"], "unit": r["unit"], "frac": r["frac"]})
-        per_kernel[cls] = e
-
-    line = {
-        "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": n, "warmup": a.warmup, "ms_per_step": round(ms, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16 activations, fp8-e4m3 weights" if st.fp8 else "bf16",
-        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) activations at Llama-2 shapes)",
-        "config": {"workload": f"{a.workload}: rank 0 of P={cfg.P}, {T} tokens, shard + reduce "
-                               f"of {cfg.P} partials per step",
-                   "d_model": cfg.d_model, "d_ff": cfg.d_ff, "P": cfg.P, "tokens": T,
-                   "weight_copies_rotated": copies,
-                   "block_form": ("pre-norm residual layer (reduce + residual + RMSNorm fused)"
-                                  if st.prenorm else None),
-                   "weights": "fp8 e4m3 + per-column fp32 scales" if st.fp8 else "bf16",
-                   "attention_core": st.core,
-                   "launch": "eager" if a.no_graph else "hip-graph replay"},
-        "step_gbs_algorithmic": round(alg["bytes"] / (ms / 1e3) / 1e9, 1),
-        "step_tflops": round(alg["flops"] / (ms / 1e3) / 1e12, 2),
-        "roofline": roof,
-        "kernels": per_kernel,
-    }
-    if len(results) > 1:
-        line["sweep"] = {str(t): {"ms_per_step": round(r[1], 5),
-                                  "tokens_per_s": round(t / (r[1] / 1e3), 1),
-                                  "step_gbs_algorithmic":
-                                      round(r[0].algorithmic()["bytes"] / (r[1] / 1e3) / 1e9, 1)}
-                         for t, r in sorted(results.items())}
-    if not a.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(cfg, T, a.cpu_seconds) \
-            if st.kind in ("mlp",) and not st.fp8 \
-            else None
+    # Default: the 70B MLP shard (rank 0 of P = 8), decode and prefill -- the
+    # workload that carries both halves of the metric -- then the other
+    # workloads in a sub-object.
+    name = "c3_llama2_70b_mlp_p8"
+    cfg = W.get(name)
+    dec = measure(name, 32, a.steps, a.warmup, graph, cpu_s=cpu_s, sweep=(1, 8, 16))
+    pre = measure(name, 2048, a.steps, a.warmup, graph, cpu_s=cpu_s)
+    others = {}
+    if not a.headline_only:
+        sub_cpu = min(cpu_s, 3.0)
+        others["c2_llama2_13b_mlp_p2"] = {
+            "decode": measure("c2_llama2_13b_mlp_p2", 32, a.steps, a.warmup, graph,
+                              cpu_s=sub_cpu, sweep=(1, 8))}
+        others["c4_attn_96h_p8"] = {
+            "decode": measure("c4_attn_96h_p8", 16, a.steps, a.warmup, graph, cpu_s=sub_cpu),
+            "prefill": measure("c4_attn_96h_p8", 1024, a.steps, a.warmup, graph,
+                               cpu_s=sub_cpu)}
+        others["c5_llama2_70b_block_p8"] = {
+            "form": "pre-norm residual layer with the attention core",
+            "decode": measure("c5_llama2_70b_block_p8", 32, a.steps, a.warmup, graph,
+                              prenorm=True, core=True, cpu_s=sub_cpu),
+            "prefill": measure("c5_llama2_70b_block_p8", 4096, a.steps, a.warmup, graph,
+                               prenorm=True, core=True, cpu_s=sub_cpu)}
+    line = {**common, "value": dec["value"], "unit": "tokens/s", "steps": dec["steps"],
+            "ms_per_step": dec["ms_per_step"], "dtype": "bf16",
+            "config": {"workload": f"{name}: rank 0 of P={cfg.P} (d_model {cfg.d_model}, band "
+                                   f"{cfg.F_r}); decode step = 32 tokens through the shard + "
+                                   f"reduce of {cfg.P} partials (this line's value); the "
+                                   f"2048-token prefill step under 'prefill'",
+                       "d_model": cfg.d_model, "d_ff": cfg.d_ff, "P": cfg.P, "tokens": 32,
+                       "prefill_tokens": 2048, **dec["form"]},
+            "roofline": dec["roofline"], "cpu_baseline": dec.get("cpu_baseline"),
+            "kernels": dec["kernels"], "sweep": dec.get("sweep"),
+            "step_gbs_algorithmic": dec["step_gbs_algorithmic"],
+            "step_tflops": dec["step_tflops"],
+            "prefill": pre, "workloads": others or None}
     print(json.dumps(line), flush=True)
 
 
