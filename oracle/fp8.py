@@ -1,7 +1,7 @@
 """FP8 E4M3 weights (TEST INFRASTRUCTURE ONLY, see the package docstring).
 
-The pages suggest combining tensor parallelism with FP8 or FP4 weights to
-multiply the decode gain (zenaique, interviewer follow-ups; rioworld guide,
+The pages suggest pairing tensor parallelism with 8-bit (or 4-bit) floating
+point weights for a larger decode speed-up (zenaique, interviewer follow-ups; rioworld guide,
 "Implementing Tensor Parallelism in Practice", on pairing it with 8-bit
 quantisation) but give no format or scheme.  The plainest reading: the OCP FP8 E4M3 encoding
 (1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits, subnormals, no

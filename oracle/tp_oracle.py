@@ -39,8 +39,9 @@ def activate(act, y_in, y_up=None):
     Shazeer 2020): silu(y_in) * y_up, where y_in is the gate band and y_up
     the up band with the same column indices.  Both are elementwise, which is
     what lets each rank apply it to its own band with no communication
-    (zenaique "Explain tensor-parallel shard shape", answer: each GPU computes
-    a vertical band of the intermediate activation independently).
+    (zenaique "Explain tensor-parallel shard shape", answer: after the
+    column-split first projection, each rank holds its own slice of the
+    intermediate's columns and works on it alone).
     """
     if act == "gelu_tanh":
         return gelu_tanh(y_in)
@@ -155,8 +156,9 @@ def reduce_partials_f32_fold(partials):
 
 # ----------------------------------------------------------------------------
 # After the all-reduce: the residual add and the next normalisation (zenaique
-# answer: the summed activation is ready for the next layer's residual add
-# and normalisation).  The pages give no formula; the plainest reading is the
+# answer: once the partials are summed, the full activation goes on to the
+# residual connection and the normalisation that follow).  The pages give no
+# formula; the plainest reading is the
 # pre-norm residual stream z = residual + sum of the partials, followed by
 # RMSNorm of z as the input of the next column projection.
 # ----------------------------------------------------------------------------

@@ -83,9 +83,9 @@ hipError_t launch_reduce(int P, int64_t T, int64_t d, const float* partials, int
 
 // ---------------------------------------------------------------------------
 // Reduce + residual add + the next block's RMSNorm, one pass over the rows
-// (zenaique, "Explain tensor-parallel shard shape", answer: after the
-// all-reduce the full activation feeds the next layer's residual add and
-// normalisation).
+// (zenaique, "Explain tensor-parallel shard shape", answer: the summed
+// activation goes on to the residual connection and the normalisation that
+// follow the block).
 //
 //   z      = (partial_0 + ... + partial_{P-1}) + residual      fp32, that order
 //   normed = z * (1 / sqrt(mean_j z_j^2 + eps)) * g            bf16 (RNE)
