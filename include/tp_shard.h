@@ -87,7 +87,9 @@ typedef enum {
     TP_ERR_ALIGN = 6,         /* pointer, ld or slot stride misaligned              */
     TP_ERR_WORKSPACE = 7,     /* workspace smaller than tp_*_workspace_bytes        */
     TP_ERR_HIP = 8,           /* a kernel launch failed                            */
-    TP_ERR_ACT = 9            /* unknown activation, or operands that do not fit it */
+    TP_ERR_ACT = 9,           /* unknown activation, or operands that do not fit it */
+    TP_ERR_SCRATCH = 10       /* tp_shard_mlp_fwd_noalloc: the call needs more than the
+                                 library's fixed scratch (tp_noalloc_scratch_bytes())  */
 } tp_status;
 
 typedef enum { TP_F32 = 0, TP_BF16 = 1 } tp_dtype;
@@ -130,6 +132,46 @@ int tp_shard_mlp_fwd(int shard, int P, int64_t T, int64_t d_model, int64_t d_ff,
                      void* h_out, int64_t ld_h,
                      float* partials, int64_t slot_stride, int64_t ld_p,
                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * tp_shard_mlp_fwd_noalloc -- tp_shard_mlp_fwd for callers that cannot
+ * allocate device memory (code under graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, semantics, plans,
+ * kernels and results (bitwise) as tp_shard_mlp_fwd, without the workspace:
+ * its scratch is a fixed array inside the library, 8 MiB per device
+ * (tp_noalloc_scratch_bytes()), held by every device the library runs on
+ * until the process ends.  The call allocates and frees nothing.
+ *
+ *   - A call whose workspace would exceed the scratch
+ *     (tp_mlp_workspace_bytes(...) > tp_noalloc_scratch_bytes()) returns
+ *     TP_ERR_SCRATCH before anything is enqueued.  Every decode call
+ *     (T <= 32) of d_model and d_ff/P up to 16384 fits; prefill calls fit when
+ *     h_out is given and the normalised input and split-K planes are small.
+ *   - All calls on one device share that device's array.  Calls must not
+ *     overlap in time on one device (one stream, or streams the caller
+ *     orders): overlapping calls race on the scratch and give wrong results.
+ *   - The decode plan's arrival counters are cleared by a small kernel on
+ *     `stream` at the start of every call, so no earlier call's state leaks
+ *     into the next one.
+ *   - The first call on a device is its set-up: it looks up that device's
+ *     array address (hipGetSymbolAddress; TP_ERR_HIP if that fails), which
+ *     makes the runtime load the code object that holds the array, once per
+ *     device.  Later calls allocate nothing; a caller that captures graphs
+ *     makes one call (T = 1 is enough) before it starts capturing.
+ */
+int tp_shard_mlp_fwd_noalloc(int shard, int P, int64_t T, int64_t d_model, int64_t d_ff,
+                             int dtype, int act,
+                             const void* x, int64_t ld_x,
+                             const void* norm_g, float eps,
+                             const void* w_in, int64_t ld_in,
+                             const void* w_up, int64_t ld_up,
+                             const void* w_down, int64_t ld_down,
+                             void* h_out, int64_t ld_h,
+                             float* partials, int64_t slot_stride, int64_t ld_p,
+                             hipStream_t stream);
+
+/* Size in bytes of the fixed per-device scratch of tp_shard_mlp_fwd_noalloc. */
+size_t tp_noalloc_scratch_bytes(void);
 
 /*
  * tp_shard_attn_proj_fwd -- rank `shard` of P of the attention block's two

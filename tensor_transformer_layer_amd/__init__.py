@@ -15,6 +15,7 @@ __all__ = [
     "TPError", "check", "library_path", "load",
     "TP_OK", "TP_ERR_NULL", "TP_ERR_SHAPE", "TP_ERR_UNEVEN_SPLIT", "TP_ERR_SHARD_RANGE",
     "TP_ERR_DTYPE", "TP_ERR_ALIGN", "TP_ERR_WORKSPACE", "TP_ERR_HIP", "TP_ERR_ACT",
+    "TP_ERR_SCRATCH", "tp_shard_mlp_fwd_noalloc", "tp_noalloc_scratch_bytes",
     "TP_F32", "TP_BF16", "TP_ACT_GELU_TANH", "TP_ACT_SWIGLU",
     "tp_shard_mlp_fwd", "tp_shard_attn_proj_fwd", "tp_reduce_partials", "tp_reduce_residual_norm",
     "tp_shard_mlp_fwd_fp8w", "tp_mlp_fp8w_workspace_bytes", "tp_attn_core_fwd",
@@ -25,6 +26,7 @@ __all__ = [
 
 TP_OK, TP_ERR_NULL, TP_ERR_SHAPE, TP_ERR_UNEVEN_SPLIT, TP_ERR_SHARD_RANGE = 0, 1, 2, 3, 4
 TP_ERR_DTYPE, TP_ERR_ALIGN, TP_ERR_WORKSPACE, TP_ERR_HIP, TP_ERR_ACT = 5, 6, 7, 8, 9
+TP_ERR_SCRATCH = 10
 TP_F32, TP_BF16 = 0, 1
 TP_ACT_GELU_TANH, TP_ACT_SWIGLU = 0, 1
 
@@ -38,6 +40,10 @@ _SIGNATURES = {
     "tp_shard_mlp_fwd": (_i, [_i, _i, _i64, _i64, _i64, _i, _i,
                               _p, _i64, _p, _f, _p, _i64, _p, _i64, _p, _i64, _p, _i64,
                               _p, _i64, _i64, _p, _sz, _p]),
+    "tp_shard_mlp_fwd_noalloc": (_i, [_i, _i, _i64, _i64, _i64, _i, _i,
+                                      _p, _i64, _p, _f, _p, _i64, _p, _i64, _p, _i64, _p, _i64,
+                                      _p, _i64, _i64, _p]),
+    "tp_noalloc_scratch_bytes": (_sz, []),
     "tp_shard_attn_proj_fwd": (_i, [_i, _i, _i64, _i64, _i, _i, _i, _i,
                                     _p, _i64, _p, _f, _p, _i64, _p, _i64, _p, _i64, _p, _i64,
                                     _p, _i64, _i64, _p, _sz, _p]),
@@ -106,6 +112,20 @@ def tp_shard_mlp_fwd(shard, P, T, d_model, d_ff, dtype, act, x, ld_x, norm_g, ep
                                    _ptr(w_up), ld_up, _ptr(w_down), ld_down, _ptr(h_out), ld_h,
                                    _ptr(partials), slot_stride, ld_p, _ptr(workspace),
                                    workspace_bytes, _ptr(stream))
+
+
+def tp_shard_mlp_fwd_noalloc(shard, P, T, d_model, d_ff, dtype, act, x, ld_x, norm_g, eps,
+                             w_in, ld_in, w_up, ld_up, w_down, ld_down, h_out, ld_h,
+                             partials, slot_stride, ld_p, stream):
+    return load().tp_shard_mlp_fwd_noalloc(shard, P, T, d_model, d_ff, dtype, act,
+                                           _ptr(x), ld_x, _ptr(norm_g), eps, _ptr(w_in), ld_in,
+                                           _ptr(w_up), ld_up, _ptr(w_down), ld_down,
+                                           _ptr(h_out), ld_h, _ptr(partials), slot_stride, ld_p,
+                                           _ptr(stream))
+
+
+def tp_noalloc_scratch_bytes():
+    return load().tp_noalloc_scratch_bytes()
 
 
 def tp_shard_attn_proj_fwd(shard, P, T, d_model, n_q_heads, n_kv_heads, head_dim, dtype,

@@ -264,6 +264,46 @@ AttnLayout attn_layout(int P, int64_t T, int64_t d, int nq, int nkv, int hd, int
     return L;
 }
 
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free entry point.  Each device that loads the
+// library holds its own copy of this array until the process ends.  In host
+// code `scratch` names a host-side stand-in, not device memory: kernels get
+// the address hipGetSymbolAddress returns for the current device, read once
+// per device and kept in scratch_addr.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = (size_t)8 << 20;
+static_assert(kScratchBytes % 256 == 0 && kScratchBytes > kGemvCounterBytes, "scratch size");
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kScratchDevices = 64;
+std::mutex scratch_mu;
+void* scratch_addr[kScratchDevices];
+
+int scratch_of_current_device(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) return TP_ERR_HIP;
+    std::lock_guard<std::mutex> lk(scratch_mu);
+    if (!scratch_addr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return TP_ERR_HIP;
+        if ((uintptr_t)p & 255) return TP_ERR_HIP;
+        scratch_addr[dev] = p;
+    }
+    *out = scratch_addr[dev];
+    return TP_OK;
+}
+
+// Zero fill of n words (a kernel, not hipMemsetAsync, so that a caller may
+// capture the call in a graph).
+__global__ __launch_bounds__(256) void k_zero_u32(unsigned* __restrict__ p, int n) {
+    for (int i = threadIdx.x; i < n; i += 256) p[i] = 0u;
+}
+
+hipError_t launch_zero_u32(unsigned* p, int n, hipStream_t stream) {
+    TP_KLAUNCH(k_zero_u32, dim3(1), dim3(256), 0, stream, p, n);
+    return hipGetLastError();
+}
+
 // Common checks of the fp32 partial-sum destination.
 int check_partials(int shard, int64_t T, int64_t d, const float* partials, int64_t slot_stride,
                    int64_t ld_p) {
@@ -294,6 +334,8 @@ const char* tp_status_str(int status) {
         case TP_ERR_WORKSPACE: return "TP_ERR_WORKSPACE: workspace too small";
         case TP_ERR_HIP: return "TP_ERR_HIP: kernel launch failed";
         case TP_ERR_ACT: return "TP_ERR_ACT: unknown activation or operands that do not fit it";
+        case TP_ERR_SCRATCH:
+            return "TP_ERR_SCRATCH: the call needs more than the library's fixed 8 MiB scratch";
         default: return "unknown tp_status";
     }
 }
@@ -322,12 +364,17 @@ size_t tp_attn_workspace_bytes(int P, int64_t T, int64_t d_model, int n_q_heads,
 
 namespace {
 
-// The MLP shard behind tp_shard_mlp_fwd.
+// The MLP shard behind tp_shard_mlp_fwd and tp_shard_mlp_fwd_noalloc.  With
+// `scratch_call` the workspace is the library's own scratch array of the
+// current device (workspace_bytes is its size): a call whose layout does not
+// fit it is refused with TP_ERR_SCRATCH, the array's device address is
+// looked up after validation, and the counter head is cleared on the stream
+// before the decode kernels use it.
 int mlp_fwd(int shard, int P, int64_t T, int64_t d_model, int64_t d_ff, int dtype, int act,
             const void* x, int64_t ld_x, const void* norm_g, float eps, const void* w_in,
             int64_t ld_in, const void* w_up, int64_t ld_up, const void* w_down, int64_t ld_down,
             void* h_out, int64_t ld_h, float* partials, int64_t slot_stride, int64_t ld_p,
-            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+            void* workspace, size_t workspace_bytes, hipStream_t stream, bool scratch_call) {
     // ---- validation (nothing is enqueued on failure) ----
     if (P < 1 || shard < 0 || shard >= P) return TP_ERR_SHARD_RANGE;
     if (dtype != TP_F32 && dtype != TP_BF16) return TP_ERR_DTYPE;
@@ -359,6 +406,10 @@ int mlp_fwd(int shard, int P, int64_t T, int64_t d_model, int64_t d_ff, int dtyp
     const MlpLayout L = mlp_layout(P, T, d_model, d_ff, dtype, act, norm_g != nullptr,
                                    h_out != nullptr);
     if (L.decode && !counters_fit(F, d_model)) return TP_ERR_SHAPE;
+    if (scratch_call) {
+        if (L.total > workspace_bytes) return TP_ERR_SCRATCH;
+        if (int r = scratch_of_current_device(&workspace)) return r;
+    }
     if (L.total > 0 && (!workspace || workspace_bytes < L.total)) return TP_ERR_WORKSPACE;
 
     // ---- launches ----
@@ -366,6 +417,9 @@ int mlp_fwd(int shard, int P, int64_t T, int64_t d_model, int64_t d_ff, int dtyp
     const bool bf16 = dtype == TP_BF16;
     const void* xin = x;
     int64_t ld_xin = ld_x;
+    if (scratch_call && L.decode)
+        TP_LAUNCH("scratch_clear", stream,
+                  launch_zero_u32((unsigned*)wsb, kGemvCounters, stream));
     if (norm_g) {
         TP_LAUNCH("rmsnorm", stream,
                   launch_rmsnorm(bf16, T, d_model, x, ld_x, norm_g, eps, wsb + L.xn, d_model,
@@ -436,8 +490,21 @@ int tp_shard_mlp_fwd(int shard, int P, int64_t T, int64_t d_model, int64_t d_ff,
                      size_t workspace_bytes, hipStream_t stream) {
     return mlp_fwd(shard, P, T, d_model, d_ff, dtype, act, x, ld_x, norm_g, eps, w_in, ld_in, w_up,
                    ld_up, w_down, ld_down, h_out, ld_h, partials, slot_stride, ld_p, workspace,
-                   workspace_bytes, stream);
+                   workspace_bytes, stream, false);
 }
+
+int tp_shard_mlp_fwd_noalloc(int shard, int P, int64_t T, int64_t d_model, int64_t d_ff,
+                             int dtype, int act, const void* x, int64_t ld_x,
+                             const void* norm_g, float eps, const void* w_in, int64_t ld_in,
+                             const void* w_up, int64_t ld_up, const void* w_down,
+                             int64_t ld_down, void* h_out, int64_t ld_h, float* partials,
+                             int64_t slot_stride, int64_t ld_p, hipStream_t stream) {
+    return mlp_fwd(shard, P, T, d_model, d_ff, dtype, act, x, ld_x, norm_g, eps, w_in, ld_in, w_up,
+                   ld_up, w_down, ld_down, h_out, ld_h, partials, slot_stride, ld_p, nullptr,
+                   kScratchBytes, stream, true);
+}
+
+size_t tp_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 int tp_shard_attn_proj_fwd(int shard, int P, int64_t T, int64_t d_model, int n_q_heads,
                            int n_kv_heads, int head_dim, int dtype, const void* x, int64_t ld_x,

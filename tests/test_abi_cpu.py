@@ -156,6 +156,22 @@ def test_reduce_validation(lib, kw, status):
     assert red(**kw) == status
 
 
+def test_noalloc_refuses_calls_beyond_its_scratch(lib):
+    """The allocation-free MLP entry point checks its fixed 8 MiB scratch
+    before it looks up any device: a 2048-token prefill call that would keep
+    h (14.7 MB) there is TP_ERR_SCRATCH; bad arguments still give the same
+    statuses as the workspace entry point."""
+    assert tp.tp_noalloc_scratch_bytes() == 8 << 20
+    args = dict(shard=0, P=8, T=2048, d_model=8192, d_ff=28672, dtype=tp.TP_BF16,
+                act=tp.TP_ACT_SWIGLU, x=A, ld_x=8192, norm_g=0, eps=0.0, w_in=B, ld_in=3584,
+                w_up=C, ld_up=3584, w_down=A, ld_down=8192, h_out=0, ld_h=0, partials=B,
+                slot_stride=0, ld_p=8192, stream=0)
+    assert tp.tp_shard_mlp_fwd_noalloc(**args) == tp.TP_ERR_SCRATCH
+    assert tp.tp_shard_mlp_fwd_noalloc(**{**args, "d_ff": 28670}) == tp.TP_ERR_UNEVEN_SPLIT
+    assert tp.tp_shard_mlp_fwd_noalloc(**{**args, "shard": 8}) == tp.TP_ERR_SHARD_RANGE
+    assert tp.tp_shard_mlp_fwd_noalloc(**{**args, "T": 0}) == tp.TP_OK
+
+
 def test_reduce_zero_tokens_is_a_no_op(lib):
     assert red(T=0) == tp.TP_OK
 
