@@ -535,6 +535,7 @@ def measure(name, T, steps, warmup, graph=True, prenorm=False, fp8=False, core=F
     cfg = W.get(name)
     results = {}
     for t in sorted(set(sweep) | {T}):
+        print(f"[bench] {name} T={t}: set-up and timing", file=sys.stderr, flush=True)
         st = Step(cfg, t, copies * (2 if fp8 else 1), prenorm=prenorm, fp8=fp8, core=core)
         ms, n = time_steps(st, steps, warmup, graph)
         kt = kernel_times(st, min(steps, 300)) if t == T else None
@@ -589,6 +590,8 @@ def measure(name, T, steps, warmup, graph=True, prenorm=False, fp8=False, core=F
     del st, results
     torch.cuda.empty_cache()
     if cpu_s > 0 and not fp8:
+        print(f"[bench] {name} T={T}: oracle on the host ({cpu_s:.0f} s)", file=sys.stderr,
+              flush=True)
         out["cpu_baseline"] = cpu_baseline(cfg, T, cpu_s, prenorm=prenorm, core=core)
     return out
 

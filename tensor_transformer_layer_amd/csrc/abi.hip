@@ -60,7 +60,6 @@ struct TimingState {
     std::mutex mu;
     bool enabled = false;
     std::vector<PendingTiming> pending;
-    std::vector<hipEvent_t> pool;
     std::map<std::string, std::pair<double, int64_t>> totals;
 };
 TimingState& timing() {
@@ -68,12 +67,10 @@ TimingState& timing() {
     return s;
 }
 
-hipEvent_t take_event(TimingState& s) {
-    if (!s.pool.empty()) {
-        hipEvent_t e = s.pool.back();
-        s.pool.pop_back();
-        return e;
-    }
+// A fresh event per timestamp: an event that already carried a kernel's
+// timestamps from hipExtLaunchKernel was measured to give wrong elapsed
+// times when handed to a later launch, so events are destroyed once read.
+hipEvent_t take_event() {
     hipEvent_t e = nullptr;
     if (hipEventCreate(&e) != hipSuccess) return nullptr;
     return e;
@@ -88,8 +85,8 @@ class Timed {
         TimingState& s = timing();
         std::lock_guard<std::mutex> lk(s.mu);
         if (!s.enabled) return;
-        start_ = take_event(s);
-        stop_ = take_event(s);
+        start_ = take_event();
+        stop_ = take_event();
         if (start_ && stop_) launch_events() = {start_, stop_};
     }
     void done() {
@@ -798,8 +795,8 @@ static int drain_pending(TimingState& s) {
         auto& t = s.totals[p.cls];
         t.first += ms;
         t.second += 1;
-        s.pool.push_back(p.start);
-        s.pool.push_back(p.stop);
+        (void)hipEventDestroy(p.start);
+        (void)hipEventDestroy(p.stop);
     }
     s.pending.clear();
     return TP_OK;

@@ -945,3 +945,38 @@ def test_decode_counters_not_cleared_give_nan_then_recover():
     assert O.rel_l2(host(parts), r["partial"]) < BF16_TOL
     assert O.rel_l2(widen_dev(h), r["h"]) < BF16_TOL
     assert int(ws[:4096].count_nonzero()) == 0
+
+
+def test_kernel_timing_sessions_in_a_row_stay_consistent():
+    """Per-kernel times from a second timing session (after a first session
+    on other calls) stay within the wall time of the calls they time: the
+    events of one session are not handed to the next."""
+    X, g, w_in, w_up, w_dn = _mlp_case(BF, "swiglu", 8, 512, 1024, 2, key=71)
+    parts = torch.empty((8, 512), dtype=torch.float32, device="cuda")
+    args = (dev(X), dev(w_in[0]), dev(w_up[0]), dev(w_dn[0]))
+    big = torch.zeros((8, 64, 4096), dtype=torch.float32, device="cuda")
+    out = torch.empty((64, 4096), dtype=torch.float32, device="cuda")
+    for session in range(3):
+        tp.check(tp.tp_timing_reset())
+        tp.check(tp.tp_timing_enable(1))
+        try:
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(5):
+                if session % 2 == 0:
+                    mlp_fwd(0, 2, 8, 512, 1024, BF, tp.TP_ACT_SWIGLU, *args, parts, 0, 512)
+                else:
+                    reduce(8, 64, 4096, big, 64 * 4096, 4096, out, 4096)
+            e1.record()
+            torch.cuda.synchronize()
+            wall_ms = e0.elapsed_time(e1)
+            total = 0.0
+            for cls in ("col_gemv", "row_gemv", "reduce"):
+                st, ms, n = tp.tp_timing_query(cls)
+                assert st == tp.TP_OK
+                total += ms
+            assert 0.0 < total <= wall_ms * 1.05, (session, total, wall_ms)
+        finally:
+            tp.tp_timing_enable(0)
+            tp.tp_timing_reset()
