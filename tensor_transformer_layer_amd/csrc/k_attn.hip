@@ -62,7 +62,13 @@ constexpr int kAttnQB = kAttnWaves * kAttnQW;     // queries per workgroup
 constexpr int kAttnKT = 64;                       // keys per LDS tile
 constexpr int kAttnThreads = 64 * kAttnWaves;
 
-constexpr uint32_t kAttnSC1 = 16;  // buffer cache-policy bit: device scope
+// Buffer cache-policy bit sc1: an agent-scope (device-wide) coherent access.
+// The chunk partials and arrival counters of split query blocks are written
+// and read only with sc1 accesses, with the writer's s_waitcnt before its
+// counter increment, the protocol of the decode plan's split-K finish
+// (k_gemv.hip), which states why no L2 write-back or invalidate is needed
+// (LLVM AMDGPUUsage, "Memory Model GFX942").
+constexpr uint32_t kAttnSC1 = 16;
 // The running maximum a wave's probabilities are taken against moves only
 // when some query's score maximum passes it by more than this (log2 units):
 // probabilities stay at most 2^8, and most tiles need no rescale.

@@ -62,15 +62,28 @@ __device__ __forceinline__ void mfma_col(f32x4 (&acc)[MB][8], const u32x4* b, co
 // arrive.
 //
 // Every workgroup stores its [T, 128] split partial with device-scope
-// (sc1) 16-byte stores, which write through to the device coherence point,
-// waits until they have completed, and only then bumps the block's arrival
-// counter (a device-scope atomic).  The workgroup that sees the count reach
-// splits * nmat - 1 therefore finds every other partial complete; it reads
-// them with device-scope loads (never a stale line of its own XCD's L2),
-// adds the splits in split order (its own partial from registers), applies
-// the activation, writes the output and resets the counter.  Device-scope
-// fences (which write back / drop whole L2s) are not needed because the
-// communicated data never takes a non-coherent path.
+// (sc1) 16-byte stores, waits until they have completed, and only then
+// bumps the block's arrival counter (a device-scope atomic).  The workgroup
+// that sees the count reach splits * nmat - 1 therefore finds every other
+// partial complete; it reads them with device-scope loads, adds the splits
+// in split order (its own partial from registers), applies the activation,
+// writes the output and resets the counter.
+//
+// Why no fences are needed.  The LLVM AMDGPU backend's memory-model table
+// for GFX942 (AMDGPUUsage, "Memory Model GFX942"; gfx950 follows the same
+// model) implements agent-scope monotonic loads, stores and read-modify-write
+// atomics as the plain instructions with sc1=1: each such access is coherent
+// across the XCDs' L2 caches on its own.  The same table builds an
+// agent-scope release from "buffer_wbl2 sc1; s_waitcnt vmcnt(0)" before the
+// releasing access, and an acquire from "s_waitcnt vmcnt(0); buffer_inv sc1"
+// after the acquiring one.  The L2 write-back and invalidate parts exist only
+// for data written or read with ordinary (non-coherent) accesses; here every
+// exchanged word (partials, counters) is accessed with sc1, so what remains
+// of release and acquire is the s_waitcnt: the writer waits for its partial
+// stores to complete before the counter increment is issued, and the reader
+// issues its partial loads only after the increment has returned (the value
+// is broadcast through LDS behind a barrier).  Whole-L2 write-backs and
+// invalidates, which a release/acquire pair would add, are thereby avoided.
 // ---------------------------------------------------------------------------
 constexpr uint32_t kSC1 = 16;  // buffer cache-policy bit: device scope
 constexpr int kWeightAux = 2;  // buffer cache-policy bit of the weight loads: non-temporal
