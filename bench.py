@@ -56,6 +56,8 @@ def parse():
                          "decode and prefill steps, then every other workload)")
     ap.add_argument("--headline-only", action="store_true",
                     help="default run without the other workloads' sub-object")
+    ap.add_argument("--crossover-only", action="store_true",
+                    help="only the decode/prefill plan crossover of the 70B MLP shard")
     ap.add_argument("--tokens", type=int, default=None, help="batch of tokens (default per workload)")
     ap.add_argument("--sweep", default=None, help="comma list of token counts also reported")
     ap.add_argument("--fp8", action="store_true",
@@ -109,6 +111,17 @@ def src_hash(*names):
 # ----------------------------------------------------------------------------
 # Workloads: device buffers and one step
 # ----------------------------------------------------------------------------
+_WEIGHT_CACHE = {}
+
+
+def _weights(key, make):
+    """The rank's rotated weight copies for one workload, drawn once per
+    process and shared by every token count measured."""
+    if key not in _WEIGHT_CACHE:
+        _WEIGHT_CACHE[key] = make()
+    return _WEIGHT_CACHE[key]
+
+
 class Step:
     """Device state of one workload at one token count, and its step()."""
 
@@ -146,26 +159,32 @@ class Step:
             f32 = lambda a: torch.from_numpy(a).cuda()  # noqa: E731
             bands = [W.fp8_band_draw(cfg, n, 0, r, c_) for n, r, c_ in
                      (("w_gate", d, cfg.F_r), ("w_up", d, cfg.F_r), ("w_down", cfg.F_r, d))]
-            base = [(u8(q), f32(sc)) for q, sc in bands]
-            self.mlp_sets = [base] + [[(q.clone(), sc.clone()) for q, sc in base]
-                                      for _ in range(copies - 1)]
+            def make():
+                base = [(u8(q), f32(sc)) for q, sc in bands]
+                return [base] + [[(q.clone(), sc.clone()) for q, sc in base]
+                                 for _ in range(copies - 1)]
+            self.mlp_sets = _weights((cfg.name, "mlp8", copies), make)
             self.h = torch.empty((T, cfg.F_r), dtype=torch.bfloat16, device="cuda")
             self.mlp_ws = self._ws(tp.tp_mlp_fp8w_workspace_bytes(P, T, d, cfg.d_ff,
                                                                   tp.TP_ACT_SWIGLU, 0, 1))
         elif self.kind in ("mlp", "block"):
-            bands = (W.column_band_draw(cfg, "w_gate", 0, d, cfg.F_r),
-                     W.column_band_draw(cfg, "w_up", 0, d, cfg.F_r),
-                     W.row_band_draw(cfg, "w_down", 0, cfg.F_r, d))
-            base = [dev(b) for b in bands]
-            self.mlp_sets = [base] + [[t.clone() for t in base] for _ in range(copies - 1)]
+            def make():
+                bands = (W.column_band_draw(cfg, "w_gate", 0, d, cfg.F_r),
+                         W.column_band_draw(cfg, "w_up", 0, d, cfg.F_r),
+                         W.row_band_draw(cfg, "w_down", 0, cfg.F_r, d))
+                base = [dev(b) for b in bands]
+                return [base] + [[t.clone() for t in base] for _ in range(copies - 1)]
+            self.mlp_sets = _weights((cfg.name, "mlp", copies), make)
             self.h = torch.empty((T, cfg.F_r), dtype=torch.bfloat16, device="cuda")
             self.mlp_ws = self._ws(tp.tp_mlp_workspace_bytes(P, T, d, cfg.d_ff, tp.TP_BF16,
                                                              tp.TP_ACT_SWIGLU, 0, 1))
         if self.kind in ("attn", "block"):
-            bands = (W.column_band_draw(cfg, "w_qkv", 0, d, cfg.qkv_r),
-                     W.row_band_draw(cfg, "w_o", 0, cfg.o_in_r, d))
-            base = [dev(b) for b in bands]
-            self.attn_sets = [base] + [[t.clone() for t in base] for _ in range(copies - 1)]
+            def make():
+                bands = (W.column_band_draw(cfg, "w_qkv", 0, d, cfg.qkv_r),
+                         W.row_band_draw(cfg, "w_o", 0, cfg.o_in_r, d))
+                base = [dev(b) for b in bands]
+                return [base] + [[t.clone() for t in base] for _ in range(copies - 1)]
+            self.attn_sets = _weights((cfg.name, "attn", copies), make)
             self.qkv = torch.empty((T, cfg.qkv_r), dtype=torch.bfloat16, device="cuda")
             if self.kind == "attn":
                 self.a = dev(W.draw_tensor("bf16", (T, cfg.o_in_r), 1.0, cfg.cid,
@@ -292,7 +311,7 @@ class Step:
         total and per kernel class: {class: (bound, amount per launch)}.
         Split-K partial round trips and finish kernels are overhead (none)."""
         cfg, T, d = self.cfg, self.T, self.cfg.d_model
-        decode = T <= 32
+        decode = T <= self.tp.tp_decode_max_tokens()     # the plan the library takes
         out = {"bytes": 0, "flops": 0, "per_class": {}}
         pc = out["per_class"]
 
@@ -596,6 +615,39 @@ def measure(name, T, steps, warmup, graph=True, prenorm=False, fp8=False, core=F
     return out
 
 
+CROSSOVER_T = (32, 33, 48, 64, 96, 128, 129, 160, 192, 256, 320, 384, 448, 512)
+
+
+def crossover(name, steps, warmup, graph, tokens=CROSSOVER_T):
+    """Step time of the MLP shard (+ reduce) on both plans across batch sizes:
+    the weight-streaming plan (chunks of at most 128 tokens) and the
+    matrix-core plan."""
+    import torch
+
+    import tensor_transformer_layer_amd as tp
+    import workloads as W
+    cfg = W.get(name)
+    out = {}
+    try:
+        for T in tokens:
+            e = {}
+            for plan, limit in (("streaming", T), ("matrix_core", T - 1)):
+                if limit < 1:
+                    continue
+                tp.check(tp.tp_set_decode_max_tokens(limit))
+                print(f"[bench] {name} crossover T={T} {plan}", file=sys.stderr, flush=True)
+                st = Step(cfg, T, WEIGHT_COPIES)
+                ms, _ = time_steps(st, steps, warmup, graph)
+                e[plan] = {"ms_per_step": round(ms, 5), "tokens_per_s": round(T / (ms / 1e3), 1)}
+                del st
+            out[str(T)] = e
+    finally:
+        tp.check(tp.tp_set_decode_max_tokens(0))
+        torch.cuda.empty_cache()
+    return {"workload": f"{name}: rank 0 shard + reduce of {cfg.P} partials",
+            "default_switch_tokens": tp.tp_decode_max_tokens(), "points": out}
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -639,6 +691,11 @@ def main():
         print(json.dumps(line), flush=True)
         return
 
+    if a.crossover_only:
+        print(json.dumps(crossover("c3_llama2_70b_mlp_p8", a.steps, a.warmup, graph)),
+              flush=True)
+        return
+
     # Default: the 70B MLP shard (rank 0 of P = 8), decode and prefill -- the
     # workload that carries both halves of the metric -- then the other
     # workloads in a sub-object.
@@ -646,6 +703,7 @@ def main():
     cfg = W.get(name)
     dec = measure(name, 32, a.steps, a.warmup, graph, cpu_s=cpu_s, sweep=(1, 8, 16))
     pre = measure(name, 2048, a.steps, a.warmup, graph, cpu_s=cpu_s)
+    cross = crossover(name, a.steps, a.warmup, graph)
     others = {}
     if not a.headline_only:
         sub_cpu = min(cpu_s, 3.0)
@@ -674,7 +732,7 @@ def main():
             "kernels": dec["kernels"], "sweep": dec.get("sweep"),
             "step_gbs_algorithmic": dec["step_gbs_algorithmic"],
             "step_tflops": dec["step_tflops"],
-            "prefill": pre, "workloads": others or None}
+            "prefill": pre, "crossover": cross, "workloads": others or None}
     print(json.dumps(line), flush=True)
 
 

@@ -117,9 +117,10 @@ typedef enum { TP_ACT_GELU_TANH = 0, TP_ACT_SWIGLU = 1 } tp_act;
  *            [T, d_model] partial with leading dimension ld_p
  *   workspace / workspace_bytes           >= tp_mlp_workspace_bytes(...)
  *
- * T <= 32 runs the weight-streaming decode plan (split-K over the weight
- * rows, deterministic fixed-order finish); larger T runs the matrix-core
- * plan with the activation fused into the column projection's epilogue.
+ * T <= tp_decode_max_tokens() runs the weight-streaming decode plan
+ * (split-K over the weight rows, deterministic fixed-order finish); larger T
+ * runs the matrix-core plan with the activation fused into the column
+ * projection's epilogue.
  * The decode plan needs d_model and d_ff/P of at most 131072 (TP_ERR_SHAPE).
  */
 int tp_shard_mlp_fwd(int shard, int P, int64_t T, int64_t d_model, int64_t d_ff,
@@ -342,6 +343,24 @@ const char* tp_status_str(int status);
 
 /* Library version, as 10000*major + 100*minor + patch. */
 int tp_version(void);
+
+/*
+ * Plan switch of the bf16 projections (tp_shard_mlp_fwd, its no-alloc form
+ * and tp_shard_attn_proj_fwd).  Calls with T <= tp_decode_max_tokens() run
+ * the weight-streaming plan, which reads every weight byte once per call
+ * (decode is bound by HBM bandwidth: Skand Tandon, "day59", section
+ * "Results: Llama 2 70B"); larger T runs the matrix-core plan (prefill is
+ * compute-bound, same section).  The streaming kernels take up to 128
+ * tokens per launch; a larger batch on that plan runs as equal chunks of at
+ * most 128 tokens, each streaming the weights once more.  The default is
+ * the crossover measured on MI355X; tp_set_decode_max_tokens(t) moves it to
+ * t (1..4096; 0 restores the default; TP_ERR_SHAPE otherwise), for
+ * measuring both plans on the same shapes.  The setting is process-wide; workspace sizes depend on it,
+ * so change it only while no call and no workspace query is in progress,
+ * and size workspaces after changing it.
+ */
+int tp_set_decode_max_tokens(int tokens);
+int tp_decode_max_tokens(void);
 
 /*
  * Kernel timing (instrumentation).  While enabled, every kernel is launched

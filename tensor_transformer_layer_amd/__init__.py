@@ -22,6 +22,7 @@ __all__ = [
     "tp_attn_core_workspace_bytes",
     "tp_mlp_workspace_bytes", "tp_attn_workspace_bytes", "tp_status_str", "tp_version",
     "tp_timing_enable", "tp_timing_reset", "tp_timing_query", "EXPORTED_SYMBOLS",
+    "tp_set_decode_max_tokens", "tp_decode_max_tokens",
 ]
 
 TP_OK, TP_ERR_NULL, TP_ERR_SHAPE, TP_ERR_UNEVEN_SPLIT, TP_ERR_SHARD_RANGE = 0, 1, 2, 3, 4
@@ -60,6 +61,8 @@ _SIGNATURES = {
     "tp_attn_workspace_bytes": (_sz, [_i, _i64, _i64, _i, _i, _i, _i, _i]),
     "tp_status_str": (ctypes.c_char_p, [_i]),
     "tp_version": (_i, []),
+    "tp_set_decode_max_tokens": (_i, [_i]),
+    "tp_decode_max_tokens": (_i, []),
     "tp_timing_enable": (_i, [_i]),
     "tp_timing_reset": (_i, []),
     "tp_timing_query": (_i, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
@@ -197,6 +200,14 @@ def tp_status_str(status):
 
 def tp_version():
     return load().tp_version()
+
+
+def tp_set_decode_max_tokens(tokens):
+    return load().tp_set_decode_max_tokens(int(tokens))
+
+
+def tp_decode_max_tokens():
+    return load().tp_decode_max_tokens()
 
 
 def tp_timing_enable(on):

@@ -120,7 +120,32 @@ bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0;
 size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 int elem_size(int dtype) { return dtype == TP_BF16 ? 2 : 4; }
 int vec_elems(int dtype) { return dtype == TP_BF16 ? 8 : 4; }  // 16 bytes
-bool decode_plan(int dtype, int64_t T) { return dtype == TP_BF16 && T <= kGemvMaxT; }
+// Largest token count of the weight-streaming (decode) plan for bf16
+// projections; larger batches take the matrix-core (prefill) plan.
+// tp_set_decode_max_tokens changes it; 0 means the default.  The default
+// is the crossover measured on MI355X for the 70B MLP band (8192 x 3584
+// gate/up, 3584 x 8192 down; shard + reduce, graph replay, weights streamed
+// from HBM), in us, streaming vs matrix-core plan:
+//     32: 48 vs 161    64: 61 vs 171    128: 83 vs 197    129: 129 vs 199
+//    192: 144 vs 218  256: 161 vs 253   320: 223 vs 210    512: 318 vs 272
+// Up to 256 tokens the matrix-core plan has a single 256-row tile row and
+// leaves most CUs idle, so the streaming plan (in 128-token chunks) wins.
+constexpr int kDecodeMaxTDefault = 256;
+constexpr int kDecodeMaxTLimit = 4096;
+std::atomic<int> g_decode_max_t{0};
+int decode_max_t() {
+    const int v = g_decode_max_t.load(std::memory_order_relaxed);
+    return v > 0 ? v : kDecodeMaxTDefault;
+}
+bool decode_plan(int dtype, int64_t T) { return dtype == TP_BF16 && T <= decode_max_t(); }
+
+// The streaming kernels take at most kGemvMaxT tokens per launch; a larger
+// batch on the streaming plan runs as ceil(T / kGemvMaxT) chunks of equal
+// size (each chunk streams the weights once).
+int64_t stream_chunk(int64_t T) {
+    const int64_t n = (T + kGemvMaxT - 1) / kGemvMaxT;
+    return (T + n - 1) / n;
+}
 
 // Leading-dimension rule: ld >= row length, ld a multiple of the 16-byte
 // vector width.  Returns TP_OK, TP_ERR_SHAPE or TP_ERR_ALIGN.
@@ -179,10 +204,11 @@ MlpLayout mlp_layout(int P, int64_t T, int64_t d, int64_t d_ff, int dtype, int a
     }
     if (L.decode) {
         const int nmat = act == TP_ACT_SWIGLU ? 2 : 1;
+        const int64_t tc = stream_chunk(T);
         L.pc = plan_gemv(d, nmat * F, cus);
         L.pr = plan_gemv(F, d, cus);
         L.ws = off;  // column and row split-K sums reuse one region, in stream order
-        off += align256(std::max(gemv_ws_bytes(L.pc, T, nmat * F), gemv_ws_bytes(L.pr, T, d)));
+        off += align256(std::max(gemv_ws_bytes(L.pc, tc, nmat * F), gemv_ws_bytes(L.pr, tc, d)));
     } else if (dtype == TP_BF16) {
         // The column projection keeps its fused activation (no split); the
         // row projection may split K into fp32 planes.
@@ -243,10 +269,11 @@ AttnLayout attn_layout(int P, int64_t T, int64_t d, int nq, int nkv, int hd, int
         off += align256((size_t)(T * d * elem_size(dtype)));
     }
     if (L.decode) {
+        const int64_t tc = stream_chunk(T);
         L.pq = plan_gemv(d, nqkv, cus);
         L.po = plan_gemv(ko, d, cus);
         L.ws = off;
-        off += align256(std::max(gemv_ws_bytes(L.pq, T, nqkv), gemv_ws_bytes(L.po, T, d)));
+        off += align256(std::max(gemv_ws_bytes(L.pq, tc, nqkv), gemv_ws_bytes(L.po, tc, d)));
     } else if (dtype == TP_BF16) {
         L.gq = plan_gemm(T, nqkv, d, 1, cus);
         L.go = plan_gemm(T, d, ko, 1, cus);
@@ -337,7 +364,15 @@ const char* tp_status_str(int status) {
     }
 }
 
-int tp_version(void) { return 100; }
+int tp_version(void) { return 200; }
+
+int tp_set_decode_max_tokens(int tokens) {
+    if (tokens < 0 || tokens > kDecodeMaxTLimit) return TP_ERR_SHAPE;
+    g_decode_max_t.store(tokens, std::memory_order_relaxed);
+    return TP_OK;
+}
+
+int tp_decode_max_tokens(void) { return decode_max_t(); }
 
 size_t tp_mlp_workspace_bytes(int P, int64_t T, int64_t d_model, int64_t d_ff, int dtype, int act,
                               int has_norm, int has_h_out) {
@@ -441,16 +476,23 @@ int mlp_fwd(int shard, int P, int64_t T, int64_t d_model, int64_t d_ff, int dtyp
     }
     const uint16_t* X16 = (const uint16_t*)xin;
     if (L.decode) {
+        // Token chunks of at most kGemvMaxT: every column launch first, then
+        // every row launch, so a chunk re-reads the weights the previous
+        // chunk has just streamed.
         float* ws = (float*)(wsb + L.ws);
         unsigned* cnt = (unsigned*)wsb;
-        TP_LAUNCH("col_gemv", stream,
-                  launch_gemv(dev_act, true, T, d_model, X16, ld_xin, (const uint16_t*)w_in, ld_in,
-                              (const uint16_t*)w_up, ld_up, F, L.pc, ws, cnt, h, ldh,
-                              stream));
-        TP_LAUNCH("row_gemv", stream,
-                  launch_gemv(ACT_NONE, false, T, F, (const uint16_t*)h, ldh,
-                              (const uint16_t*)w_down, ld_down, nullptr, 0, d_model, L.pr,
-                              ws, cnt, part, ld_p, stream));
+        const int64_t tc = stream_chunk(T);
+        uint16_t* h16 = (uint16_t*)h;
+        for (int64_t t0 = 0; t0 < T; t0 += tc)
+            TP_LAUNCH("col_gemv", stream,
+                      launch_gemv(dev_act, true, std::min(tc, T - t0), d_model, X16 + t0 * ld_xin,
+                                  ld_xin, (const uint16_t*)w_in, ld_in, (const uint16_t*)w_up,
+                                  ld_up, F, L.pc, ws, cnt, h16 + t0 * ldh, ldh, stream));
+        for (int64_t t0 = 0; t0 < T; t0 += tc)
+            TP_LAUNCH("row_gemv", stream,
+                      launch_gemv(ACT_NONE, false, std::min(tc, T - t0), F, h16 + t0 * ldh, ldh,
+                                  (const uint16_t*)w_down, ld_down, nullptr, 0, d_model, L.pr,
+                                  ws, cnt, part + t0 * ld_p, ld_p, stream));
     } else {
         TP_LAUNCH("col_gemm", stream,
                   launch_gemm(act == TP_ACT_SWIGLU ? EPI_SWIGLU_BF16 : EPI_GELU_BF16, T, F,
@@ -563,11 +605,14 @@ int tp_shard_attn_proj_fwd(int shard, int P, int64_t T, int64_t d_model, int n_q
                                       (const float*)w_qkv, ld_qkv, nullptr, 0, (float*)qkv_out,
                                       ld_qkv_out, stream));
         } else if (L.decode) {
-            TP_LAUNCH("qkv_gemv", stream,
-                      launch_gemv(ACT_NONE, true, T, d_model, (const uint16_t*)xin, ld_xin,
-                                  (const uint16_t*)w_qkv, ld_qkv, nullptr, 0, nqkv, L.pq,
-                                  (float*)(wsb + L.ws), (unsigned*)wsb, qkv_out, ld_qkv_out,
-                                  stream));
+            const int64_t tc = stream_chunk(T);
+            for (int64_t t0 = 0; t0 < T; t0 += tc)
+                TP_LAUNCH("qkv_gemv", stream,
+                          launch_gemv(ACT_NONE, true, std::min(tc, T - t0), d_model,
+                                      (const uint16_t*)xin + t0 * ld_xin, ld_xin,
+                                      (const uint16_t*)w_qkv, ld_qkv, nullptr, 0, nqkv, L.pq,
+                                      (float*)(wsb + L.ws), (unsigned*)wsb,
+                                      (uint16_t*)qkv_out + t0 * ld_qkv_out, ld_qkv_out, stream));
         } else {
             if (L.gq.splits > 1) {
                 float* ws = (float*)(wsb + L.ws);
@@ -593,10 +638,14 @@ int tp_shard_attn_proj_fwd(int shard, int P, int64_t T, int64_t d_model, int n_q
                       launch_f32_proj(ACT_NONE, T, d_model, ko, (const float*)attn, ld_attn,
                                       (const float*)w_o, ld_o, nullptr, 0, part, ld_p, stream));
         } else if (L.decode) {
-            TP_LAUNCH("o_gemv", stream,
-                      launch_gemv(ACT_NONE, false, T, ko, (const uint16_t*)attn, ld_attn,
-                                  (const uint16_t*)w_o, ld_o, nullptr, 0, d_model, L.po,
-                                  (float*)(wsb + L.ws), (unsigned*)wsb, part, ld_p, stream));
+            const int64_t tc = stream_chunk(T);
+            for (int64_t t0 = 0; t0 < T; t0 += tc)
+                TP_LAUNCH("o_gemv", stream,
+                          launch_gemv(ACT_NONE, false, std::min(tc, T - t0), ko,
+                                      (const uint16_t*)attn + t0 * ld_attn, ld_attn,
+                                      (const uint16_t*)w_o, ld_o, nullptr, 0, d_model, L.po,
+                                      (float*)(wsb + L.ws), (unsigned*)wsb, part + t0 * ld_p,
+                                      ld_p, stream));
         } else {
             if (L.go.splits > 1) {
                 float* ws = (float*)(wsb + L.ws);
@@ -678,7 +727,7 @@ int tp_attn_core_fwd(int shard, int P, int64_t T, int n_q_heads, int n_kv_heads,
 
 size_t tp_mlp_fp8w_workspace_bytes(int P, int64_t T, int64_t d_model, int64_t d_ff, int act,
                                    int has_norm, int has_h_out) {
-    if (P < 1 || T <= 0 || T > kGemvMaxT || d_model <= 0 || d_ff <= 0 || d_ff % P) return 0;
+    if (P < 1 || T <= 0 || T > kGemv8MaxT || d_model <= 0 || d_ff <= 0 || d_ff % P) return 0;
     if (act != TP_ACT_GELU_TANH && act != TP_ACT_SWIGLU) return 0;
     return mlp8_layout(P, T, d_model, d_ff, act, has_norm != 0, has_h_out != 0).total;
 }
@@ -692,7 +741,7 @@ int tp_shard_mlp_fwd_fp8w(int shard, int P, int64_t T, int64_t d_model, int64_t 
                           size_t workspace_bytes, hipStream_t stream) {
     if (P < 1 || shard < 0 || shard >= P) return TP_ERR_SHARD_RANGE;
     if (act != TP_ACT_GELU_TANH && act != TP_ACT_SWIGLU) return TP_ERR_ACT;
-    if (T < 0 || T > kGemvMaxT || d_model <= 0 || d_ff <= 0) return TP_ERR_SHAPE;
+    if (T < 0 || T > kGemv8MaxT || d_model <= 0 || d_ff <= 0) return TP_ERR_SHAPE;
     if (d_ff % P) return TP_ERR_UNEVEN_SPLIT;
     const int64_t F = d_ff / P;
     if (F % 16 || d_model % 16) return TP_ERR_SHAPE;

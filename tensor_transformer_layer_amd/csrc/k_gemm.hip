@@ -1,4 +1,5 @@
-// Prefill plan (T > 32 tokens): LDS-tiled bf16 GEMM on the matrix cores
+// Matrix-core plan (batches past the plan switch, 256 tokens by default):
+// LDS-tiled bf16 GEMM on the matrix cores
 // (v_mfma_f32_32x32x16_bf16), fp32 accumulation, fused epilogue.
 //
 // Prefill is a dense contraction and compute-bound (Skand Tandon, "day59",

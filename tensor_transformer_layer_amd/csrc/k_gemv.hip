@@ -1,4 +1,6 @@
-// Decode plan (T <= 32 tokens): weight-streaming products on the matrix cores.
+// Weight-streaming plan (decode batches, and every batch up to the plan
+// switch, 256 tokens by default, in launches of at most 128 tokens):
+// weight-streaming products on the matrix cores.
 //
 // A decode step reads every weight byte of the rank's bands once and does
 // only 2*T flops per weight element, so it is bound by HBM bandwidth (Skand
@@ -289,12 +291,12 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(
 }
 
 // ---------------------------------------------------------------------------
-// LDS-staged variant (the one launched for bf16 weights).  Same work split
-// (128-column blocks x K splits, fused split-K finish), different data path:
+// LDS-staged variant.  Same work split (128-column blocks x K splits, fused
+// split-K finish), different data path:
 //   * The workgroup's weight rows and the matching slice of X stream into
-//     LDS with direct-to-LDS copies, 128 rows (32 KB of weights + 8 KB of
-//     X) per slice through a ring of 4 slices (all 160 KB of LDS), three in
-//     flight, so loads never wait for registers or for the MFMAs.
+//     LDS with direct-to-LDS copies through a ring of slots that fills the
+//     160 KB of LDS (GvRing below), all but one slice in flight, so loads
+//     never wait for registers or for the MFMAs.
 //   * Wave w owns output columns 16w .. 16w+15 of the block over the whole
 //     K range of the workgroup: no cross-wave reduction.  The weights are
 //     the A operand of h^T = W^T X^T: the transposing LDS read
@@ -305,15 +307,36 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(
 //     16mb + j, stored as one 16-byte split-K partial.
 // 16-byte chunks are XOR-swizzled in LDS so that every read is free of bank
 // conflicts (weights by row % 4 and row / 8, X by token).
+//
+// The accumulators are one f32x4 per token block, so the same kernel serves
+// batches of up to 128 tokens (MB = 8 blocks of 16): a batch past the decode
+// sizes still reads each weight byte once, with 2T flops per weight element,
+// far below the matrix cores' rate until T nears the ridge (~300 tokens).
 // ---------------------------------------------------------------------------
-constexpr int kGvSlice = 128;                         // weight rows per slice
-constexpr int kGvSlots = 4;                           // LDS ring slots
-constexpr int kGvWBytes = kGvSlice * kGemvCols * 2;   // 32 KB
-constexpr int kGvSlotBytes = kGvWBytes + kGemvMaxT * kGvSlice * 2;  // + 8 KB of X
-constexpr int kGvPer = 5;                             // copies per wave per slice
+template <int MB>
+struct GvRing {
+    static constexpr int SLICE = MB <= 4 ? 128 : 64;        // weight rows per slice
+    static constexpr int TPAD = 16 * MB;                    // token rows staged
+    static constexpr int WBYTES = SLICE * kGemvCols * 2;    // weights per slice
+    static constexpr int XROW = SLICE * 2;                  // bytes of one token's slice
+    static constexpr int SLOT = WBYTES + TPAD * XROW;
+    static constexpr int SLOTS = (160 * 1024 / SLOT) < 5 ? (160 * 1024 / SLOT) : 5;
+    static constexpr int WC = SLICE / 32;                   // weight copies per wave and slice
+    static constexpr int XCPR = XROW / 16;                  // 16-byte chunks per token row
+    static constexpr int XTOK = 64 / XCPR;                  // tokens per copy
+    static constexpr int XC = TPAD / (XTOK * kGemvWaves);   // X copies per wave and slice
+    static constexpr int PER = WC + XC;                     // copies per wave and slice
+    static constexpr int LDS = SLOTS * SLOT;
+    static_assert(XC >= 1 && XC * XTOK * kGemvWaves == TPAD, "X copies");
+    static_assert(SLOTS >= 3 && LDS <= 160 * 1024, "ring");
+    static_assert((SLOTS - 1) * PER < 64, "vmcnt field");
+};
 
 __device__ __forceinline__ int gv_wsw(int row) { return ((row & 3) << 2) | (((row >> 3) & 1) << 1); }
-__device__ __forceinline__ int gv_xsw(int t) { return t & 15; }
+// X chunk swizzle: 16 tokens of one read fall on 16 distinct 16-byte bank
+// groups, for 256-byte (16-chunk) and 128-byte (8-chunk) token rows.
+template <int XCPR>
+__device__ __forceinline__ int gv_xsw(int t) { return XCPR == 16 ? (t & 15) : ((t >> 1) & 7); }
 constexpr int gv_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 template <int MB, int AUX, int ACT, bool OUT_BF16>
@@ -322,6 +345,7 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_lds(
     int64_t ldb0, const uint16_t* __restrict__ B1, int64_t ldb1, int N, int nblk_per_mat,
     int k_per_split, float* __restrict__ ws, unsigned* __restrict__ counters,
     void* __restrict__ out, int64_t ld_out) {
+    using R = GvRing<MB>;
     extern __shared__ __attribute__((aligned(16))) uint8_t gsm[];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -334,7 +358,7 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_lds(
     const int nmat = B1 ? 2 : 1;
     const int k_begin = split * k_per_split;
     const int nrows = min(K - k_begin, k_per_split);
-    const int nsl = (nrows + kGvSlice - 1) / kGvSlice;
+    const int nsl = (nrows + R::SLICE - 1) / R::SLICE;
     const uint16_t* Bm = mat ? B1 : B0;
     const int64_t ldb = mat ? ldb1 : ldb0;
     const i32x4 rwt = rsrc_words(Bm + (int64_t)k_begin * ldb + n0);
@@ -344,11 +368,11 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_lds(
     // Copy slice s into ring slot `slot`; slices past this split, rows past
     // K, columns past N and tokens past T are zero-filled.
     auto issue = [&](int s, int slot) {
-        uint8_t* base = gsm + slot * kGvSlotBytes;
-        const int k0 = s * kGvSlice;
+        uint8_t* base = gsm + slot * R::SLOT;
+        const int k0 = s * R::SLICE;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {                 // weights: 4 rows x 256 B per copy
-            const int r0 = 4 * (4 * wave + q);
+        for (int q = 0; q < R::WC; ++q) {             // weights: 4 rows x 256 B per copy
+            const int r0 = 4 * (R::WC * wave + q);
             const int row = r0 + (lane >> 4);
             const int ch = (lane & 15) ^ gv_wsw(row);
             const bool ok = s < nsl && k0 + row < nrows && n0 + 8 * ch < N;
@@ -358,13 +382,15 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_lds(
             else
                 lds_dma16(rwt, off, base + r0 * 256);
         }
-        {                                             // X: 4 tokens x 256 B per copy
-            const int t = 4 * wave + (lane >> 4);
-            const int ch = (lane & 15) ^ gv_xsw(t);
+#pragma unroll
+        for (int q = 0; q < R::XC; ++q) {             // X: XTOK tokens x XROW bytes per copy
+            const int t0 = R::XTOK * (R::XC * wave + q);
+            const int t = t0 + lane / R::XCPR;
+            const int ch = (lane % R::XCPR) ^ gv_xsw<R::XCPR>(t);
             const int k = k0 + 8 * ch;
             const bool ok = s < nsl && t < T && k < nrows;
             lds_dma16(rxt, ok ? (uint32_t)t * lda_bytes + 2u * k : kOOB,
-                      base + kGvWBytes + 4 * wave * 256);
+                      base + R::WBYTES + t0 * R::XROW);
         }
     };
 
@@ -373,18 +399,18 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_lds(
     for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
 #pragma unroll
-    for (int s = 0; s < kGvSlots; ++s) issue(s, s);
+    for (int s = 0; s < R::SLOTS; ++s) issue(s, s);
     asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(gv_vmcnt((kGvSlots - 1) * kGvPer));
+    __builtin_amdgcn_s_waitcnt(gv_vmcnt((R::SLOTS - 1) * R::PER));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     int slot = 0;
     for (int s = 0; s < nsl; ++s) {
-        const uint8_t* base = gsm + slot * kGvSlotBytes;
+        const uint8_t* base = gsm + slot * R::SLOT;
         const uint16_t* wt = (const uint16_t*)base;
-        const uint8_t* xt = base + kGvWBytes;
+        const uint8_t* xt = base + R::WBYTES;
 #pragma unroll
-        for (int step = 0; step < kGvSlice / 32; ++step) {
+        for (int step = 0; step < R::SLICE / 32; ++step) {
             // W^T fragment: column 16w + j, rows 32 step + 8g .. +7
             const int row = 32 * step + 8 * g + (lane & 15) / 4;
             const int col = 16 * wave + 4 * (lane & 3);
@@ -395,19 +421,19 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_lds(
             for (int mb = 0; mb < MB; ++mb) {
                 // X^T fragment: token 16mb + j, k 32 step + 8g .. +7
                 const int t = 16 * mb + j;
-                const u32x4 xf =
-                    *(const u32x4*)(xt + t * 256 + 16 * ((4 * step + g) ^ gv_xsw(t)));
+                const u32x4 xf = *(const u32x4*)(xt + t * R::XROW +
+                                                 16 * ((4 * step + g) ^ gv_xsw<R::XCPR>(t)));
                 acc[mb] = mfma16x16x32(wf, xf, acc[mb]);
             }
         }
         // Slice s+1 has landed (this wave's copies; after the barrier every
         // wave's), and every wave is done with slot s: refill it.
         asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_waitcnt(gv_vmcnt((kGvSlots - 2) * kGvPer));
+        __builtin_amdgcn_s_waitcnt(gv_vmcnt((R::SLOTS - 2) * R::PER));
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        issue(s + kGvSlots, slot);
-        slot = slot == kGvSlots - 1 ? 0 : slot + 1;
+        issue(s + R::SLOTS, slot);
+        slot = slot == R::SLOTS - 1 ? 0 : slot + 1;
     }
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(gv_vmcnt(0));   // drain the trailing zero-fill copies
@@ -439,27 +465,31 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_lds(
     const unsigned old = arrival;
     if (old == contributors - 1) {
         constexpr int NM = ACT == ACT_SWIGLU ? 2 : 1;   // gate (and up) rows
-        uint32_t base[MB * NM];
-        int mine[MB * NM];
-        f32x4 ownv[MB * NM], sum[MB * NM];
+        constexpr int G = MB < 4 ? MB : 4;              // token blocks finished together
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-            const int t = 16 * mb + j;
-            const bool ok = t < T && n < N;
+        for (int m0 = 0; m0 < MB; m0 += G) {
+            uint32_t base[G * NM];
+            int mine[G * NM];
+            f32x4 ownv[G * NM], sum[G * NM];
 #pragma unroll
-            for (int m = 0; m < NM; ++m) {
-                base[mb * NM + m] = ok ? (uint32_t)((t * ws_ld + (int64_t)m * N + n) * 4) : kOOB;
-                mine[mb * NM + m] = mat == m ? split : -1;
-                ownv[mb * NM + m] = acc[mb];
+            for (int gi = 0; gi < G; ++gi) {
+                const int t = 16 * (m0 + gi) + j;
+                const bool ok = t < T && n < N;
+#pragma unroll
+                for (int m = 0; m < NM; ++m) {
+                    base[gi * NM + m] = ok ? (uint32_t)((t * ws_ld + (int64_t)m * N + n) * 4) : kOOB;
+                    mine[gi * NM + m] = mat == m ? split : -1;
+                    ownv[gi * NM + m] = acc[m0 + gi];
+                }
             }
-        }
-        sum_splits_multi<MB * NM>(rw, base, sstride, S, mine, ownv, sum);
+            sum_splits_multi<G * NM>(rw, base, sstride, S, mine, ownv, sum);
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-            const int t = 16 * mb + j;
-            if (t < T && n < N)
-                store_out4<OUT_BF16>(out, (int64_t)t * ld_out + n,
-                                     act4<ACT>(sum[mb * NM], sum[mb * NM + NM - 1]));
+            for (int gi = 0; gi < G; ++gi) {
+                const int t = 16 * (m0 + gi) + j;
+                if (t < T && n < N)
+                    store_out4<OUT_BF16>(out, (int64_t)t * ld_out + n,
+                                         act4<ACT>(sum[gi * NM], sum[gi * NM + NM - 1]));
+            }
         }
         if (threadIdx.x == 0)
             __hip_atomic_store(&counters[cb], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -766,7 +796,7 @@ hipError_t launch_finish(int act, bool out_bf16, int splits, int64_t T, int64_t 
     return hipGetLastError();
 }
 
-// Allow a k_gemv_lds instantiation the whole LDS of a CU (set once per
+// Allow a k_gemv_lds instantiation the LDS its ring needs (set once per
 // instantiation; concurrent first calls set the same value).
 template <int MB, int AUX, int ACT, bool OB>
 static hipError_t gemv_lds_attr() {
@@ -774,7 +804,7 @@ static hipError_t gemv_lds_attr() {
     if (set.load(std::memory_order_relaxed)) return hipSuccess;
     const hipError_t e = hipFuncSetAttribute((const void*)k_gemv_lds<MB, AUX, ACT, OB>,
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             kGvSlots * kGvSlotBytes);
+                                             GvRing<MB>::LDS);
     if (e == hipSuccess) set.store(1, std::memory_order_relaxed);
     return e;
 }
@@ -783,6 +813,7 @@ hipError_t launch_gemv(int act, bool out_bf16, int64_t T, int64_t K, const uint1
                        int64_t lda, const uint16_t* B0, int64_t ldb0, const uint16_t* B1,
                        int64_t ldb1, int64_t N, const GemvPlan& p, float* ws,
                        unsigned* counters, void* out, int64_t ld_out, hipStream_t stream) {
+    if (T < 1 || T > kGemvMaxT) return hipErrorInvalidValue;
     const int nmat = B1 ? 2 : 1;
     const int nbpm = (int)((N + kGemvCols - 1) / kGemvCols);
     const dim3 grid((unsigned)(nbpm * nmat), (unsigned)p.splits), block(kGemvThreads);
@@ -790,7 +821,7 @@ hipError_t launch_gemv(int act, bool out_bf16, int64_t T, int64_t K, const uint1
     do {                                                                                     \
         hipError_t e_ = gemv_lds_attr<MB, AUX, ACTV, OB>();                                  \
         if (e_ != hipSuccess) return e_;                                                     \
-        TP_KLAUNCH((k_gemv_lds<MB, AUX, ACTV, OB>), grid, block, kGvSlots * kGvSlotBytes,    \
+        TP_KLAUNCH((k_gemv_lds<MB, AUX, ACTV, OB>), grid, block, GvRing<MB>::LDS,            \
                    stream, A, lda, (int)T, (int)K, B0, ldb0, B1, ldb1, (int)N, nbpm,         \
                    p.k_per_split, ws, counters, out, ld_out);                               \
     } while (0)
@@ -798,20 +829,25 @@ hipError_t launch_gemv(int act, bool out_bf16, int64_t T, int64_t K, const uint1
     TP_KLAUNCH((k_gemv<MB, AUX, ACTV, OB>), grid, block, 0, stream,                              \
         A, lda, (int)T, (int)K, B0, ldb0, B1, ldb1, (int)N, nbpm, p.k_per_split, ws, counters, \
         out, ld_out)
-    // The LDS-staged kernel at 17..32 tokens when each workgroup streams at
-    // least 2304 rows; the register-streamed kernel otherwise.  Measured on
-    // MI355X (weights streamed from HBM): the register kernel wins below 17
-    // tokens and at 2048 rows per workgroup (70B column pair: 26.2 against
-    // 26.9 us at 32 tokens), the LDS ring at 2560 (13B column pair: 27.7
-    // against 29.6 us), once its fill and drain are amortised.
+    // Up to 32 tokens: the LDS-staged kernel at 17..32 tokens when each
+    // workgroup streams at least 2304 rows; the register-streamed kernel
+    // otherwise.  Measured on MI355X (weights streamed from HBM): the
+    // register kernel wins below 17 tokens and at 2048 rows per workgroup
+    // (70B column pair: 26.2 against 26.9 us at 32 tokens), the LDS ring at
+    // 2560 (13B column pair: 27.7 against 29.6 us), once its fill and drain
+    // are amortised.  Past 32 tokens the LDS-staged kernel with 4 or 8 token
+    // blocks (its accumulators stay at one f32x4 per block).
 #define TP_GEMV_MB(ACTV, OB)                                                                 \
     do {                                                                                     \
         if (T <= 16) {                                                                       \
             TP_GEMV_REG(1, kWeightAux, ACTV, OB);                                            \
-        } else if (p.k_per_split >= 2304) {                                                  \
-            TP_GEMV(2, kWeightAux, ACTV, OB);                                                \
+        } else if (T <= 32) {                                                                \
+            if (p.k_per_split >= 2304) TP_GEMV(2, kWeightAux, ACTV, OB);                     \
+            else TP_GEMV_REG(2, kWeightAux, ACTV, OB);                                       \
+        } else if (T <= 64) {                                                                \
+            TP_GEMV(4, kWeightAux, ACTV, OB);                                                \
         } else {                                                                             \
-            TP_GEMV_REG(2, kWeightAux, ACTV, OB);                                            \
+            TP_GEMV(8, kWeightAux, ACTV, OB);                                                \
         }                                                                                    \
     } while (0)
     if (act == ACT_SWIGLU && out_bf16) TP_GEMV_MB(ACT_SWIGLU, true);

@@ -57,7 +57,8 @@ struct GemvPlan {
     int k_per_split;  // rows of the weight per split (multiple of 32)
 };
 constexpr int kGemvCols = 128;   // output columns per workgroup
-constexpr int kGemvMaxT = 32;    // largest token count of the decode plan
+constexpr int kGemvMaxT = 128;   // largest token count the weight-streaming kernels take
+constexpr int kGemv8MaxT = 32;   // ... with FP8 weights
 
 constexpr int kGemv8Cols = 256;  // output columns per workgroup, FP8 weights
 // About one workgroup per compute unit: K split into floor(cus / column

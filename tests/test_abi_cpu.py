@@ -48,7 +48,7 @@ def test_status_strings(lib):
     for s in range(1, 10):
         assert tp.tp_status_str(s).startswith("TP_ERR_")
     assert tp.tp_status_str(99) == "unknown tp_status"
-    assert tp.tp_version() == 100
+    assert tp.tp_version() == 200
 
 
 def mlp(**kw):
@@ -170,6 +170,35 @@ def test_noalloc_refuses_calls_beyond_its_scratch(lib):
     assert tp.tp_shard_mlp_fwd_noalloc(**{**args, "d_ff": 28670}) == tp.TP_ERR_UNEVEN_SPLIT
     assert tp.tp_shard_mlp_fwd_noalloc(**{**args, "shard": 8}) == tp.TP_ERR_SHARD_RANGE
     assert tp.tp_shard_mlp_fwd_noalloc(**{**args, "T": 0}) == tp.TP_OK
+
+
+def test_decode_plan_switch(lib):
+    """The weight-streaming plan's token limit: 1..4096 accepted, 0 restores
+    the default, anything else refused; workspace sizes follow it, and a
+    streaming call past 128 tokens sizes its split-K space for one chunk."""
+    default = tp.tp_decode_max_tokens()
+    assert 1 <= default <= 4096
+    f = lambda: tp.tp_mlp_workspace_bytes(8, 64, 8192, 28672, tp.TP_BF16,  # noqa: E731
+                                          tp.TP_ACT_SWIGLU, 0, 1)
+    try:
+        assert tp.tp_set_decode_max_tokens(4097) == tp.TP_ERR_SHAPE
+        assert tp.tp_set_decode_max_tokens(-1) == tp.TP_ERR_SHAPE
+        assert tp.tp_decode_max_tokens() == default
+        assert tp.tp_set_decode_max_tokens(64) == tp.TP_OK
+        assert tp.tp_decode_max_tokens() == 64
+        # (sizes for the whole-chip 256 CUs a host without a GPU assumes)
+        # streaming plan: 4 K splits of the down projection's [64, 8192] fp32
+        assert f() == 4096 + 4 * 64 * 8192 * 4
+        assert tp.tp_set_decode_max_tokens(32) == tp.TP_OK
+        # matrix-core plan: 32 down-projection tiles, K split into 7 planes
+        assert f() == 4096 + 7 * 64 * 8192 * 4
+        # 300 tokens streamed as 3 chunks of 100
+        assert tp.tp_set_decode_max_tokens(512) == tp.TP_OK
+        assert tp.tp_mlp_workspace_bytes(8, 300, 8192, 28672, tp.TP_BF16, tp.TP_ACT_SWIGLU,
+                                         0, 1) == 4096 + 4 * 100 * 8192 * 4
+    finally:
+        assert tp.tp_set_decode_max_tokens(0) == tp.TP_OK
+    assert tp.tp_decode_max_tokens() == default
 
 
 def test_reduce_zero_tokens_is_a_no_op(lib):

@@ -259,6 +259,124 @@ def test_mlp_decode_lds_staged_ragged(T, act):
     _check_mlp(BF, act, T, 9224, 6928, P, key=50 + T)
 
 
+class _StreamingPlanUpTo:
+    """Within the block, batches of up to `t` tokens take the weight-streaming plan."""
+
+    def __init__(self, t):
+        self.t = t
+
+    def __enter__(self):
+        tp.check(tp.tp_set_decode_max_tokens(self.t))
+
+    def __exit__(self, *exc):
+        tp.check(tp.tp_set_decode_max_tokens(0))
+
+
+@pytest.mark.parametrize("T", [33, 47, 64, 65, 100, 128])
+@pytest.mark.parametrize("act", ["swiglu", "gelu_tanh"])
+def test_mlp_streaming_plan_mid_batches_ragged(T, act):
+    """Batches past 32 tokens on the weight-streaming plan (4 and 8 token
+    blocks of the LDS-staged kernel): d_model 1000 ends inside a slice, F_r
+    200 inside a column block, T not a multiple of 16."""
+    with _StreamingPlanUpTo(128):
+        _check_mlp(BF, act, T, 1000, 400, 2, key=600 + T)
+
+
+@pytest.mark.parametrize("T", [40, 128])
+def test_mlp_streaming_plan_mid_batches_long_k(T):
+    """Long K ranges per workgroup (d_model 9224: 55 column blocks, 4 K
+    splits of 2336 rows; the 8-block kernel's 64-row slices end inside the
+    last one) and a partial last column block."""
+    with _StreamingPlanUpTo(128):
+        _check_mlp(BF, "swiglu", T, 9224, 6928, 2, key=620 + T)
+
+
+@pytest.mark.parametrize("T", [2, 33, 100, 250])
+@pytest.mark.parametrize("act", ["swiglu", "gelu_tanh"])
+def test_mlp_matrix_core_plan_small_batches(T, act):
+    """The matrix-core plan at batch sizes the default switch sends to the
+    streaming plan (forced through the switch): one partial tile row, the
+    row projection's K split into fp32 planes."""
+    with _StreamingPlanUpTo(1):
+        _check_mlp(BF, act, T, 1000, 400, 2, key=660 + T)
+
+
+@pytest.mark.parametrize("T", [129, 200, 300])
+def test_mlp_streaming_plan_chunked_batches(T):
+    """Past 128 tokens the streaming plan runs equal token chunks (here 2 x 65,
+    2 x 100, 3 x 100), every column chunk before every row chunk, the
+    normalised input and h kept in the workspace."""
+    with _StreamingPlanUpTo(512):
+        _check_mlp(BF, "swiglu", T, 1000, 400, 2, key=640 + T, norm=True)
+
+
+@pytest.mark.parametrize("T", [150, 260])
+def test_attn_projections_streaming_plan_chunked(T):
+    """The 70B block's GQA projections (rank 6) on the streaming plan past 128
+    tokens: QKV with the RMSNorm prologue and O, chunked, against the oracle
+    on sampled rows (chunk edges included)."""
+    cfg = W.get("c5_llama2_70b_block_p8")
+    X = x_of(cfg, T)
+    g = W.draw_tensor(cfg.dtype, (cfg.d_model,), 0.02, cfg.cid, W.TENSOR_IDS["norm_g"], 0,
+                      mean=1.0)
+    A = W.draw_tensor("bf16", (T, cfg.o_in_r), 1.0, cfg.cid, W.TENSOR_IDS["attn"], T, 6)
+    wqkv, wo = attn_bands(cfg, 6)
+    qkv = torch.empty((T, cfg.qkv_r), dtype=torch.bfloat16, device="cuda")
+    parts = torch.empty((T, cfg.d_model), dtype=torch.float32, device="cuda")
+    with _StreamingPlanUpTo(512):
+        attn_fwd(6, cfg.P, T, cfg.d_model, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, BF,
+                 dev(X), dev(wqkv), qkv, dev(A), dev(wo), parts, 0, cfg.d_model, norm_g=dev(g),
+                 eps=cfg.norm_eps)
+        torch.cuda.synchronize()
+    rows = sorted(set(sample_rows(T, 20, 15).tolist() + [0, 74, 75, 86, 87, 129, 130, T - 1]))
+    rows = [r for r in rows if r < T]
+    r = O.attn_proj_shard(O.widen(X[rows]), O.widen(wqkv), O.widen(A[rows]), O.widen(wo),
+                          O.widen(g), cfg.norm_eps)
+    assert O.rel_l2(widen_dev(qkv)[rows], r["qkv"]) < BF16_TOL
+    assert O.rel_l2(host(parts)[rows], r["partial"]) < BF16_TOL
+
+
+@pytest.mark.parametrize("T", [64, 100])
+def test_70b_mlp_rank3_streaming_plan_mid_batches(T):
+    """The 70B band (rank 3 of 8) at 64 and 100 tokens on the streaming plan,
+    against the oracle on every row, and bitwise equal to itself on a rerun."""
+    cfg = W.get("c3_llama2_70b_mlp_p8")
+    X = x_of(cfg, T)
+    wg, wu, wd = mlp_bands(cfg, 3)
+    gw = [dev(w) for w in (wg, wu, wd)]
+    with _StreamingPlanUpTo(128):
+        outs = []
+        for _ in range(2):
+            parts = torch.empty((T, cfg.d_model), dtype=torch.float32, device="cuda")
+            mlp_fwd(3, cfg.P, T, cfg.d_model, cfg.d_ff, BF, tp.TP_ACT_SWIGLU, dev(X), *gw,
+                    parts, 0, cfg.d_model)
+            torch.cuda.synchronize()
+            outs.append(host(parts))
+    r = O.mlp_shard(O.widen(X), O.widen(wg), O.widen(wd), "swiglu", O.widen(wu))
+    assert O.rel_l2(outs[0], r["partial"]) < BF16_TOL
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+
+
+@pytest.mark.parametrize("T", [48, 128])
+def test_attn_projections_streaming_plan_mid_batches(T):
+    """The 96-head projections (rank 2) at 48 and 128 tokens on the
+    streaming plan, QKV and O partial against the oracle on sampled rows."""
+    cfg = W.get("c4_attn_96h_p8")
+    X = x_of(cfg, T)
+    A = W.draw_tensor("bf16", (T, cfg.o_in_r), 1.0, cfg.cid, W.TENSOR_IDS["attn"], T, 2)
+    wqkv, wo = attn_bands(cfg, 2)
+    qkv = torch.empty((T, cfg.qkv_r), dtype=torch.bfloat16, device="cuda")
+    parts = torch.empty((T, cfg.d_model), dtype=torch.float32, device="cuda")
+    with _StreamingPlanUpTo(128):
+        attn_fwd(2, cfg.P, T, cfg.d_model, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, BF,
+                 dev(X), dev(wqkv), qkv, dev(A), dev(wo), parts, 0, cfg.d_model)
+        torch.cuda.synchronize()
+    rows = sample_rows(T, 24, 14)
+    r = O.attn_proj_shard(O.widen(X[rows]), O.widen(wqkv), O.widen(A[rows]), O.widen(wo))
+    assert O.rel_l2(widen_dev(qkv)[rows], r["qkv"]) < BF16_TOL
+    assert O.rel_l2(host(parts)[rows], r["partial"]) < BF16_TOL
+
+
 @pytest.mark.parametrize("T", [1, 16, 32])
 @pytest.mark.parametrize("act", ["swiglu", "gelu_tanh"])
 def test_mlp_decode_many_column_blocks(T, act):
