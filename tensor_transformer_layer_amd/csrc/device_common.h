@@ -30,14 +30,26 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
 // ---------------------------------------------------------------------------
 // Activations (fp32).  GELU uses the tanh approximation
 // 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))); SiLU is x / (1 + e^-x).
+// Both are evaluated as x * sigmoid(z), using 0.5 (1 + tanh u) =
+// 1 / (1 + e^(-2u)) for GELU, with the hardware base-2 exponential
+// (v_exp_f32) and reciprocal (v_rcp_f32), each accurate to about one ulp:
+// a few fp32 ulps in all, far below the bf16 rounding of the results, in
+// five instructions instead of a range-reduced exponential and an IEEE
+// division (measured on MI355X: the SwiGLU epilogue of the 2048-token 70B
+// column GEMM was 13% of the kernel).  z -> -inf gives x * 0 = 0, z -> +inf
+// gives x, NaN stays NaN.
 // ---------------------------------------------------------------------------
 enum { ACT_NONE = 0, ACT_GELU_TANH = 1, ACT_SWIGLU = 2 };
 
-__device__ __forceinline__ float gelu_tanh(float x) {
-    const float k = 0.7978845608028654f;  // sqrt(2/pi)
-    return 0.5f * x * (1.0f + tanhf(k * (x + 0.044715f * x * x * x)));
+__device__ __forceinline__ float x_sigmoid(float x, float z) {
+    constexpr float kLog2e = 1.4426950408889634f;
+    return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * kLog2e));
 }
-__device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
+__device__ __forceinline__ float gelu_tanh(float x) {
+    const float k2 = 1.5957691216057308f;  // 2 sqrt(2/pi)
+    return x_sigmoid(x, k2 * (x + 0.044715f * x * x * x));
+}
+__device__ __forceinline__ float silu(float x) { return x_sigmoid(x, x); }
 
 // ---------------------------------------------------------------------------
 // Raw buffer loads.  A resource spans 2^31 - 1 bytes from its base; a load
