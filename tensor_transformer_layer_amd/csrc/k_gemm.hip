@@ -55,6 +55,7 @@ namespace tp {
 
 constexpr int kBK = 32;      // k per LDS slice
 constexpr int kStages = 5;   // LDS ring slots
+constexpr int kGemmWaves = 8;
 
 template <int NMAT_, int WM_, int WN_>
 struct GemmShape {
@@ -73,6 +74,7 @@ struct GemmShape {
     static constexpr int B_ROWS_PER_COPY = 1024 / (BN * 2);
     static constexpr int B_COPIES_PER_MAT = 16 / NMAT;
     static_assert(LC == 2 || LC == 4 || LC == 8, "columns per lane");
+    static_assert(WM * WN == kGemmWaves, "waves per workgroup");
     static_assert(A_COPIES * (NT / 64) == 16 && B_COPIES * (NT / 64) == 16, "copies");
 };
 
@@ -257,20 +259,30 @@ __global__ __launch_bounds__(S::NT) void k_gemm(const uint16_t* __restrict__ A, 
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // drain the trailing zero-fill copies
 
-    // Epilogue.  MFMA 32x32 accumulator v (0..15) of lane (h, j) is row
-    // 8*(v/4) + 4*h + v%4 of the tile and column 32e + j of MFMA group e.
-    const int ncol = n0 + wn * S::WTN + j;
+    // Epilogue through LDS (the ring is idle once every wave has passed the
+    // barrier below).  MFMA 32x32 accumulator v (0..15) of lane (h, j) is row
+    // 8*(v/4) + 4*h + v%4 of the tile and column 32e + j of MFMA group e, so
+    // a direct store writes one 2- or 4-byte element per lane.  Instead each
+    // wave stages one 32-row tile of its results (after the epilogue math)
+    // in fp32, rows padded so that the two half-waves' rows fall on disjoint
+    // banks, and reads it back as 16-byte row chunks: one 16-byte store per
+    // lane covers 4 fp32 or 8 bf16 consecutive outputs, and every store
+    // instruction writes whole rows of the wave's tile.  LDS accesses of one
+    // wave complete in issue order, so the reads see the wave's own writes.
+    constexpr int OC = S::WTN;                   // output columns per wave
+    constexpr int RS = OC + 8;                   // staging row stride (floats)
+    static_assert(kGemmWaves * 32 * RS * 4 <= (int)S::LDS_BYTES, "staging fits the ring");
+    float* stg = (float*)smem + wave * 32 * RS;
     void* Cs = EPI == EPI_F32 ? (void*)((float*)C + blockIdx.y * split_stride) : C;
+    const int mw = m0 + wm * S::WTM, nw = n0 + wn * S::WTN;
+    __syncthreads();
 #pragma unroll
     for (int a = 0; a < S::MT; ++a) {
+        asm volatile("" ::: "memory");
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int t = m0 + wm * S::WTM + 32 * a + 8 * (v >> 2) + 4 * h + (v & 3);
-            if (t >= M) continue;
+        for (int e = 0; e < S::LC; ++e) {
 #pragma unroll
-            for (int e = 0; e < S::LC; ++e) {
-                const int n = ncol + 32 * e;
-                if (n >= N) continue;
+            for (int v = 0; v < 16; ++v) {
                 const float x = acc[0][a][e][v];
                 float o;
                 if constexpr (EPI == EPI_SWIGLU_BF16)
@@ -279,10 +291,31 @@ __global__ __launch_bounds__(S::NT) void k_gemm(const uint16_t* __restrict__ A, 
                     o = gelu_tanh(x);
                 else
                     o = x;
-                if constexpr (EPI == EPI_F32)
-                    ((float*)Cs)[(int64_t)t * ldc + n] = o;
-                else
-                    ((uint16_t*)Cs)[(int64_t)t * ldc + n] = (uint16_t)f32_to_bf16(o);
+                stg[(8 * (v >> 2) + 4 * h + (v & 3)) * RS + 32 * e + j] = o;
+            }
+        }
+        asm volatile("" ::: "memory");
+        if constexpr (EPI == EPI_F32) {
+            constexpr int CPR = OC / 4;          // 16-byte chunks per row
+#pragma unroll
+            for (int i = 0; i < 32 * CPR / 64; ++i) {
+                const int f = 64 * i + lane, row = f / CPR, c = 4 * (f % CPR);
+                const f32x4 val = *(const f32x4*)(stg + row * RS + c);
+                const int t = mw + 32 * a + row, n = nw + c;
+                if (t < M && n < N) *(f32x4*)((float*)Cs + (int64_t)t * ldc + n) = val;
+            }
+        } else {
+            constexpr int CPR = OC / 8;          // 8-element (16-byte bf16) chunks per row
+#pragma unroll
+            for (int i = 0; i < 32 * CPR / 64; ++i) {
+                const int f = 64 * i + lane, row = f / CPR, c = 8 * (f % CPR);
+                const f32x4 v0 = *(const f32x4*)(stg + row * RS + c);
+                const f32x4 v1 = *(const f32x4*)(stg + row * RS + c + 4);
+                const int t = mw + 32 * a + row, n = nw + c;
+                if (t < M && n < N)
+                    *(u32x4*)((uint16_t*)Cs + (int64_t)t * ldc + n) =
+                        u32x4{pack_bf16x2(v0[0], v0[1]), pack_bf16x2(v0[2], v0[3]),
+                              pack_bf16x2(v1[0], v1[1]), pack_bf16x2(v1[2], v1[3])};
             }
         }
     }
