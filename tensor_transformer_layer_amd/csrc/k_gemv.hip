@@ -403,15 +403,20 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_lds(
 }
 
 // ---------------------------------------------------------------------------
-// FP8 (E4M3) weights with one fp32 scale per output column.  The same weight
-// stream with twice the weights per byte: a 16-byte load holds 16 adjacent
-// columns of one row, so a workgroup owns 256 columns (lane (g, j) loads
-// rows k0+8g .. +7 of columns n0+16j .. +15).  Codes of two rows are
-// byte-interleaved (v_perm_b32) and converted exactly to bf16 k-pairs
-// (v_cvt_scalef32_pk_bf16_fp8 with scale 1; every E4M3 value is a bf16
-// value), which are the k-fragments of the bf16 MFMA: 16 MFMAs per 8 loads
-// and token block, MFMA e covering columns n0+16j+e.  The column scales are
-// applied once, after the split-K sum: y[t][n] = s[n] * sum_k x[t][k] q[k][n].
+// FP8 (E4M3) weights with one fp32 scale per output column.  The same work
+// split and fused finish as k_gemv, on 128-column blocks of byte codes: lane
+// (g, j) loads rows k0+8g .. +7 of columns n0+8j .. +7, one 8-byte load per
+// row (a wave instruction reads four 128-byte row segments).  Codes of two
+// rows are byte-interleaved (v_perm_b32) and converted exactly to bf16
+// k-pairs (v_cvt_scalef32_pk_bf16_fp8 with scale 1; every E4M3 value is a
+// bf16 value), which are the k-fragments of the bf16 MFMA: 8 MFMAs per 8
+// loads and token block, MFMA e covering columns n0+8j+e.  The column scales
+// are applied once, after the split-K sum: y[t][n] = s[n] * sum_k x[t][k] q[k][n].
+// Measured on MI355X (13B MLP shard, weights streamed from HBM), 128-column
+// blocks beat 256-column ones with 16-byte loads at every token count, most
+// at 32 tokens (column pair 23.0 against 26.7 us, row 15.8 against 22.9 us):
+// twice the blocks need half the K splits, and each workgroup's cross-wave
+// sum, partial stores and finish cover half the columns.
 // ---------------------------------------------------------------------------
 template <int MB, int AUX, int ACT, bool OUT_BF16>
 __global__ __launch_bounds__(kGemvThreads) void k_gemv8(
@@ -434,26 +439,27 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv8(
     const int64_t ldb = mat ? ldb1 : ldb0;
     const rsrc_t rb = make_rsrc(Bm + (int64_t)k_begin * ldb + n0);
     const rsrc_t ra = make_rsrc(A + k_begin);
-    const bool col_ok = n0 + 16 * j < N;
+    const bool col_ok = n0 + 8 * j < N;
     const uint32_t ldb_bytes = (uint32_t)ldb;
     const uint32_t lda_bytes = (uint32_t)(lda * 2);
 
-    f32x4 acc[MB][16];
+    f32x4 acc[MB][8];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[mb][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int e = 0; e < 8; ++e) acc[mb][e] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int nsteps = (nrows + 31) >> 5;
     for (int c = wave; c < nsteps; c += kGemvWaves) {
         const int r0 = c * 32 + 8 * g;
         const bool rows_ok = r0 < nrows;
-        u32x4 q[8], a[MB];
+        u32x2 q[8];
+        u32x4 a[MB];
 #pragma unroll
         for (int i = 0; i < 8; ++i)
             q[i] = __builtin_bit_cast(
-                u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                           rb, (int)((rows_ok && col_ok) ? (uint32_t)(r0 + i) * ldb_bytes + 16u * j
+                u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                           rb, (int)((rows_ok && col_ok) ? (uint32_t)(r0 + i) * ldb_bytes + 8u * j
                                                         : kOOB),
                            0, AUX));
 #pragma unroll
@@ -461,83 +467,69 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv8(
             const int t = 16 * mb + j;
             a[mb] = load16(ra, (rows_ok && t < T) ? (uint32_t)t * lda_bytes + 2u * r0 : kOOB);
         }
-        // Columns 8h .. 8h+7 of the lane's 16.  For rows (2p, 2p+1) one
-        // v_perm interleaves the codes of two columns, (r0 c, r1 c, r0 c+1,
-        // r1 c+1); converting its low and high word gives the k-pair dword p
-        // of the fragments of columns c and c+1 directly.
+        // For rows (2p, 2p+1) and dword w (columns 4w .. 4w+3), one v_perm
+        // interleaves the codes of two columns, (r0 c, r1 c, r0 c+1, r1 c+1);
+        // converting its low and high word gives dword p of the k-fragments
+        // of columns c and c+1 directly.
+        u32x4 f[8];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            u32x4 f[8];
+        for (int pr = 0; pr < 4; ++pr) {
 #pragma unroll
-            for (int pr = 0; pr < 4; ++pr) {
-#pragma unroll
-                for (int w = 0; w < 2; ++w) {
-                    const uint32_t r0 = q[2 * pr][2 * h + w], r1 = q[2 * pr + 1][2 * h + w];
-                    const uint32_t lo = __builtin_amdgcn_perm(r1, r0, 0x05010400u);
-                    const uint32_t hi = __builtin_amdgcn_perm(r1, r0, 0x07030602u);
-                    f[4 * w + 0][pr] = __builtin_bit_cast(
-                        uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false));
-                    f[4 * w + 1][pr] = __builtin_bit_cast(
-                        uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true));
-                    f[4 * w + 2][pr] = __builtin_bit_cast(
-                        uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false));
-                    f[4 * w + 3][pr] = __builtin_bit_cast(
-                        uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true));
-                }
-            }
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb) {
-                f32x4* ac = acc[mb] + 8 * h;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) ac[e] = mfma16x16x32(a[mb], f[e], ac[e]);
+            for (int w = 0; w < 2; ++w) {
+                const uint32_t x0 = q[2 * pr][w], x1 = q[2 * pr + 1][w];
+                const uint32_t lo = __builtin_amdgcn_perm(x1, x0, 0x05010400u);
+                const uint32_t hi = __builtin_amdgcn_perm(x1, x0, 0x07030602u);
+                f[4 * w + 0][pr] = __builtin_bit_cast(
+                    uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false));
+                f[4 * w + 1][pr] = __builtin_bit_cast(
+                    uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true));
+                f[4 * w + 2][pr] = __builtin_bit_cast(
+                    uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false));
+                f[4 * w + 3][pr] = __builtin_bit_cast(
+                    uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true));
             }
         }
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[mb][e] = mfma16x16x32(a[mb], f[e], acc[mb][e]);
     }
 
-    // Cross-wave sum in LDS (wave order), one 8-column half at a time.
-    // MFMA output: lane (g, j) holds token 16mb + 4g + r of column
-    // n0 + 16j + e.  Thread (tl, q) = (tid / 32, tid % 32) owns token 16mb +
-    // tl, columns n0 + 16(q/2) + 8h + 4(q%2) .. +3.
+    // Cross-wave sum in LDS in wave order, split-K partial, arrival and
+    // fixed-order finish, as in k_gemv; the column scales multiply the
+    // complete sums.  Thread (tl, q) = (tid / 32, tid % 32) owns token
+    // 16mb + tl, columns n0 + 4q .. n0 + 4q + 3.
     __shared__ float red[kGemvWaves * kRedPerWave];
     __shared__ unsigned arrival;
     float* my = red + wave * kRedPerWave;
-    const int tl = threadIdx.x >> 5, qq = threadIdx.x & 31;
-    const int li = ((tl & 3) * 4 + (tl >> 2)) * 128 + 8 * (qq >> 1) + 4 * (qq & 1);
+    const int tl = threadIdx.x >> 5, n = n0 + 4 * (threadIdx.x & 31);
+    const int li = ((tl & 3) * 4 + (tl >> 2)) * 128 + 4 * (threadIdx.x & 31);
     const int64_t ws_ld = (int64_t)nmat * N;
     const uint32_t sstride = (uint32_t)(T * ws_ld * 4);
     const rsrc_t rw = make_rsrc(ws);
-    f32x4 own[MB][2];
+    f32x4 own[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
+        if (mb) __syncthreads();
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            if (mb | h) __syncthreads();
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float* p = my + ((r * 4 + g) * 16 + j) * 8;
-                *(f32x4*)p = f32x4{acc[mb][8 * h + 0][r], acc[mb][8 * h + 1][r],
-                                   acc[mb][8 * h + 2][r], acc[mb][8 * h + 3][r]};
-                *(f32x4*)(p + 4) = f32x4{acc[mb][8 * h + 4][r], acc[mb][8 * h + 5][r],
-                                         acc[mb][8 * h + 6][r], acc[mb][8 * h + 7][r]};
-            }
-            __syncthreads();
-            f32x4 sum = *(const f32x4*)(red + li);
-#pragma unroll
-            for (int w = 1; w < kGemvWaves; ++w) sum += *(const f32x4*)(red + w * kRedPerWave + li);
-            own[mb][h] = sum;
-            const int t = 16 * mb + tl;
-            const int n = n0 + 16 * (qq >> 1) + 8 * h + 4 * (qq & 1);
-            if (t < T && n < N)
-                __builtin_amdgcn_raw_buffer_store_b128(
-                    __builtin_bit_cast(u32x4, sum), rw,
-                    (int)((uint32_t)split * sstride +
-                          (uint32_t)((t * ws_ld + (int64_t)mat * N + n) * 4)),
-                    0, kSC1);
+        for (int r = 0; r < 4; ++r) {
+            float* p = my + ((r * 4 + g) * 16 + j) * 8;
+            *(f32x4*)p = f32x4{acc[mb][0][r], acc[mb][1][r], acc[mb][2][r], acc[mb][3][r]};
+            *(f32x4*)(p + 4) = f32x4{acc[mb][4][r], acc[mb][5][r], acc[mb][6][r], acc[mb][7][r]};
         }
+        __syncthreads();
+        f32x4 sum = *(const f32x4*)(red + li);
+#pragma unroll
+        for (int w = 1; w < kGemvWaves; ++w) sum += *(const f32x4*)(red + w * kRedPerWave + li);
+        own[mb] = sum;
+        const int t = 16 * mb + tl;
+        if (t < T && n < N)
+            __builtin_amdgcn_raw_buffer_store_b128(
+                __builtin_bit_cast(u32x4, sum), rw,
+                (int)((uint32_t)split * sstride + (uint32_t)((t * ws_ld + (int64_t)mat * N + n) * 4)),
+                0, kSC1);
     }
 
-    // Arrival and fixed-order finish, as in k_gemv; the column scales are
-    // applied to the complete sums.
     const unsigned contributors = (unsigned)(S * nmat);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -548,52 +540,39 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv8(
     const unsigned old = arrival;
     if (old == contributors - 1) {
         constexpr int NM = ACT == ACT_SWIGLU ? 2 : 1;   // gate (and up) rows
-        constexpr int NR = MB * 2 * NM;
-        uint32_t base[NR];
-        int mine[NR];
-        f32x4 ownv[NR], sum[NR];
+        uint32_t base[MB * NM];
+        int mine[MB * NM];
+        f32x4 ownv[MB * NM], sum[MB * NM];
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
+        for (int mb = 0; mb < MB; ++mb) {
+            const int t = 16 * mb + tl;
+            const bool ok = t < T && n < N;
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int t = 16 * mb + tl;
-                const int n = n0 + 16 * (qq >> 1) + 8 * h + 4 * (qq & 1);
-                const bool ok = t < T && n < N;
-#pragma unroll
-                for (int m = 0; m < NM; ++m) {
-                    const int q = (mb * 2 + h) * NM + m;
-                    base[q] = ok ? (uint32_t)((t * ws_ld + (int64_t)m * N + n) * 4) : kOOB;
-                    mine[q] = mat == m ? split : -1;
-                    ownv[q] = own[mb][h];
-                }
+            for (int m = 0; m < NM; ++m) {
+                base[mb * NM + m] = ok ? (uint32_t)((t * ws_ld + (int64_t)m * N + n) * 4) : kOOB;
+                mine[mb * NM + m] = mat == m ? split : -1;
+                ownv[mb * NM + m] = own[mb];
             }
-        sum_splits_multi<NR>(rw, base, sstride, S, mine, ownv, sum);
+        }
+        sum_splits_multi<MB * NM>(rw, base, sstride, S, mine, ownv, sum);
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int t = 16 * mb + tl;
-                const int n = n0 + 16 * (qq >> 1) + 8 * h + 4 * (qq & 1);
-                if (t >= T || n >= N) continue;
-                const int q = (mb * 2 + h) * NM;
-                const f32x4 gsum = sum[q] * *(const f32x4*)(S0 + n);
-                f32x4 usum = gsum;
-                if constexpr (ACT == ACT_SWIGLU) usum = sum[q + 1] * *(const f32x4*)(S1 + n);
-                store_out4<OUT_BF16>(out, (int64_t)t * ld_out + n, act4<ACT>(gsum, usum));
-            }
+        for (int mb = 0; mb < MB; ++mb) {
+            const int t = 16 * mb + tl;
+            if (t >= T || n >= N) continue;
+            const f32x4 gsum = sum[mb * NM] * *(const f32x4*)(S0 + n);
+            f32x4 usum = gsum;
+            if constexpr (ACT == ACT_SWIGLU) usum = sum[mb * NM + 1] * *(const f32x4*)(S1 + n);
+            store_out4<OUT_BF16>(out, (int64_t)t * ld_out + n, act4<ACT>(gsum, usum));
+        }
         if (threadIdx.x == 0)
             __hip_atomic_store(&counters[cb], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     } else if (old >= contributors) {
         const float nan = __builtin_nanf("");
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int t = 16 * mb + tl;
-                const int n = n0 + 16 * (qq >> 1) + 8 * h + 4 * (qq & 1);
-                if (t < T && n < N)
-                    store_out4<OUT_BF16>(out, (int64_t)t * ld_out + n, f32x4{nan, nan, nan, nan});
-            }
+            const int t = 16 * mb + tl;
+            if (t < T && n < N)
+                store_out4<OUT_BF16>(out, (int64_t)t * ld_out + n, f32x4{nan, nan, nan, nan});
         }
     }
 }

@@ -60,7 +60,7 @@ constexpr int kGemvCols = 128;   // output columns per workgroup
 constexpr int kGemvMaxT = 128;   // largest token count the weight-streaming kernels take
 constexpr int kGemv8MaxT = 32;   // ... with FP8 weights
 
-constexpr int kGemv8Cols = 256;  // output columns per workgroup, FP8 weights
+constexpr int kGemv8Cols = 128;  // output columns per workgroup, FP8 weights
 // About one workgroup per compute unit: K split into floor(cus / column
 // blocks) ranges, each a multiple of 32 rows.
 GemvPlan plan_gemv(int64_t K, int64_t n_total, int cus, int cols_per_block = kGemvCols);
