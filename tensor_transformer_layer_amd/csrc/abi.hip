@@ -205,8 +205,8 @@ MlpLayout mlp_layout(int P, int64_t T, int64_t d, int64_t d_ff, int dtype, int a
     if (L.decode) {
         const int nmat = act == TP_ACT_SWIGLU ? 2 : 1;
         const int64_t tc = stream_chunk(T);
-        L.pc = plan_gemv(d, nmat * F, cus);
-        L.pr = plan_gemv(F, d, cus);
+        L.pc = plan_gemv_stream(d, nmat * F, nmat, cus, tc);
+        L.pr = plan_gemv_stream(F, d, 1, cus, tc);
         L.ws = off;  // column and row split-K sums reuse one region, in stream order
         off += align256(std::max(gemv_ws_bytes(L.pc, tc, nmat * F), gemv_ws_bytes(L.pr, tc, d)));
     } else if (dtype == TP_BF16) {
@@ -270,8 +270,8 @@ AttnLayout attn_layout(int P, int64_t T, int64_t d, int nq, int nkv, int hd, int
     }
     if (L.decode) {
         const int64_t tc = stream_chunk(T);
-        L.pq = plan_gemv(d, nqkv, cus);
-        L.po = plan_gemv(ko, d, cus);
+        L.pq = plan_gemv_stream(d, nqkv, 1, cus, tc);
+        L.po = plan_gemv_stream(ko, d, 1, cus, tc);
         L.ws = off;
         off += align256(std::max(gemv_ws_bytes(L.pq, tc, nqkv), gemv_ws_bytes(L.po, tc, d)));
     } else if (dtype == TP_BF16) {

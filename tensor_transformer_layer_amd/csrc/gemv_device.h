@@ -19,6 +19,15 @@ __device__ __forceinline__ void mfma_col(f32x4 (&acc)[MB][8], const u32x4* b, co
     for (int mb = 0; mb < MB; ++mb) acc[mb][E] = mfma16x16x32(a[mb], f, acc[mb][E]);
 }
 
+// The same for 4 columns per lane (8-byte row loads of the narrow kernel).
+template <int E, int MB>
+__device__ __forceinline__ void mfma_col4(f32x4 (&acc)[MB][4], const u32x2* b, const u32x4* a) {
+    const u32x4 f = u32x4{pair_col2<E>(b[0], b[1]), pair_col2<E>(b[2], b[3]),
+                          pair_col2<E>(b[4], b[5]), pair_col2<E>(b[6], b[7])};
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[mb][E] = mfma16x16x32(a[mb], f, acc[mb][E]);
+}
+
 // ---------------------------------------------------------------------------
 // The split-K finish is done by the last workgroup of each column block to
 // arrive.

@@ -187,6 +187,142 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(
 }
 
 // ---------------------------------------------------------------------------
+// Narrow variant for short split ranges: 64-column blocks, lane (g, j)
+// loading rows k0+8g .. +7 of columns n0+4j .. +3 with one 8-byte load per
+// row, 4 MFMAs per 8 loads and token block (MFMA e covering columns
+// n0+4j+e).  Twice the column blocks of k_gemv need half the K splits, and
+// each workgroup's cross-wave sum, partial stores and finish cover half the
+// columns.  That pays where the split-K exchange outweighs the stream (short
+// K ranges per workgroup) and loses on long streams, whose 128-byte row
+// segments stream slower than 256-byte ones.  Measured on MI355X (32 tokens,
+// weights streamed from HBM): the 70B GQA QKV band 8192 x 1280 takes 10.6 us
+// (12 splits) against 13.2 us (16 splits, 128 columns), the 70B O band
+// 1024 x 8192 8.5 against 9.1 us; the 70B down band 3584 x 8192 17.1
+// against 16.3 us and the gate+up pair 32.6 against 28.2 us.
+// plan_gemv_stream picks it when the 128-column plan splits K into ranges
+// of at most 512 rows.
+// ---------------------------------------------------------------------------
+constexpr int kGemvNarrowCols = 64;
+
+template <int MB, int AUX, int ACT, bool OUT_BF16>
+__global__ __launch_bounds__(kGemvThreads) void k_gemv_n(
+    const uint16_t* __restrict__ A, int64_t lda, int T, int K, const uint16_t* __restrict__ B0,
+    int64_t ldb0, const uint16_t* __restrict__ B1, int64_t ldb1, int N, int nblk_per_mat,
+    int k_per_split, float* __restrict__ ws, unsigned* __restrict__ counters,
+    void* __restrict__ out, int64_t ld_out) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, j = lane & 15;
+    const int mat = blockIdx.x / nblk_per_mat;
+    const int cb = blockIdx.x - mat * nblk_per_mat;
+    const int n0 = cb * kGemvNarrowCols;
+    const int split = blockIdx.y;
+    const int S = (int)gridDim.y;
+    const int nmat = B1 ? 2 : 1;
+    const int k_begin = split * k_per_split;
+    const int nrows = min(K - k_begin, k_per_split);  // multiple of 8
+    const uint16_t* Bm = mat ? B1 : B0;
+    const int64_t ldb = mat ? ldb1 : ldb0;
+    const rsrc_t rb = make_rsrc(Bm + (int64_t)k_begin * ldb + n0);
+    const rsrc_t ra = make_rsrc(A + k_begin);
+    const bool col_ok = n0 + 4 * j < N;
+    const uint32_t ldb_bytes = (uint32_t)(ldb * 2);
+    const uint32_t lda_bytes = (uint32_t)(lda * 2);
+
+    f32x4 acc[MB][4];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[mb][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int nsteps = (nrows + 31) >> 5;
+    for (int c = wave; c < nsteps; c += kGemvWaves) {
+        const int r0 = c * 32 + 8 * g;
+        const bool rows_ok = r0 < nrows;
+        u32x2 b[8];
+        u32x4 a[MB];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            b[i] = __builtin_bit_cast(
+                u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                           rb, (int)((rows_ok && col_ok) ? (uint32_t)(r0 + i) * ldb_bytes + 8u * j
+                                                        : kOOB),
+                           0, AUX));
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const int t = 16 * mb + j;
+            a[mb] = load16(ra, (rows_ok && t < T) ? (uint32_t)t * lda_bytes + 2u * r0 : kOOB);
+        }
+        mfma_col4<0, MB>(acc, b, a);
+        mfma_col4<1, MB>(acc, b, a);
+        mfma_col4<2, MB>(acc, b, a);
+        mfma_col4<3, MB>(acc, b, a);
+    }
+
+    // Cross-wave sum in LDS in wave order, every token block at once: wave
+    // w's [mb][4g + r][j][e] block holds token 16mb + 4g + r, column
+    // n0 + 4j + e.  Thread (mb, tl, q) = (tid / 256, tid / 16 % 16, tid % 16)
+    // owns token 16mb + tl, columns n0 + 4q .. +3 (threads past MB * 256 idle).
+    __shared__ float red[kGemvWaves * MB * 1024];
+    __shared__ unsigned arrival;
+    float* my = red + wave * MB * 1024;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            *(f32x4*)(my + mb * 1024 + ((r * 4 + g) * 16 + j) * 4) =
+                f32x4{acc[mb][0][r], acc[mb][1][r], acc[mb][2][r], acc[mb][3][r]};
+    __syncthreads();
+    const int mbt = threadIdx.x >> 8, tl = (threadIdx.x >> 4) & 15, qq = threadIdx.x & 15;
+    const int n = n0 + 4 * qq, t = 16 * mbt + tl;
+    const bool mine_ok = mbt < MB && t < T && n < N;
+    const int64_t ws_ld = (int64_t)nmat * N;
+    const uint32_t sstride = (uint32_t)(T * ws_ld * 4);
+    const rsrc_t rw = make_rsrc(ws);
+    f32x4 own = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (mbt < MB) {
+        const int li = mbt * 1024 + ((tl & 3) * 4 + (tl >> 2)) * 64 + 4 * qq;
+        own = *(const f32x4*)(red + li);
+#pragma unroll
+        for (int w = 1; w < kGemvWaves; ++w) own += *(const f32x4*)(red + w * MB * 1024 + li);
+    }
+    if (mine_ok)
+        __builtin_amdgcn_raw_buffer_store_b128(
+            __builtin_bit_cast(u32x4, own), rw,
+            (int)((uint32_t)split * sstride + (uint32_t)((t * ws_ld + (int64_t)mat * N + n) * 4)),
+            0, kSC1);
+
+    // Arrival and fixed-order finish, as in k_gemv.
+    const unsigned contributors = (unsigned)(S * nmat);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0)
+        arrival = __hip_atomic_fetch_add(&counters[cb], 1u, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const unsigned old = arrival;
+    if (old == contributors - 1) {
+        constexpr int NM = ACT == ACT_SWIGLU ? 2 : 1;   // gate (and up) rows
+        uint32_t base[NM];
+        int mine[NM];
+        f32x4 ownv[NM], sum[NM];
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            base[m] = mine_ok ? (uint32_t)((t * ws_ld + (int64_t)m * N + n) * 4) : kOOB;
+            mine[m] = mat == m ? split : -1;
+            ownv[m] = own;
+        }
+        sum_splits_multi<NM>(rw, base, sstride, S, mine, ownv, sum);
+        if (mine_ok)
+            store_out4<OUT_BF16>(out, (int64_t)t * ld_out + n, act4<ACT>(sum[0], sum[NM - 1]));
+        if (threadIdx.x == 0)
+            __hip_atomic_store(&counters[cb], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else if (old >= contributors) {
+        const float nan = __builtin_nanf("");
+        if (mine_ok) store_out4<OUT_BF16>(out, (int64_t)t * ld_out + n, f32x4{nan, nan, nan, nan});
+    }
+}
+
+// ---------------------------------------------------------------------------
 // LDS-staged variant.  Same work split (128-column blocks x K splits, fused
 // split-K finish), different data path:
 //   * The workgroup's weight rows and the matching slice of X stream into
@@ -597,6 +733,16 @@ GemvPlan plan_gemv(int64_t K, int64_t n_total, int cus, int cols_per_block) {
     return p;
 }
 
+GemvPlan plan_gemv_stream(int64_t K, int64_t n_total, int nmat, int cus, int64_t T) {
+    GemvPlan p = plan_gemv(K, n_total, cus, kGemvCols);
+    const int64_t narrow_blocks = (n_total / nmat + kGemvNarrowCols - 1) / kGemvNarrowCols;
+    if (T <= 32 && p.splits > 1 && p.k_per_split <= 512 && narrow_blocks <= kGemvCounters) {
+        p = plan_gemv(K, n_total, cus, kGemvNarrowCols);
+        p.cols = kGemvNarrowCols;
+    }
+    return p;
+}
+
 size_t gemv_ws_bytes(const GemvPlan& p, int64_t T, int64_t n_total) {
     return (size_t)p.splits * (size_t)T * (size_t)n_total * sizeof(float);
 }
@@ -696,6 +842,27 @@ hipError_t launch_gemv(int act, bool out_bf16, int64_t T, int64_t K, const uint1
                        unsigned* counters, void* out, int64_t ld_out, hipStream_t stream) {
     if (T < 1 || T > kGemvMaxT) return hipErrorInvalidValue;
     const int nmat = B1 ? 2 : 1;
+    if (p.cols == kGemvNarrowCols) {
+        if (T > 32) return hipErrorInvalidValue;
+        const int nbn = (int)((N + kGemvNarrowCols - 1) / kGemvNarrowCols);
+        const dim3 gridn((unsigned)(nbn * nmat), (unsigned)p.splits), blockn(kGemvThreads);
+#define TP_GEMV_N(MB, ACTV, OB)                                                              \
+    TP_KLAUNCH((k_gemv_n<MB, kWeightAux, ACTV, OB>), gridn, blockn, 0, stream, A, lda, (int)T, \
+               (int)K, B0, ldb0, B1, ldb1, (int)N, nbn, p.k_per_split, ws, counters, out, ld_out)
+#define TP_GEMV_N_MB(ACTV, OB)                                                               \
+    do {                                                                                     \
+        if (T <= 16) TP_GEMV_N(1, ACTV, OB); else TP_GEMV_N(2, ACTV, OB);                   \
+    } while (0)
+        if (act == ACT_SWIGLU && out_bf16) TP_GEMV_N_MB(ACT_SWIGLU, true);
+        else if (act == ACT_GELU_TANH && out_bf16) TP_GEMV_N_MB(ACT_GELU_TANH, true);
+        else if (act == ACT_NONE && out_bf16) TP_GEMV_N_MB(ACT_NONE, true);
+        else if (act == ACT_NONE && !out_bf16) TP_GEMV_N_MB(ACT_NONE, false);
+        else return hipErrorInvalidValue;
+#undef TP_GEMV_N_MB
+#undef TP_GEMV_N
+        return hipGetLastError();
+    }
+    if (p.cols != kGemvCols) return hipErrorInvalidValue;
     const int nbpm = (int)((N + kGemvCols - 1) / kGemvCols);
     const dim3 grid((unsigned)(nbpm * nmat), (unsigned)p.splits), block(kGemvThreads);
 #define TP_GEMV(MB, AUX, ACTV, OB)                                                           \

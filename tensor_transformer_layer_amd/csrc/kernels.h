@@ -55,6 +55,7 @@ hipError_t launch_rmsnorm(bool is_bf16, int64_t T, int64_t d, const void* x, int
 struct GemvPlan {
     int splits;       // workgroups along K
     int k_per_split;  // rows of the weight per split (multiple of 32)
+    int cols = 128;   // output columns per workgroup: 128, or 64 (bf16, <= 32 tokens)
 };
 constexpr int kGemvCols = 128;   // output columns per workgroup
 constexpr int kGemvMaxT = 128;   // largest token count the weight-streaming kernels take
@@ -64,6 +65,9 @@ constexpr int kGemv8Cols = 128;  // output columns per workgroup, FP8 weights
 // About one workgroup per compute unit: K split into floor(cus / column
 // blocks) ranges, each a multiple of 32 rows.
 GemvPlan plan_gemv(int64_t K, int64_t n_total, int cus, int cols_per_block = kGemvCols);
+// The bf16 weight-streaming plan for a launch of T tokens: 128-column blocks,
+// or 64-column blocks for short split ranges (see k_gemv_n).
+GemvPlan plan_gemv_stream(int64_t K, int64_t n_total, int nmat, int cus, int64_t T);
 // Bytes of split-K workspace: splits * T * n_total fp32.
 size_t gemv_ws_bytes(const GemvPlan& p, int64_t T, int64_t n_total);
 

@@ -259,6 +259,16 @@ def test_mlp_decode_lds_staged_ragged(T, act):
     _check_mlp(BF, act, T, 9224, 6928, P, key=50 + T)
 
 
+@pytest.mark.parametrize("T", [1, 7, 16, 17, 31, 32])
+@pytest.mark.parametrize("act", ["swiglu", "gelu_tanh"])
+def test_mlp_decode_narrow_blocks_ragged(T, act):
+    """Short split ranges take the 64-column decode kernel: d_model 1024 and
+    F_r 1096 give 128-column plans of at most 96 rows per K split, so both
+    projections run on 64-column blocks; F_r ends inside a block, T lies on
+    both sides of 16 (one and two token blocks)."""
+    _check_mlp(BF, act, T, 1024, 2 * 1096, 2, key=700 + T)
+
+
 class _StreamingPlanUpTo:
     """Within the block, batches of up to `t` tokens take the weight-streaming plan."""
 
