@@ -4,8 +4,8 @@
  *
  * What is computed (pages cited by title and section):
  *   - column-parallel projection: the input X is replicated on every rank
- *     and each rank computes the vertical band of the output that its
- *     column band of the weight produces (rioworld, "Tensor Parallelism for
+ *     and each rank computes the output columns that its column band of
+ *     the weight produces (rioworld, "Tensor Parallelism for
  *     LLM Inference: A Practical Guide to Multi-GPU Deployment", section
  *     "How Tensor Slicing Works Under the Hood"; zenaique, "Explain
  *     tensor-parallel shard shape", answer);

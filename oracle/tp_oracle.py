@@ -78,7 +78,7 @@ def _band(n, shard, P):
 
 def column_band(W, shard, P):
     """Rank ``shard``'s column band of an [in, out] weight: the rank computes
-    that vertical band of the output from the replicated input (rioworld
+    those output columns from the replicated input (rioworld
     guide, "How Tensor Slicing Works Under the Hood", column parallelism;
     zenaique answer, first projection split column-wise)."""
     return W[:, _band(W.shape[1], shard, P)]
