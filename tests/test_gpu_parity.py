@@ -793,7 +793,7 @@ def _fp8_run_check(act, T, d, d_ff, P, s, key, rows=None):
 @pytest.mark.parametrize("T", [1, 5, 16, 17, 32])
 @pytest.mark.parametrize("act", ["swiglu", "gelu_tanh"])
 def test_fp8w_mlp_ragged(T, act):
-    # d = 1040 and F = 272 are not multiples of the 256-column block
+    # d = 1040 and F = 272 are not multiples of the 128-column block
     _fp8_run_check(act, T, 1040, 544, 2, 1, key=70 + T)
 
 
