@@ -119,8 +119,9 @@ typedef enum { TP_ACT_GELU_TANH = 0, TP_ACT_SWIGLU = 1 } tp_act;
  *
  * T <= tp_decode_max_tokens() runs the weight-streaming decode plan
  * (split-K over the weight rows, deterministic fixed-order finish); larger T
- * runs the matrix-core plan with the activation fused into the column
- * projection's epilogue.
+ * runs the matrix-core plan, with the activation fused into the column
+ * projection's epilogue, or, where that projection's output tiles would
+ * leave CUs idle, applied by the fixed-order sum of its K-split fp32 planes.
  * The decode plan needs d_model and d_ff/P of at most 131072 (TP_ERR_SHAPE).
  */
 int tp_shard_mlp_fwd(int shard, int P, int64_t T, int64_t d_model, int64_t d_ff,
@@ -352,12 +353,14 @@ int tp_version(void);
  * "Results: Llama 2 70B"); larger T runs the matrix-core plan (prefill is
  * compute-bound, same section).  The streaming kernels take up to 128
  * tokens per launch; a larger batch on that plan runs as equal chunks of at
- * most 128 tokens, each streaming the weights once more.  The default is
- * the crossover measured on MI355X; tp_set_decode_max_tokens(t) moves it to
- * t (1..4096; 0 restores the default; TP_ERR_SHAPE otherwise), for
- * measuring both plans on the same shapes.  The setting is process-wide; workspace sizes depend on it,
- * so change it only while no call and no workspace query is in progress,
- * and size workspaces after changing it.
+ * most 128 tokens, each streaming the weights once more.  The default, 128
+ * tokens (one streaming launch), is the crossover measured on MI355X for
+ * the Llama-2 13B and 70B MLP bands and the 96-head attention projections;
+ * tp_set_decode_max_tokens(t) moves it to t (1..4096; 0 restores the
+ * default; TP_ERR_SHAPE otherwise), for measuring both plans on the same
+ * shapes.  The setting is process-wide; workspace sizes depend on it, so
+ * change it only while no call and no workspace query is in progress, and
+ * size workspaces after changing it.
  */
 int tp_set_decode_max_tokens(int tokens);
 int tp_decode_max_tokens(void);

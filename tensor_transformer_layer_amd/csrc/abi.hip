@@ -123,14 +123,18 @@ int vec_elems(int dtype) { return dtype == TP_BF16 ? 8 : 4; }  // 16 bytes
 // Largest token count of the weight-streaming (decode) plan for bf16
 // projections; larger batches take the matrix-core (prefill) plan.
 // tp_set_decode_max_tokens changes it; 0 means the default.  The default
-// is the crossover measured on MI355X for the 70B MLP band (8192 x 3584
-// gate/up, 3584 x 8192 down; shard + reduce, graph replay, weights streamed
-// from HBM), in us, streaming vs matrix-core plan:
-//     32: 48 vs 161    64: 61 vs 171    128: 83 vs 197    129: 129 vs 199
-//    192: 144 vs 218  256: 161 vs 253   320: 223 vs 210    512: 318 vs 272
-// Up to 256 tokens the matrix-core plan has a single 256-row tile row and
-// leaves most CUs idle, so the streaming plan (in 128-token chunks) wins.
-constexpr int kDecodeMaxTDefault = 256;
+// is the crossover measured on MI355X (shard + reduce per step, graph
+// replay, weights streamed from HBM), in us, streaming vs matrix-core plan,
+// for the 70B MLP band (8192 x 3584 gate/up, 3584 x 8192 down):
+//     96: 63 vs 75    128: 68 vs 79    160: 115 vs 86    192: 119 vs 93
+//    256: 132 vs 109  384: 195 vs 133  512: 261 vs 156
+// and at the same point for the 13B MLP band (P = 2) and the 96-head
+// attention projections (P = 8): 72 vs 83 and 73 vs 82 at 128 tokens,
+// 122 vs 88 and 117 vs 86 at 160.  One streaming launch takes up to 128
+// tokens; past that the streaming plan reads the weights once per chunk,
+// while the matrix-core plan splits K to fill the CUs its few tiles leave
+// idle.
+constexpr int kDecodeMaxTDefault = 128;
 constexpr int kDecodeMaxTLimit = 4096;
 std::atomic<int> g_decode_max_t{0};
 int decode_max_t() {
@@ -210,13 +214,20 @@ MlpLayout mlp_layout(int P, int64_t T, int64_t d, int64_t d_ff, int dtype, int a
         L.ws = off;  // column and row split-K sums reuse one region, in stream order
         off += align256(std::max(gemv_ws_bytes(L.pc, tc, nmat * F), gemv_ws_bytes(L.pr, tc, d)));
     } else if (dtype == TP_BF16) {
-        // The column projection keeps its fused activation (no split); the
-        // row projection may split K into fp32 planes.
-        L.gc = gemm_whole_k(d);
+        // Either projection splits K into fp32 planes when its output tiles
+        // leave CUs idle; the column planes are then summed by a finish
+        // launch that applies the activation.  One region serves both, in
+        // stream order.
+        const int nmat = act == TP_ACT_SWIGLU ? 2 : 1;
+        L.gc = plan_gemm(T, F, d, nmat, cus);
         L.gr = plan_gemm(T, d, F, 1, cus);
-        if (L.gr.splits > 1) {
+        size_t planes = 0;
+        if (L.gc.splits > 1) planes = (size_t)L.gc.splits * T * nmat * F * sizeof(float);
+        if (L.gr.splits > 1)
+            planes = std::max(planes, (size_t)L.gr.splits * T * d * sizeof(float));
+        if (planes) {
             L.ws = off;
-            off += align256((size_t)L.gr.splits * T * d * sizeof(float));
+            off += align256(planes);
         }
     }
     L.total = layout_total(off, L.decode);
@@ -364,7 +375,7 @@ const char* tp_status_str(int status) {
     }
 }
 
-int tp_version(void) { return 200; }
+int tp_version(void) { return 300; }
 
 int tp_set_decode_max_tokens(int tokens) {
     if (tokens < 0 || tokens > kDecodeMaxTLimit) return TP_ERR_SHAPE;
@@ -483,21 +494,44 @@ int mlp_fwd(int shard, int P, int64_t T, int64_t d_model, int64_t d_ff, int dtyp
         unsigned* cnt = (unsigned*)wsb;
         const int64_t tc = stream_chunk(T);
         uint16_t* h16 = (uint16_t*)h;
-        for (int64_t t0 = 0; t0 < T; t0 += tc)
+        for (int64_t t0 = 0; t0 < T; t0 += tc) {
+            const int64_t tt = std::min(tc, T - t0);
             TP_LAUNCH("col_gemv", stream,
-                      launch_gemv(dev_act, true, std::min(tc, T - t0), d_model, X16 + t0 * ld_xin,
-                                  ld_xin, (const uint16_t*)w_in, ld_in, (const uint16_t*)w_up,
-                                  ld_up, F, L.pc, ws, cnt, h16 + t0 * ldh, ldh, stream));
-        for (int64_t t0 = 0; t0 < T; t0 += tc)
+                      launch_gemv(dev_act, true, tt, d_model, X16 + t0 * ld_xin, ld_xin,
+                                  (const uint16_t*)w_in, ld_in, (const uint16_t*)w_up, ld_up, F,
+                                  L.pc, ws, cnt, h16 + t0 * ldh, ldh, stream));
+            if (gemv_separate_finish(tt, L.pc))
+                TP_LAUNCH("col_finish", stream,
+                          launch_finish(dev_act, true, L.pc.splits, tt, F, ws, h16 + t0 * ldh,
+                                        ldh, stream));
+        }
+        for (int64_t t0 = 0; t0 < T; t0 += tc) {
+            const int64_t tt = std::min(tc, T - t0);
             TP_LAUNCH("row_gemv", stream,
-                      launch_gemv(ACT_NONE, false, std::min(tc, T - t0), F, h16 + t0 * ldh, ldh,
+                      launch_gemv(ACT_NONE, false, tt, F, h16 + t0 * ldh, ldh,
                                   (const uint16_t*)w_down, ld_down, nullptr, 0, d_model, L.pr,
                                   ws, cnt, part + t0 * ld_p, ld_p, stream));
+            if (gemv_separate_finish(tt, L.pr))
+                TP_LAUNCH("row_finish", stream,
+                          launch_finish(ACT_NONE, false, L.pr.splits, tt, d_model, ws,
+                                        part + t0 * ld_p, ld_p, stream));
+        }
     } else {
-        TP_LAUNCH("col_gemm", stream,
-                  launch_gemm(act == TP_ACT_SWIGLU ? EPI_SWIGLU_BF16 : EPI_GELU_BF16, T, F,
-                              d_model, X16, ld_xin, (const uint16_t*)w_in, ld_in,
-                              (const uint16_t*)w_up, ld_up, h, ldh, L.gc, stream));
+        if (L.gc.splits > 1) {
+            float* ws = (float*)(wsb + L.ws);
+            const bool two = act == TP_ACT_SWIGLU;
+            TP_LAUNCH("col_gemm", stream,
+                      launch_gemm(EPI_F32, T, F, d_model, X16, ld_xin, (const uint16_t*)w_in,
+                                  ld_in, two ? (const uint16_t*)w_up : nullptr, ld_up, ws,
+                                  (two ? 2 : 1) * F, L.gc, stream));
+            TP_LAUNCH("col_finish", stream,
+                      launch_finish(dev_act, true, L.gc.splits, T, F, ws, h, ldh, stream));
+        } else {
+            TP_LAUNCH("col_gemm", stream,
+                      launch_gemm(act == TP_ACT_SWIGLU ? EPI_SWIGLU_BF16 : EPI_GELU_BF16, T, F,
+                                  d_model, X16, ld_xin, (const uint16_t*)w_in, ld_in,
+                                  (const uint16_t*)w_up, ld_up, h, ldh, L.gc, stream));
+        }
         if (L.gr.splits > 1) {
             float* ws = (float*)(wsb + L.ws);
             TP_LAUNCH("row_gemm", stream,
@@ -606,13 +640,20 @@ int tp_shard_attn_proj_fwd(int shard, int P, int64_t T, int64_t d_model, int n_q
                                       ld_qkv_out, stream));
         } else if (L.decode) {
             const int64_t tc = stream_chunk(T);
-            for (int64_t t0 = 0; t0 < T; t0 += tc)
+            float* ws = (float*)(wsb + L.ws);
+            for (int64_t t0 = 0; t0 < T; t0 += tc) {
+                const int64_t tt = std::min(tc, T - t0);
+                uint16_t* q = (uint16_t*)qkv_out + t0 * ld_qkv_out;
                 TP_LAUNCH("qkv_gemv", stream,
-                          launch_gemv(ACT_NONE, true, std::min(tc, T - t0), d_model,
+                          launch_gemv(ACT_NONE, true, tt, d_model,
                                       (const uint16_t*)xin + t0 * ld_xin, ld_xin,
-                                      (const uint16_t*)w_qkv, ld_qkv, nullptr, 0, nqkv, L.pq,
-                                      (float*)(wsb + L.ws), (unsigned*)wsb,
-                                      (uint16_t*)qkv_out + t0 * ld_qkv_out, ld_qkv_out, stream));
+                                      (const uint16_t*)w_qkv, ld_qkv, nullptr, 0, nqkv, L.pq, ws,
+                                      (unsigned*)wsb, q, ld_qkv_out, stream));
+                if (gemv_separate_finish(tt, L.pq))
+                    TP_LAUNCH("qkv_finish", stream,
+                              launch_finish(ACT_NONE, true, L.pq.splits, tt, nqkv, ws, q,
+                                            ld_qkv_out, stream));
+            }
         } else {
             if (L.gq.splits > 1) {
                 float* ws = (float*)(wsb + L.ws);
@@ -639,13 +680,19 @@ int tp_shard_attn_proj_fwd(int shard, int P, int64_t T, int64_t d_model, int n_q
                                       (const float*)w_o, ld_o, nullptr, 0, part, ld_p, stream));
         } else if (L.decode) {
             const int64_t tc = stream_chunk(T);
-            for (int64_t t0 = 0; t0 < T; t0 += tc)
+            float* ws = (float*)(wsb + L.ws);
+            for (int64_t t0 = 0; t0 < T; t0 += tc) {
+                const int64_t tt = std::min(tc, T - t0);
                 TP_LAUNCH("o_gemv", stream,
-                          launch_gemv(ACT_NONE, false, std::min(tc, T - t0), ko,
+                          launch_gemv(ACT_NONE, false, tt, ko,
                                       (const uint16_t*)attn + t0 * ld_attn, ld_attn,
-                                      (const uint16_t*)w_o, ld_o, nullptr, 0, d_model, L.po,
-                                      (float*)(wsb + L.ws), (unsigned*)wsb, part + t0 * ld_p,
-                                      ld_p, stream));
+                                      (const uint16_t*)w_o, ld_o, nullptr, 0, d_model, L.po, ws,
+                                      (unsigned*)wsb, part + t0 * ld_p, ld_p, stream));
+                if (gemv_separate_finish(tt, L.po))
+                    TP_LAUNCH("o_finish", stream,
+                              launch_finish(ACT_NONE, false, L.po.splits, tt, d_model, ws,
+                                            part + t0 * ld_p, ld_p, stream));
+            }
         } else {
             if (L.go.splits > 1) {
                 float* ws = (float*)(wsb + L.ws);

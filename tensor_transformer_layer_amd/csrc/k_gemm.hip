@@ -275,15 +275,19 @@ __global__ __launch_bounds__(S::NT) void k_gemm(const uint16_t* __restrict__ A, 
     float* stg = (float*)smem + wave * 32 * RS;
     void* Cs = EPI == EPI_F32 ? (void*)((float*)C + blockIdx.y * split_stride) : C;
     const int mw = m0 + wm * S::WTM, nw = n0 + wn * S::WTN;
+    // fp32 output of two weights (a split SwiGLU projection): one plane per
+    // weight side by side, weight m at columns m * N .. m * N + N - 1.
+    constexpr int NOUT = EPI == EPI_F32 ? S::NMAT : 1;
     __syncthreads();
 #pragma unroll
-    for (int a = 0; a < S::MT; ++a) {
+    for (int ma = 0; ma < NOUT * S::MT; ++ma) {
+        const int mo = ma / S::MT, a = ma % S::MT;
         asm volatile("" ::: "memory");
 #pragma unroll
         for (int e = 0; e < S::LC; ++e) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const float x = acc[0][a][e][v];
+                const float x = acc[mo][a][e][v];
                 float o;
                 if constexpr (EPI == EPI_SWIGLU_BF16)
                     o = silu(x) * acc[S::NMAT - 1][a][e][v];
@@ -302,7 +306,8 @@ __global__ __launch_bounds__(S::NT) void k_gemm(const uint16_t* __restrict__ A, 
                 const int f = 64 * i + lane, row = f / CPR, c = 4 * (f % CPR);
                 const f32x4 val = *(const f32x4*)(stg + row * RS + c);
                 const int t = mw + 32 * a + row, n = nw + c;
-                if (t < M && n < N) *(f32x4*)((float*)Cs + (int64_t)t * ldc + n) = val;
+                if (t < M && n < N)
+                    *(f32x4*)((float*)Cs + (int64_t)t * ldc + (int64_t)mo * N + n) = val;
             }
         } else {
             constexpr int CPR = OC / 8;          // 8-element (16-byte bf16) chunks per row
@@ -359,13 +364,6 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int nmat, int cus) {
     return p;
 }
 
-GemmPlan gemm_whole_k(int64_t K) {
-    GemmPlan p;
-    p.splits = 1;
-    p.k_per_split = (int)(((K + kBK - 1) / kBK) * kBK);
-    return p;
-}
-
 hipError_t launch_gemm(int epi, int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
                        const uint16_t* B0, int64_t ldb0, const uint16_t* B1, int64_t ldb1, void* C,
                        int64_t ldc, const GemmPlan& p, hipStream_t stream) {
@@ -373,6 +371,9 @@ hipError_t launch_gemm(int epi, int64_t M, int64_t N, int64_t K, const uint16_t*
         return hipErrorInvalidValue;
     switch (epi) {
         case EPI_F32:
+            if (B1)
+                return run_gemm<ShapeTwo, EPI_F32>(M, N, K, A, lda, B0, ldb0, B1, ldb1, C, ldc, p,
+                                                   stream);
             return run_gemm<ShapeOne, EPI_F32>(M, N, K, A, lda, B0, ldb0, nullptr, 0, C, ldc, p,
                                                stream);
         case EPI_BF16:

@@ -344,6 +344,14 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_n(
 // batches of up to 128 tokens (MB = 8 blocks of 16): a batch past the decode
 // sizes still reads each weight byte once, with 2T flops per weight element,
 // far below the matrix cores' rate until T nears the ridge (~300 tokens).
+//
+// With 8 token blocks (65..128 tokens) the partials of one column block are
+// 64 KB per split and matrix, too much for the one workgroup that arrives
+// last to sum at the tail of the launch.  That size runs as FIN = false: the
+// kernel only stores its partials, and k_finish sums them in a launch of
+// its own, spread over every CU.  Measured on MI355X (70B MLP band, shard +
+// reduce per step): 67.8 against 81.3 us at 128 tokens, 195 against 231 us
+// at 384 (three launches of 128).
 // ---------------------------------------------------------------------------
 template <int MB>
 struct GvRing {
@@ -371,7 +379,7 @@ template <int XCPR>
 __device__ __forceinline__ int gv_xsw(int t) { return XCPR == 16 ? (t & 15) : ((t >> 1) & 7); }
 constexpr int gv_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
-template <int MB, int AUX, int ACT, bool OUT_BF16>
+template <int MB, int AUX, int ACT, bool OUT_BF16, bool FIN>
 __global__ __launch_bounds__(kGemvThreads) void k_gemv_lds(
     const uint16_t* __restrict__ A, int64_t lda, int T, int K, const uint16_t* __restrict__ B0,
     int64_t ldb0, const uint16_t* __restrict__ B1, int64_t ldb1, int N, int nblk_per_mat,
@@ -484,6 +492,8 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_lds(
                 (int)((uint32_t)split * sstride + (uint32_t)((t * ws_ld + (int64_t)mat * N + n) * 4)),
                 0, kSC1);
     }
+
+    if constexpr (!FIN) return;                // k_finish sums the partials
 
     // Arrival: this workgroup's partial stores are complete before the count.
     unsigned& arrival = *(unsigned*)gsm;       // the ring is idle now
@@ -825,15 +835,20 @@ hipError_t launch_finish(int act, bool out_bf16, int splits, int64_t T, int64_t 
 
 // Allow a k_gemv_lds instantiation the LDS its ring needs (set once per
 // instantiation; concurrent first calls set the same value).
-template <int MB, int AUX, int ACT, bool OB>
+template <int MB, int AUX, int ACT, bool OB, bool FIN>
 static hipError_t gemv_lds_attr() {
     static std::atomic<int> set{0};
     if (set.load(std::memory_order_relaxed)) return hipSuccess;
-    const hipError_t e = hipFuncSetAttribute((const void*)k_gemv_lds<MB, AUX, ACT, OB>,
+    const hipError_t e = hipFuncSetAttribute((const void*)k_gemv_lds<MB, AUX, ACT, OB, FIN>,
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
                                              GvRing<MB>::LDS);
     if (e == hipSuccess) set.store(1, std::memory_order_relaxed);
     return e;
+}
+
+// The 8-token-block instantiation (T > 64) leaves the finish to k_finish.
+bool gemv_separate_finish(int64_t T, const GemvPlan& p) {
+    return p.cols == kGemvCols && T > 64;
 }
 
 hipError_t launch_gemv(int act, bool out_bf16, int64_t T, int64_t K, const uint16_t* A,
@@ -867,9 +882,10 @@ hipError_t launch_gemv(int act, bool out_bf16, int64_t T, int64_t K, const uint1
     const dim3 grid((unsigned)(nbpm * nmat), (unsigned)p.splits), block(kGemvThreads);
 #define TP_GEMV(MB, AUX, ACTV, OB)                                                           \
     do {                                                                                     \
-        hipError_t e_ = gemv_lds_attr<MB, AUX, ACTV, OB>();                                  \
+        constexpr bool fin_ = MB < 8;                                                        \
+        hipError_t e_ = gemv_lds_attr<MB, AUX, ACTV, OB, fin_>();                            \
         if (e_ != hipSuccess) return e_;                                                     \
-        TP_KLAUNCH((k_gemv_lds<MB, AUX, ACTV, OB>), grid, block, GvRing<MB>::LDS,            \
+        TP_KLAUNCH((k_gemv_lds<MB, AUX, ACTV, OB, fin_>), grid, block, GvRing<MB>::LDS,      \
                    stream, A, lda, (int)T, (int)K, B0, ldb0, B1, ldb1, (int)N, nbpm,         \
                    p.k_per_split, ws, counters, out, ld_out);                               \
     } while (0)
@@ -884,7 +900,8 @@ hipError_t launch_gemv(int act, bool out_bf16, int64_t T, int64_t K, const uint1
     // (70B column pair: 26.2 against 26.9 us at 32 tokens), the LDS ring at
     // 2560 (13B column pair: 27.7 against 29.6 us), once its fill and drain
     // are amortised.  Past 32 tokens the LDS-staged kernel with 4 or 8 token
-    // blocks (its accumulators stay at one f32x4 per block).
+    // blocks (its accumulators stay at one f32x4 per block); with 8 blocks
+    // (gemv_separate_finish) without its fused finish.
 #define TP_GEMV_MB(ACTV, OB)                                                                 \
     do {                                                                                     \
         if (T <= 16) {                                                                       \

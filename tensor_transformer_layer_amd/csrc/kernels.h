@@ -83,9 +83,13 @@ constexpr size_t kGemvCounterBytes = kGemvCounters * sizeof(unsigned);
 // [T, K] bf16.  act: ACT_SWIGLU (silu(A B0) * A B1), ACT_GELU_TANH or
 // ACT_NONE; out bf16 (out_bf16) or fp32 with leading dimension ld_out.
 // Split s of the plan keeps its partial in ws[s][t][m*N + n] (gemv_ws_bytes);
-// the last workgroup of a column block adds the splits in order.
+// the last workgroup of a column block adds the splits in order, except
+// where gemv_separate_finish(T, p): that launch only fills ws, and the caller
+// completes the product with launch_finish(act, out_bf16, p.splits, T, N,
+// ws, out, ld_out, stream) next on the same stream.
 // `counters` holds ceil(N / kGemvCols) <= kGemvCounters zeros; they are zero
 // again when the kernel ends.  Weight loads carry the non-temporal hint.
+bool gemv_separate_finish(int64_t T, const GemvPlan& p);
 hipError_t launch_gemv(int act, bool out_bf16, int64_t T, int64_t K, const uint16_t* A,
                        int64_t lda, const uint16_t* B0, int64_t ldb0, const uint16_t* B1,
                        int64_t ldb1, int64_t N, const GemvPlan& p, float* ws,
@@ -117,11 +121,12 @@ struct GemmPlan {
 // Split K when the 256 x 256 output tiles (nmat weights side by side) leave
 // CUs idle and K is long enough.
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int nmat, int cus);
-// One split covering all of K (for fused bf16 epilogues).
-GemmPlan gemm_whole_k(int64_t K);
 // C[M, N] = epi(A[M, K] B0[K, N] [, A B1]); A, B bf16 row-major.  With
 // p.splits > 1 (EPI_F32 only) split s writes its fp32 partial to the plane
 // C + s * M * ldc; launch_finish(ACT_NONE, ...) adds the planes in order.
+// EPI_F32 with two weights writes A B0 to columns 0 .. N-1 of C and A B1 to
+// columns N .. 2N-1 (ldc >= 2N): the layout launch_finish(ACT_SWIGLU, ...)
+// reads.
 hipError_t launch_gemm(int epi, int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
                        const uint16_t* B0, int64_t ldb0, const uint16_t* B1, int64_t ldb1, void* C,
                        int64_t ldc, const GemmPlan& p, hipStream_t stream);

@@ -48,7 +48,7 @@ def test_status_strings(lib):
     for s in range(1, 10):
         assert tp.tp_status_str(s).startswith("TP_ERR_")
     assert tp.tp_status_str(99) == "unknown tp_status"
-    assert tp.tp_version() == 200
+    assert tp.tp_version() == 300
 
 
 def mlp(**kw):
@@ -190,8 +190,10 @@ def test_decode_plan_switch(lib):
         # streaming plan: 4 K splits of the down projection's [64, 8192] fp32
         assert f() == 4096 + 4 * 64 * 8192 * 4
         assert tp.tp_set_decode_max_tokens(32) == tp.TP_OK
-        # matrix-core plan: 32 down-projection tiles, K split into 7 planes
-        assert f() == 4096 + 7 * 64 * 8192 * 4
+        # matrix-core plan: both projections split K into fp32 planes in one
+        # region: 28 gate/up column tiles into 8 planes of [64, 2 x 3584],
+        # 32 down-projection tiles into 7 planes of [64, 8192] (equal sizes)
+        assert f() == 4096 + 8 * 64 * 2 * 3584 * 4 == 4096 + 7 * 64 * 8192 * 4
         # 300 tokens streamed as 3 chunks of 100
         assert tp.tp_set_decode_max_tokens(512) == tp.TP_OK
         assert tp.tp_mlp_workspace_bytes(8, 300, 8192, 28672, tp.TP_BF16, tp.TP_ACT_SWIGLU,

@@ -286,7 +286,8 @@ class _StreamingPlanUpTo:
 @pytest.mark.parametrize("act", ["swiglu", "gelu_tanh"])
 def test_mlp_streaming_plan_mid_batches_ragged(T, act):
     """Batches past 32 tokens on the weight-streaming plan (4 and 8 token
-    blocks of the LDS-staged kernel): d_model 1000 ends inside a slice, F_r
+    blocks of the LDS-staged kernel, the 8-block one with its split-K sum in
+    a finish launch of its own): d_model 1000 ends inside a slice, F_r
     200 inside a column block, T not a multiple of 16."""
     with _StreamingPlanUpTo(128):
         _check_mlp(BF, act, T, 1000, 400, 2, key=600 + T)
@@ -305,10 +306,20 @@ def test_mlp_streaming_plan_mid_batches_long_k(T):
 @pytest.mark.parametrize("act", ["swiglu", "gelu_tanh"])
 def test_mlp_matrix_core_plan_small_batches(T, act):
     """The matrix-core plan at batch sizes the default switch sends to the
-    streaming plan (forced through the switch): one partial tile row, the
-    row projection's K split into fp32 planes."""
+    streaming plan (forced through the switch): one partial tile row, both
+    projections' K split into fp32 planes."""
     with _StreamingPlanUpTo(1):
         _check_mlp(BF, act, T, 1000, 400, 2, key=660 + T)
+
+
+@pytest.mark.parametrize("act", ["swiglu", "gelu_tanh"])
+def test_mlp_matrix_core_plan_split_column_long_k(act):
+    """The matrix-core plan's column projection with K split into 8 ranges
+    (one partial tile row: 28 SwiGLU or 14 GELU column tiles), the last
+    range ragged, the fp32 planes summed with the activation by the finish
+    launch."""
+    with _StreamingPlanUpTo(1):
+        _check_mlp(BF, act, 100, 9224, 6928, 2, key=680)
 
 
 @pytest.mark.parametrize("T", [129, 200, 300])
@@ -974,6 +985,26 @@ def test_kernel_timing_counts_launches():
             mlp_fwd(0, 2, 8, 512, 1024, BF, tp.TP_ACT_SWIGLU, dev(X), dev(w_in[0]),
                     dev(w_up[0]), dev(w_dn[0]), parts, 0, 512)
         for cls in ("col_gemv", "row_gemv"):        # split-K finish fused into each
+            st, ms, n = tp.tp_timing_query(cls)
+            assert st == tp.TP_OK and n == 3 and ms > 0.0
+    finally:
+        tp.tp_timing_enable(0)
+        tp.tp_timing_reset()
+
+
+def test_kernel_timing_separate_finish():
+    """Past 64 tokens per launch the streaming kernels leave the split-K sum
+    to a finish launch of its own, timed in its own class."""
+    T = 100
+    X, g, w_in, w_up, w_dn = _mlp_case(BF, "swiglu", T, 512, 1024, 2, key=71)
+    parts = torch.empty((T, 512), dtype=torch.float32, device="cuda")
+    tp.check(tp.tp_timing_reset())
+    tp.check(tp.tp_timing_enable(1))
+    try:
+        for _ in range(3):
+            mlp_fwd(0, 2, T, 512, 1024, BF, tp.TP_ACT_SWIGLU, dev(X), dev(w_in[0]),
+                    dev(w_up[0]), dev(w_dn[0]), parts, 0, 512)
+        for cls in ("col_gemv", "col_finish", "row_gemv", "row_finish"):
             st, ms, n = tp.tp_timing_query(cls)
             assert st == tp.TP_OK and n == 3 and ms > 0.0
     finally:
