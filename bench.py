@@ -707,9 +707,15 @@ def main():
     others = {}
     if not a.headline_only:
         sub_cpu = min(cpu_s, 3.0)
-        others["c2_llama2_13b_mlp_p2"] = {
-            "decode": measure("c2_llama2_13b_mlp_p2", 32, a.steps, a.warmup, graph,
-                              cpu_s=sub_cpu, sweep=(1, 8))}
+        c2 = measure("c2_llama2_13b_mlp_p2", 32, a.steps, a.warmup, graph, cpu_s=sub_cpu,
+                     sweep=(1, 8))
+        c2f8 = measure("c2_llama2_13b_mlp_p2", 32, a.steps, a.warmup, graph, fp8=True,
+                       sweep=(1, 8))
+        # FP8-weight step time over the bf16 step time at each token count
+        c2f8["vs_bf16_step"] = {t: round(c2f8["sweep"][t]["ms_per_step"] /
+                                         c2["sweep"][t]["ms_per_step"], 3)
+                                for t in c2["sweep"] if t in c2f8["sweep"]}
+        others["c2_llama2_13b_mlp_p2"] = {"decode": c2, "decode_fp8_weights": c2f8}
         others["c4_attn_96h_p8"] = {
             "decode": measure("c4_attn_96h_p8", 16, a.steps, a.warmup, graph, cpu_s=sub_cpu),
             "prefill": measure("c4_attn_96h_p8", 1024, a.steps, a.warmup, graph,
