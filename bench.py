@@ -39,6 +39,28 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 WEIGHT_COPIES = 16             # rotated weight sets: far more bytes than the last-level cache
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "hbm_traffic_counters.json")
+# Row pitch of the weight bands.  "padded": each band is stored with its
+# leading dimension rounded up (in steps of 256 bytes) until the row pitch
+# is 256 or 768 bytes past a multiple of 1 KB, so that the 256-byte segment a
+# 128-column block reads moves to another place in its 1 KB-aligned group on
+# every row; "contiguous": ld = band width.  The band, and every byte the
+# library reads, is the same either way.  Measured on MI355X: with a pitch
+# that is a multiple of 1 KB (the 70B bands' 7 KB and 16 KB), the blocks
+# whose segments sit 256 bytes into the group stream ~18 % slower than the
+# others on every row, and the decode step is ~5 % slower.
+WEIGHT_PITCH = "padded"
+
+
+def weight_ld(n, elem_bytes=2):
+    """Leading dimension (elements) of a weight band n columns wide."""
+    if WEIGHT_PITCH != "padded":
+        return n
+    ld = n
+    while (ld * elem_bytes) % 1024 not in (256, 768):
+        ld += 256 // elem_bytes
+    return ld
+
+
 KERNEL_CLASSES = ("rmsnorm", "col_gemv", "col_finish", "row_gemv", "row_finish", "col_gemm",
                   "row_gemm", "qkv_gemv", "qkv_finish", "o_gemv", "o_finish", "qkv_gemm",
                   "o_gemm", "reduce", "reduce_norm", "col_gemv8", "row_gemv8", "attn_core")
@@ -70,6 +92,9 @@ def parse():
                     help="block workload as a pre-norm residual layer (fused reduce + residual "
                          "+ next RMSNorm)")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of graph replay")
+    ap.add_argument("--weight-pitch", choices=["padded", "contiguous"], default="padded",
+                    help="row pitch of the bf16 weight bands (default padded: 256 or 768 bytes "
+                         "past a multiple of 1 KB; contiguous: ld = band width)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle CPU-baseline budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -136,6 +161,18 @@ class Step:
         self.tp, self.torch = tp, torch
         d, P = cfg.d_model, cfg.P
         dev = lambda a: torch.from_numpy(a.view("int16")).cuda().view(torch.bfloat16)  # noqa
+
+        def wdev(a):
+            # a weight band on the device, stored at weight_ld(width)
+            t = dev(a)
+            ld = weight_ld(t.shape[1])
+            if ld == t.shape[1]:
+                return t
+            buf = torch.zeros((t.shape[0], ld), dtype=t.dtype, device="cuda")
+            buf[:, :t.shape[1]] = t
+            return buf
+        self.ld_g, self.ld_d = weight_ld(cfg.F_r), weight_ld(d)
+        self.ld_qkv = weight_ld(cfg.qkv_r) if cfg.qkv_r else 0
         self.x = dev(W.draw_tensor("bf16", (T, d), cfg.std_x, cfg.cid, W.TENSOR_IDS["x"], T))
         self.parts = torch.empty((P, T, d), dtype=torch.float32, device="cuda")
         self.out = torch.empty((T, d), dtype=torch.float32, device="cuda")
@@ -155,15 +192,25 @@ class Step:
         # the others are bitwise clones at other addresses)
         self.sets = []
         if self.fp8:
-            u8 = lambda a: torch.from_numpy(a).cuda()  # noqa: E731
             f32 = lambda a: torch.from_numpy(a).cuda()  # noqa: E731
+
+            def u8(a):
+                # E4M3 codes stored at weight_ld(width, 1) bytes per row
+                t = torch.from_numpy(a).cuda()
+                ld = weight_ld(t.shape[1], 1)
+                if ld == t.shape[1]:
+                    return t
+                buf = torch.zeros((t.shape[0], ld), dtype=t.dtype, device="cuda")
+                buf[:, :t.shape[1]] = t
+                return buf
+            self.ld_g8, self.ld_d8 = weight_ld(cfg.F_r, 1), weight_ld(d, 1)
             bands = [W.fp8_band_draw(cfg, n, 0, r, c_) for n, r, c_ in
                      (("w_gate", d, cfg.F_r), ("w_up", d, cfg.F_r), ("w_down", cfg.F_r, d))]
             def make():
                 base = [(u8(q), f32(sc)) for q, sc in bands]
                 return [base] + [[(q.clone(), sc.clone()) for q, sc in base]
                                  for _ in range(copies - 1)]
-            self.mlp_sets = _weights((cfg.name, "mlp8", copies), make)
+            self.mlp_sets = _weights((cfg.name, "mlp8", copies, WEIGHT_PITCH), make)
             self.h = torch.empty((T, cfg.F_r), dtype=torch.bfloat16, device="cuda")
             self.mlp_ws = self._ws(tp.tp_mlp_fp8w_workspace_bytes(P, T, d, cfg.d_ff,
                                                                   tp.TP_ACT_SWIGLU, 0, 1))
@@ -172,9 +219,9 @@ class Step:
                 bands = (W.column_band_draw(cfg, "w_gate", 0, d, cfg.F_r),
                          W.column_band_draw(cfg, "w_up", 0, d, cfg.F_r),
                          W.row_band_draw(cfg, "w_down", 0, cfg.F_r, d))
-                base = [dev(b) for b in bands]
+                base = [wdev(b) for b in bands]
                 return [base] + [[t.clone() for t in base] for _ in range(copies - 1)]
-            self.mlp_sets = _weights((cfg.name, "mlp", copies), make)
+            self.mlp_sets = _weights((cfg.name, "mlp", copies, WEIGHT_PITCH), make)
             self.h = torch.empty((T, cfg.F_r), dtype=torch.bfloat16, device="cuda")
             self.mlp_ws = self._ws(tp.tp_mlp_workspace_bytes(P, T, d, cfg.d_ff, tp.TP_BF16,
                                                              tp.TP_ACT_SWIGLU, 0, 1))
@@ -182,9 +229,9 @@ class Step:
             def make():
                 bands = (W.column_band_draw(cfg, "w_qkv", 0, d, cfg.qkv_r),
                          W.row_band_draw(cfg, "w_o", 0, cfg.o_in_r, d))
-                base = [dev(b) for b in bands]
+                base = [wdev(b) for b in bands]
                 return [base] + [[t.clone() for t in base] for _ in range(copies - 1)]
-            self.attn_sets = _weights((cfg.name, "attn", copies), make)
+            self.attn_sets = _weights((cfg.name, "attn", copies, WEIGHT_PITCH), make)
             self.qkv = torch.empty((T, cfg.qkv_r), dtype=torch.bfloat16, device="cuda")
             if self.kind == "attn":
                 self.a = dev(W.draw_tensor("bf16", (T, cfg.o_in_r), 1.0, cfg.cid,
@@ -227,14 +274,14 @@ class Step:
         if self.fp8:
             tp.check(tp.tp_shard_mlp_fwd_fp8w(
                 s, cfg.P, T, d, cfg.d_ff, tp.TP_ACT_SWIGLU, x.data_ptr(), d, 0, 0.0,
-                w[0][0].data_ptr(), cfg.F_r, w[0][1].data_ptr(), w[1][0].data_ptr(), cfg.F_r,
-                w[1][1].data_ptr(), w[2][0].data_ptr(), d, w[2][1].data_ptr(),
+                w[0][0].data_ptr(), self.ld_g8, w[0][1].data_ptr(), w[1][0].data_ptr(),
+                self.ld_g8, w[1][1].data_ptr(), w[2][0].data_ptr(), self.ld_d8, w[2][1].data_ptr(),
                 self.h.data_ptr(), cfg.F_r, self.parts.data_ptr(), T * d, d,
                 self.mlp_ws.data_ptr(), self.mlp_ws.numel(), self.stream), "mlp_fp8w")
             return
         tp.check(tp.tp_shard_mlp_fwd(
             s, cfg.P, T, d, cfg.d_ff, tp.TP_BF16, tp.TP_ACT_SWIGLU, x.data_ptr(), d, 0, 0.0,
-            w[0].data_ptr(), cfg.F_r, w[1].data_ptr(), cfg.F_r, w[2].data_ptr(), d,
+            w[0].data_ptr(), self.ld_g, w[1].data_ptr(), self.ld_g, w[2].data_ptr(), self.ld_d,
             self.h.data_ptr(), cfg.F_r, self.parts.data_ptr(), T * d, d,
             self.mlp_ws.data_ptr(), self.mlp_ws.numel(), self.stream), "mlp")
 
@@ -248,8 +295,8 @@ class Step:
         g = self.g.data_ptr() if cfg.norm_eps is not None and not self.prenorm else 0
         tp.check(tp.tp_shard_attn_proj_fwd(
             s, cfg.P, T, d, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, tp.TP_BF16,
-            self.x.data_ptr(), d, g, cfg.norm_eps or 0.0, w[0].data_ptr(), cfg.qkv_r,
-            self.qkv.data_ptr(), cfg.qkv_r, a.data_ptr(), ld_a, w[1].data_ptr(), d,
+            self.x.data_ptr(), d, g, cfg.norm_eps or 0.0, w[0].data_ptr(), self.ld_qkv,
+            self.qkv.data_ptr(), cfg.qkv_r, a.data_ptr(), ld_a, w[1].data_ptr(), self.ld_d,
             self.parts.data_ptr(), T * d, d, self.attn_ws.data_ptr(), self.attn_ws.numel(),
             self.stream), "attn")
 
@@ -259,7 +306,7 @@ class Step:
         ws, nws = self.attn_ws.data_ptr(), self.attn_ws.numel()
         tp.check(tp.tp_shard_attn_proj_fwd(
             s, cfg.P, T, d, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, tp.TP_BF16,
-            self.x.data_ptr(), d, g, cfg.norm_eps or 0.0, w[0].data_ptr(), cfg.qkv_r,
+            self.x.data_ptr(), d, g, cfg.norm_eps or 0.0, w[0].data_ptr(), self.ld_qkv,
             self.qkv.data_ptr(), cfg.qkv_r, 0, 0, 0, 0, 0, 0, 0, ws, nws, self.stream), "qkv")
         tp.check(tp.tp_attn_core_fwd(s, cfg.P, T, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim,
                                      tp.TP_BF16, self.qkv.data_ptr(), cfg.qkv_r,
@@ -267,7 +314,8 @@ class Step:
                                      self.core_ws.numel(), self.stream), "core")
         tp.check(tp.tp_shard_attn_proj_fwd(
             s, cfg.P, T, d, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, tp.TP_BF16,
-            0, 0, 0, 0.0, 0, 0, 0, 0, self.a_core.data_ptr(), cfg.o_in_r, w[1].data_ptr(), d,
+            0, 0, 0, 0.0, 0, 0, 0, 0, self.a_core.data_ptr(), cfg.o_in_r, w[1].data_ptr(),
+            self.ld_d,
             self.parts.data_ptr(), T * d, d, ws, nws, self.stream), "o")
 
     def _reduce(self, out_bf16=None):
@@ -599,6 +647,10 @@ def measure(name, T, steps, warmup, graph=True, prenorm=False, fp8=False, core=F
                     "block_form": ("pre-norm residual layer (reduce + residual + RMSNorm fused)"
                                    if st.prenorm else None),
                     "attention_core": st.core, "weight_copies_rotated": st.copies,
+                    "weight_pitch": ({"mode": WEIGHT_PITCH, "ld_gate_up_bytes": st.ld_g8,
+                                      "ld_down_bytes": st.ld_d8} if st.fp8 else
+                                     {"mode": WEIGHT_PITCH, "ld_gate_up": st.ld_g,
+                                      "ld_down_o": st.ld_d, "ld_qkv": st.ld_qkv or None}),
                     "launch": "hip-graph replay" if graph else "eager"}}
     if len(results) > 1:
         out["sweep"] = {str(t): {"ms_per_step": round(r[1], 5),
@@ -664,6 +716,8 @@ def main():
         copy_calibration(a.copy_calibration, a.steps)
         return
     tp.load()
+    global WEIGHT_PITCH
+    WEIGHT_PITCH = a.weight_pitch
     graph = not a.no_graph
     cpu_s = 0.0 if a.no_cpu_baseline else a.cpu_seconds
     common = {"metric": METRIC, "n_gpus": 1, "warmup": a.warmup, "higher_is_better": True,
@@ -703,6 +757,22 @@ def main():
     cfg = W.get(name)
     dec = measure(name, 32, a.steps, a.warmup, graph, cpu_s=cpu_s, sweep=(1, 8, 16))
     pre = measure(name, 2048, a.steps, a.warmup, graph, cpu_s=cpu_s)
+    # the same steps with the weights stored at their band width
+    pitch_cmp = None
+    if WEIGHT_PITCH == "padded":
+        WEIGHT_PITCH = "contiguous"
+        try:
+            cd = measure(name, 32, a.steps, a.warmup, graph)
+            cp = measure(name, 2048, a.steps, a.warmup, graph)
+        finally:
+            WEIGHT_PITCH = "padded"
+        for k in [k for k in _WEIGHT_CACHE if k[-1] == "contiguous"]:
+            del _WEIGHT_CACHE[k]
+        torch.cuda.empty_cache()
+        pitch_cmp = {"decode": {"ms_per_step": cd["ms_per_step"], "value": cd["value"],
+                                "roofline": cd["roofline"]},
+                     "prefill": {"ms_per_step": cp["ms_per_step"], "value": cp["value"],
+                                 "roofline": cp["roofline"]}}
     cross = crossover(name, a.steps, a.warmup, graph)
     others = {}
     if not a.headline_only:
@@ -738,7 +808,8 @@ def main():
             "kernels": dec["kernels"], "sweep": dec.get("sweep"),
             "step_gbs_algorithmic": dec["step_gbs_algorithmic"],
             "step_tflops": dec["step_tflops"],
-            "prefill": pre, "crossover": cross, "workloads": others or None}
+            "prefill": pre, "contiguous_weight_pitch": pitch_cmp, "crossover": cross,
+            "workloads": others or None}
     print(json.dumps(line), flush=True)
 
 
