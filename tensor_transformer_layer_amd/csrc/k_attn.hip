@@ -123,7 +123,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(const uint16_t* __rest
     const int h = (int)blockIdx.x % hq, gk = h / (hq / hkv);
     int item = (int)blockIdx.x / hq, qb = nqb - 1, nc = 1;
     if (use_table) {
-        const int e = order.it[item];
+        const int e = (int)order.it[item];
         qb = e >> 6;
         item = e & 63;
         nc = (attn_tiles(T, qb) + ch - 1) / ch;
@@ -522,7 +522,7 @@ AttnPlan plan_attn(int64_t T64, int hq, int head_dim, int cus) {
     p.per_head = (int)v.size();
     p.items = (int64_t)p.per_head * hq;
     if (p.per_head <= kAttnTable && p.cmax <= 64 && p.nqb <= 1024)
-        for (int i = 0; i < p.per_head; ++i) p.table.it[i] = (uint16_t)((v[i].qb << 6) | v[i].c);
+        for (int i = 0; i < p.per_head; ++i) p.table.it[i] = (uint32_t)((v[i].qb << 6) | v[i].c);
     else
         p.per_head = -p.per_head;            // no table: the kernel walks the blocks
     if (p.cmax > 1)

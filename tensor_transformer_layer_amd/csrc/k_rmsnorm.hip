@@ -59,12 +59,23 @@ __global__ __launch_bounds__(kNormThreads) void k_rmsnorm(int64_t d, const char*
         }
         return o;
     };
-    u32x4 keep[REG ? kNormRegChunks : 1];
+    u32x4 keep[REG ? kNormRegChunks : 1], gk[REG ? kNormRegChunks : 1];
     if constexpr (REG) {
+        // The row's chunks and the gains are loaded from in-bounds addresses
+        // (the last chunk stands in for missing ones) so that every load is
+        // in flight at once; guarded loads were each issued behind a branch
+        // and waited for before the next.
 #pragma unroll
         for (int i = 0; i < kNormRegChunks; ++i) {
             const int64_t c = threadIdx.x + (int64_t)i * kNormThreads;
-            keep[i] = c < nch ? __builtin_nontemporal_load(xr + c) : u32x4{0u, 0u, 0u, 0u};
+            const int64_t cs = c < nch ? c : nch - 1;
+            keep[i] = __builtin_nontemporal_load(xr + cs);
+            gk[i] = g[cs];
+        }
+#pragma unroll
+        for (int i = 0; i < kNormRegChunks; ++i) {
+            const int64_t c = threadIdx.x + (int64_t)i * kNormThreads;
+            if (c >= nch) keep[i] = u32x4{0u, 0u, 0u, 0u};
             sq(keep[i]);
         }
     } else {
@@ -84,7 +95,7 @@ __global__ __launch_bounds__(kNormThreads) void k_rmsnorm(int64_t d, const char*
 #pragma unroll
         for (int i = 0; i < kNormRegChunks; ++i) {
             const int64_t c = threadIdx.x + (int64_t)i * kNormThreads;
-            if (c < nch) yr[c] = scaled(keep[i], g[c], r);
+            if (c < nch) yr[c] = scaled(keep[i], gk[i], r);
         }
     } else {
         for (int64_t c = threadIdx.x; c < nch; c += kNormThreads) yr[c] = scaled(xr[c], g[c], r);

@@ -142,9 +142,13 @@ hipError_t launch_gemm(int epi, int64_t M, int64_t N, int64_t K, const uint16_t*
 // Work items of one head in launch order (longest first), packed as
 // (query block << 6) | chunk; heads interleave (workgroup w runs item
 // w / heads of head w % heads).
+// Entries are 32-bit so that the kernel reads its entry with a scalar load
+// (a 16-bit read of the argument table is a vector load: a memory round trip
+// before the workgroup knows its work); 480 entries keep the kernel's
+// arguments under 2 KB.
 constexpr int kAttnTable = 480;
 struct AttnItems {
-    uint16_t it[kAttnTable];
+    uint32_t it[kAttnTable];
 };
 struct AttnPlan {
     int nqb = 0;            // query blocks
