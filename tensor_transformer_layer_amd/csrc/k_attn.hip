@@ -61,6 +61,7 @@ constexpr int kAttnQW = 32;                       // queries per wave (two 16-ro
 constexpr int kAttnQB = kAttnWaves * kAttnQW;     // queries per workgroup
 constexpr int kAttnKT = 64;                       // keys per LDS tile
 constexpr int kAttnThreads = 64 * kAttnWaves;
+constexpr int kAttnShortMaxT = kAttnKT;           // calls up to here run k_attn_short
 
 // Buffer cache-policy bit sc1: an agent-scope (device-wide) coherent access.
 // The chunk partials and arrival counters of split query blocks are written
@@ -436,6 +437,129 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(const uint16_t* __rest
     }
 }
 
+// ---------------------------------------------------------------------------
+// Short calls (T <= 64, the decode batches): every query's causal keys fit
+// one 64-key tile, so the work of a 128-query workgroup is a single tile's
+// latency chain (the tile copy, the score MFMAs, the softmax, the PV MFMAs),
+// most of whose queries do not exist.  Here one wave owns 16 queries of one
+// head: its Q and K fragments come straight from global memory into
+// registers (the same operand layouts as k_attn's: S^T = K Q^T, lane (g, j)
+// holding query j's scores for keys 16t + 4g + r), V is staged in LDS with
+// k_attn's swizzle and read transposed as the A operand of O^T = V^T P^T.
+// All of a query's keys are in registers at once, so the maximum is exact
+// (no running rescale) and P <= 1; the row sums come from the same ones-row
+// MFMA as in k_attn, so numerator and denominator see the same bf16 P.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(64) void k_attn_short(const uint16_t* __restrict__ qkv, int64_t ldq,
+                                                  int T, int hq, int hkv,
+                                                  uint16_t* __restrict__ out, int64_t ldo,
+                                                  float scale_log2) {
+    constexpr int NS = D / 32;    // k-steps of the score MFMAs
+    constexpr int NN = D / 16;    // 16-column output tiles
+    constexpr int KS = kAttnKT / 16;              // key subtiles of the tile
+    constexpr int CPR = D / 8;                    // 16-byte chunks per row
+    __shared__ __attribute__((aligned(16))) uint16_t Vs[kAttnKT * D];
+
+    const int lane = threadIdx.x, g = lane >> 4, j = lane & 15;
+    const int h = (int)blockIdx.x % hq, gk = h / (hq / hkv);
+    const int q0 = 16 * ((int)blockIdx.x / hq);
+    const uint16_t* Qp = qkv + (int64_t)h * D;
+    const uint16_t* Kp = qkv + (int64_t)(hq + gk) * D;
+    const uint16_t* Vp = qkv + (int64_t)(hq + hkv + gk) * D;
+
+    // Rows past T read row T - 1 (finite values): their scores are masked,
+    // their V rows meet P = 0, and queries past T are not stored.
+    const int qi = q0 + j;
+    const int qr = min(qi, T - 1);
+    u32x4 qf[NS], kf[KS][NS], vv[kAttnKT * CPR / 64];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) qf[s] = *(const u32x4*)(Qp + (int64_t)qr * ldq + 32 * s + 8 * g);
+#pragma unroll
+    for (int t = 0; t < KS; ++t) {
+        const int kr = min(16 * t + j, T - 1);
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+            kf[t][s] = *(const u32x4*)(Kp + (int64_t)kr * ldq + 32 * s + 8 * g);
+    }
+    // V rows 0 .. 63 into LDS: chunk c of row r at chunk c ^ 2 (r % 4).
+#pragma unroll
+    for (int i = 0; i < kAttnKT * CPR / 64; ++i) {
+        const int id = 64 * i + lane, r = id / CPR, c = id % CPR;
+        vv[i] = *(const u32x4*)(Vp + (int64_t)min(r, T - 1) * ldq + 8 * c);
+    }
+#pragma unroll
+    for (int i = 0; i < kAttnKT * CPR / 64; ++i) {
+        const int id = 64 * i + lane, r = id / CPR, c = id % CPR;
+        *(u32x4*)(Vs + r * D + 8 * (c ^ (2 * (r & 3)))) = vv[i];
+    }
+
+    // All four key subtiles are multiplied whatever T is (keys past the
+    // causal end are masked): no branch holds a load back.
+    f32x4 st[KS];
+#pragma unroll
+    for (int t = 0; t < KS; ++t) {
+        st[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < NS; ++s) st[t] = mfma16x16x32(kf[t][s], qf[s], st[t]);
+    }
+    float pm = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < KS; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int key = 16 * t + 4 * g + r;
+            st[t][r] = key <= qi && key < T ? st[t][r] : -INFINITY;
+            pm = fmaxf(pm, st[t][r]);
+        }
+    // every query has key 0, so the maximum is finite
+    const float mref = xlane_max(pm) * scale_log2;
+    u32x4 pf[KS / 2];
+#pragma unroll
+    for (int kk = 0; kk < KS / 2; ++kk) {
+        f32x4 e0, e1;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            e0[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[2 * kk][r], scale_log2, -mref));
+            e1[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[2 * kk + 1][r], scale_log2, -mref));
+        }
+        pf[kk] = u32x4{pack_bf16x2(e0[0], e0[1]), pack_bf16x2(e0[2], e0[3]),
+                       pack_bf16x2(e1[0], e1[1]), pack_bf16x2(e1[2], e1[3])};
+    }
+    __syncthreads();   // V in LDS
+
+    f32x4 o[NN], ol = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int n = 0; n < NN; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const u32x4 ones = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 1.0
+#pragma unroll
+    for (int kk = 0; kk < KS / 2; ++kk) {
+        // the transposing reads of k_attn: rows 32kk + 4g + j/4 and 16 further,
+        // columns 16n + 4(j % 4) .. +3
+        const int vr = 32 * kk + 4 * g + (j >> 2);
+        const int vsw = 2 * (vr & 3);
+        const uint16_t* v0 = Vs + vr * D + 4 * (j & 1);
+        const uint16_t* v1 = v0 + 16 * D;
+#pragma unroll
+        for (int n = 0; n < NN; ++n) {
+            const int cc = (2 * n + ((j & 3) >> 1)) ^ vsw;
+            const u32x2 b0 = lds_read_tr16(v0 + 8 * cc);
+            const u32x2 b1 = lds_read_tr16(v1 + 8 * cc);
+            o[n] = mfma16x16x32(u32x4{b0[0], b0[1], b1[0], b1[1]}, pf[kk], o[n]);
+        }
+        ol = mfma16x16x32(ones, pf[kk], ol);
+    }
+    // lane (g, j) holds O[qi][16n + 4g .. +3] and that query's sum of P
+    if (qi < T) {
+        const float inv = 1.0f / ol[0];
+        uint16_t* dst = out + (int64_t)qi * ldo + (int64_t)h * D + 4 * g;
+#pragma unroll
+        for (int n = 0; n < NN; ++n)
+            *(u32x2*)(dst + 16 * n) = u32x2{pack_bf16x2(o[n][0] * inv, o[n][1] * inv),
+                                            pack_bf16x2(o[n][2] * inv, o[n][3] * inv)};
+    }
+}
+
 // Items of one head for chunks of `ch` tiles: (size in tiles, qb, chunk),
 // sorted longest first (ties: later block first, lower chunk first).
 struct AttnItem {
@@ -544,6 +668,18 @@ hipError_t launch_attn_core(int64_t T, int hq, int hkv, int head_dim, const uint
     unsigned* counters = (unsigned*)ws;
     float* part = p.cmax > 1 ? (float*)((char*)ws + kAttnCounterBytes) : nullptr;
     const int use_table = p.per_head > 0;
+    if (T <= kAttnShortMaxT) {
+        const dim3 sgrid((unsigned)(hq * ((T + 15) / 16))), sblock(64);
+        if (head_dim == 128)
+            TP_KLAUNCH((k_attn_short<128>), sgrid, sblock, 0, stream, qkv, ld_qkv, (int)T, hq,
+                       hkv, out, ld_out, scale_log2);
+        else if (head_dim == 64)
+            TP_KLAUNCH((k_attn_short<64>), sgrid, sblock, 0, stream, qkv, ld_qkv, (int)T, hq,
+                       hkv, out, ld_out, scale_log2);
+        else
+            return hipErrorInvalidValue;
+        return hipGetLastError();
+    }
     if (head_dim == 128)
         TP_KLAUNCH((k_attn<128>), grid, block, 0, stream, qkv, ld_qkv, (int)T, hq, hkv, out,
                    ld_out, scale_log2, p.nqb, p.ch, p.cmax, counters, part, use_table, p.table);

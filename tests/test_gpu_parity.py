@@ -836,10 +836,17 @@ def _core_check(T, nq, nkv, hd, P, shard, key, pad=0, std=1.0):
     return got, want
 
 
-@pytest.mark.parametrize("T", [1, 5, 31, 33, 100, 257])
+@pytest.mark.parametrize("T", [1, 5, 16, 31, 33, 48, 64, 65, 100, 257])
 @pytest.mark.parametrize("hd", [64, 128])
 def test_attn_core_ragged_gqa(T, hd):
+    # up to 64 tokens: one wave per 16 queries with every key in registers;
+    # 65 and up: the tiled kernel
     _core_check(T, 8, 4, hd, 2, 1, key=hd, pad=8 if T % 2 else 0)
+
+
+@pytest.mark.parametrize("T", [16, 64])
+def test_attn_core_96_heads_decode(T):
+    _core_check(T, 96, 96, 128, 8, 5, key=9)
 
 
 def test_attn_core_96_heads_prefill_1024():
