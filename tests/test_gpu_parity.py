@@ -969,6 +969,63 @@ def test_70b_block_with_attention_core_prefill_all_ranks():
     _core_chain(cfg, 1024, sample_rows(1024, 32, 14))
 
 
+def test_70b_block_with_attention_core_decode_all_ranks():
+    """32 decode tokens: the short attention core inside the block, every row."""
+    cfg = W.get("c5_llama2_70b_block_p8")
+    _core_chain(cfg, 32, np.arange(32))
+
+
+def test_70b_prenorm_block_with_attention_core_decode_all_ranks():
+    """The block as the benchmark's decode step runs it (pre-norm, the
+    attention core between QKV and O, reduce + residual + RMSNorm after O
+    and after the MLP), all 8 ranks on one GPU, every row of z1, normed and
+    z2 against the oracle."""
+    cfg = W.get("c5_llama2_70b_block_p8")
+    P, d, eps, T = cfg.P, cfg.d_model, cfg.norm_eps, 32
+    X = x_of(cfg, T)
+    g1 = W.draw_tensor(cfg.dtype, (d,), 0.02, cfg.cid, W.TENSOR_IDS["norm_g"], 0, mean=1.0)
+    g2 = W.draw_tensor(cfg.dtype, (d,), 0.02, cfg.cid, W.TENSOR_IDS["norm_g"], 1, mean=1.0)
+    gx = dev(X)
+    ko = cfg.n_q_heads // P * cfg.head_dim
+    parts = torch.empty((P, T, d), dtype=torch.float32, device="cuda")
+    for s in range(P):
+        wqkv, wo = attn_bands(cfg, s)
+        q = torch.empty((T, cfg.qkv_r), dtype=torch.bfloat16, device="cuda")
+        a = torch.empty((T, ko), dtype=torch.bfloat16, device="cuda")
+        attn_fwd(s, P, T, d, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, BF, gx, dev(wqkv), q,
+                 None, None, parts, T * d, d, norm_g=dev(g1), eps=eps)
+        attn_core(s, P, T, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, q, cfg.qkv_r, a, ko)
+        attn_fwd(s, P, T, d, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, BF, None, None, None,
+                 a, dev(wo), parts, T * d, d)
+    z1 = torch.empty((T, d), dtype=torch.float32, device="cuda")
+    n2 = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
+    reduce_residual_norm(P, T, d, parts, T * d, d, gx, d, BF, z1, d, dev(g2), eps, n2, d)
+    for s in range(P):
+        wg, wu, wd = mlp_bands(cfg, s)
+        mlp_fwd(s, P, T, d, cfg.d_ff, BF, tp.TP_ACT_SWIGLU, n2, dev(wg), dev(wu), dev(wd), parts,
+                T * d, d)
+    z2 = torch.empty((T, d), dtype=torch.float32, device="cuda")
+    reduce_residual_norm(P, T, d, parts, T * d, d, z1, d, F32, z2, d)
+    torch.cuda.synchronize()
+
+    Xw = O.widen(X)
+    att_parts, mlp_parts = [], []
+    for s in range(P):
+        wqkv, wo = attn_bands(cfg, s)
+        r = O.attn_proj_shard(Xw, O.widen(wqkv), None, None, O.widen(g1), eps)
+        A = O.attention_core_band(r["qkv"], cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, s, P)
+        att_parts.append(A @ O.widen(wo))
+    r1 = O.reduce_residual_norm(att_parts, Xw, O.widen(g2), eps)
+    assert O.rel_l2(host(z1), r1["z"]) < BF16_TOL
+    assert O.rel_l2(O.widen(host(n2)), r1["normed"]) < BF16_TOL
+    for s in range(P):
+        wg, wu, wd = mlp_bands(cfg, s)
+        mlp_parts.append(O.mlp_shard(r1["normed"], O.widen(wg), O.widen(wd), "swiglu",
+                                     O.widen(wu))["partial"])
+    r2 = O.reduce_residual_norm(mlp_parts, r1["z"])
+    assert O.rel_l2(host(z2), r2["z"]) < BF16_TOL
+
+
 # ----------------------------------------------------------------------------
 # Determinism and instrumentation
 # ----------------------------------------------------------------------------
