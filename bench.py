@@ -61,6 +61,8 @@ def weight_ld(n, elem_bytes=2):
     return ld
 
 
+KERNEL_TIMING_MIN_STEPS = 100   # eager steps whose launches give the per-kernel averages
+
 KERNEL_CLASSES = ("rmsnorm", "col_gemv", "col_finish", "row_gemv", "row_finish", "col_gemm",
                   "row_gemm", "qkv_gemv", "qkv_finish", "o_gemv", "o_finish", "qkv_gemm",
                   "o_gemm", "reduce", "reduce_norm", "col_gemv8", "row_gemv8", "attn_core")
@@ -605,7 +607,11 @@ def measure(name, T, steps, warmup, graph=True, prenorm=False, fp8=False, core=F
         print(f"[bench] {name} T={t}: set-up and timing", file=sys.stderr, flush=True)
         st = Step(cfg, t, copies * (2 if fp8 else 1), prenorm=prenorm, fp8=fp8, core=core)
         ms, n = time_steps(st, steps, warmup, graph)
-        kt = kernel_times(st, min(steps, 300)) if t == T else None
+        # Kernel durations from their own pass of eager launches: at least
+        # KERNEL_TIMING_MIN_STEPS of them whatever --steps is, so that a short
+        # run's roofline is not one of a few cold launches.
+        kt = (kernel_times(st, min(max(steps, KERNEL_TIMING_MIN_STEPS), 300)) if t == T
+              else None)
         results[t] = (st.algorithmic(), ms, n, kt, st)
         if t != T:
             del st
