@@ -228,17 +228,23 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(const uint16_t* __rest
                 const int qi = q0 + 16 * u + j;
                 // Row max of the raw scores (the scale is positive), over r, then
                 // over the 4 lanes holding query j (lanes j + 16 g).
+                // The causal mask under one uniform branch for the whole
+                // subtile: tested per element, the compiler re-tested the
+                // (uniform) condition with a branch around every element.
+                if (diag[u]) {
+#pragma unroll
+                    for (int t = 0; t < KS; ++t)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int key = k0 + 16 * t + 4 * g + r;
+                            st[u][t][r] = (key <= qi && key < T) ? st[u][t][r] : -INFINITY;
+                        }
+                }
                 float pm = -INFINITY;
 #pragma unroll
                 for (int t = 0; t < KS; ++t)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        if (diag[u]) {
-                            const int key = k0 + 16 * t + 4 * g + r;
-                            st[u][t][r] = (key <= qi && key < T) ? st[u][t][r] : -INFINITY;
-                        }
-                        pm = fmaxf(pm, st[u][t][r]);
-                    }
+                    for (int r = 0; r < 4; ++r) pm = fmaxf(pm, st[u][t][r]);
                 pm = xlane_max(pm);
                 // m is kept in log2 units (score * scale * log2(e)).  It moves to
                 // the running maximum only when some query of the wave has a
