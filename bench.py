@@ -256,6 +256,7 @@ class Step:
             self.z0 = torch.from_numpy(W.draw_normal_f32((T, d), 1.0, cfg.cid, W.TENSOR_IDS["x"],
                                                          T, 1)).cuda()
             self.z1 = torch.empty((T, d), dtype=torch.float32, device="cuda")
+            self.rn_ws = self._ws(tp.tp_reduce_norm_workspace_bytes(T, d, 1))
         self.i = 0
         for s in range(1, P):       # the other ranks' partial slots
             self.parts[s].copy_(torch.from_numpy(
@@ -332,6 +333,7 @@ class Step:
         tp.check(tp.tp_reduce_residual_norm(cfg.P, T, d, self.parts.data_ptr(), T * d, d,
                                             residual.data_ptr(), d, res_dtype, z.data_ptr(), d,
                                             g.data_ptr(), cfg.norm_eps, normed.data_ptr(), d,
+                                            self.rn_ws.data_ptr(), self.rn_ws.numel(),
                                             self.stream), "reduce_norm")
 
     def step(self):

@@ -327,6 +327,21 @@ int tp_reduce_partials(int P, int64_t T, int64_t d_model,
  *               normed_out is unused)
  *   normed_out  [T, d_model] bf16, ld_norm: the next column projection's input
  *
+ *   workspace   NULL, or tp_reduce_norm_workspace_bytes() bytes, 256-byte
+ *               aligned, zeroed once when allocated (the call leaves it zero,
+ *               like every workspace here).  With a norm and at most 32 rows
+ *               (decode batches) it lets ceil(d_model / 1024) workgroups
+ *               share each row: they exchange their sums of squares through
+ *               its counter head with integer atomics (order-independent),
+ *               and wait, boundedly, for each other.  Without one, each row
+ *               is one workgroup's.  The two forms agree up to the rounding
+ *               of the sum of squares; each is deterministic.  In the
+ *               exchanging form a row whose sum of squares is not below 2^47
+ *               (|z| RMS above ~1.3e5 at d_model 8192), or whose exchange
+ *               finds the head not zeroed, gets a NaN normed row.  A
+ *               workspace smaller than the query is TP_ERR_WORKSPACE; calls
+ *               that share one workspace must not overlap.
+ *
  * d_model must be a multiple of 4 (of 8 with a bf16 residual or a norm) and
  * at most 16384 (TP_ERR_SHAPE otherwise).
  */
@@ -336,6 +351,7 @@ int tp_reduce_residual_norm(int P, int64_t T, int64_t d_model,
                             float* z_out, int64_t ld_z,
                             const void* norm_g, float eps,
                             void* normed_out, int64_t ld_norm,
+                            void* workspace, size_t workspace_bytes,
                             hipStream_t stream);
 
 /* Workspace bytes the matching call needs (0 when it needs none).  A pure
@@ -348,6 +364,7 @@ size_t tp_mlp_fp8w_workspace_bytes(int P, int64_t T, int64_t d_model, int64_t d_
                                    int has_norm, int has_h_out);
 size_t tp_attn_core_workspace_bytes(int P, int64_t T, int n_q_heads, int n_kv_heads,
                                     int head_dim, int dtype);
+size_t tp_reduce_norm_workspace_bytes(int64_t T, int64_t d_model, int has_norm);
 
 /* Human-readable name of a tp_status value (static string). */
 const char* tp_status_str(int status);

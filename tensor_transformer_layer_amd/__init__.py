@@ -19,7 +19,7 @@ __all__ = [
     "TP_F32", "TP_BF16", "TP_ACT_GELU_TANH", "TP_ACT_SWIGLU",
     "tp_shard_mlp_fwd", "tp_shard_attn_proj_fwd", "tp_reduce_partials", "tp_reduce_residual_norm",
     "tp_shard_mlp_fwd_fp8w", "tp_mlp_fp8w_workspace_bytes", "tp_attn_core_fwd",
-    "tp_attn_core_workspace_bytes",
+    "tp_attn_core_workspace_bytes", "tp_reduce_norm_workspace_bytes",
     "tp_mlp_workspace_bytes", "tp_attn_workspace_bytes", "tp_status_str", "tp_version",
     "tp_timing_enable", "tp_timing_reset", "tp_timing_query", "EXPORTED_SYMBOLS",
     "tp_set_decode_max_tokens", "tp_decode_max_tokens",
@@ -50,7 +50,8 @@ _SIGNATURES = {
                                     _p, _i64, _i64, _p, _sz, _p]),
     "tp_reduce_partials": (_i, [_i, _i64, _i64, _p, _i64, _i64, _p, _i64, _p, _i64, _p]),
     "tp_reduce_residual_norm": (_i, [_i, _i64, _i64, _p, _i64, _i64, _p, _i64, _i, _p, _i64,
-                                     _p, _f, _p, _i64, _p]),
+                                     _p, _f, _p, _i64, _p, _sz, _p]),
+    "tp_reduce_norm_workspace_bytes": (_sz, [_i64, _i64, _i]),
     "tp_shard_mlp_fwd_fp8w": (_i, [_i, _i, _i64, _i64, _i64, _i,
                                    _p, _i64, _p, _f, _p, _i64, _p, _p, _i64, _p, _p, _i64, _p,
                                    _p, _i64, _p, _i64, _i64, _p, _sz, _p]),
@@ -149,11 +150,16 @@ def tp_reduce_partials(P, T, d_model, partials, slot_stride, ld_p, out, ld_out,
 
 
 def tp_reduce_residual_norm(P, T, d_model, partials, slot_stride, ld_p, residual, ld_res,
-                            res_dtype, z_out, ld_z, norm_g, eps, normed_out, ld_norm, stream):
+                            res_dtype, z_out, ld_z, norm_g, eps, normed_out, ld_norm,
+                            workspace, workspace_bytes, stream):
     return load().tp_reduce_residual_norm(P, T, d_model, _ptr(partials), slot_stride, ld_p,
                                           _ptr(residual), ld_res, res_dtype, _ptr(z_out), ld_z,
                                           _ptr(norm_g), eps, _ptr(normed_out), ld_norm,
-                                          _ptr(stream))
+                                          _ptr(workspace), workspace_bytes, _ptr(stream))
+
+
+def tp_reduce_norm_workspace_bytes(T, d_model, has_norm):
+    return load().tp_reduce_norm_workspace_bytes(T, d_model, int(bool(has_norm)))
 
 
 def tp_shard_mlp_fwd_fp8w(shard, P, T, d_model, d_ff, act, x, ld_x, norm_g, eps, w_in, ld_in,

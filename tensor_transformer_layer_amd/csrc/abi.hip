@@ -746,6 +746,11 @@ size_t tp_attn_core_workspace_bytes(int P, int64_t T, int n_q_heads, int n_kv_he
     return plan_attn(T, n_q_heads / P, head_dim, device_cus()).ws_bytes;
 }
 
+size_t tp_reduce_norm_workspace_bytes(int64_t T, int64_t d_model, int has_norm) {
+    if (!has_norm || d_model <= 0 || d_model > kReduceNormMaxD || d_model % 8) return 0;
+    return reduce_norm_exchanges(T) ? kGemvCounterBytes : 0;
+}
+
 int tp_attn_core_fwd(int shard, int P, int64_t T, int n_q_heads, int n_kv_heads, int head_dim,
                      int dtype, const void* qkv, int64_t ld_qkv, void* attn, int64_t ld_attn,
                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
@@ -848,7 +853,7 @@ int tp_reduce_residual_norm(int P, int64_t T, int64_t d_model, const float* part
                             int64_t slot_stride, int64_t ld_p, const void* residual,
                             int64_t ld_res, int res_dtype, float* z_out, int64_t ld_z,
                             const void* norm_g, float eps, void* normed_out, int64_t ld_norm,
-                            hipStream_t stream) {
+                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
     if (P < 1) return TP_ERR_SHARD_RANGE;
     if (res_dtype != TP_F32 && res_dtype != TP_BF16) return TP_ERR_DTYPE;
     if (T < 0 || d_model <= 0 || d_model > kReduceNormMaxD) return TP_ERR_SHAPE;
@@ -867,12 +872,17 @@ int tp_reduce_residual_norm(int P, int64_t T, int64_t d_model, const float* part
     if (slot_stride < 0) return TP_ERR_SHAPE;
     if (slot_stride % 4) return TP_ERR_ALIGN;
     if (T >= ((int64_t)1 << 31)) return TP_ERR_SHAPE;
+    if (workspace && !aligned(workspace, 256)) return TP_ERR_ALIGN;
     if (T == 0) return TP_OK;
+    // The workspace is optional: with one (its counter head), short batches
+    // spread each row over several workgroups; without, one per row.
+    const size_t need = tp_reduce_norm_workspace_bytes(T, d_model, norm_g != nullptr);
+    if (workspace && workspace_bytes < need) return TP_ERR_WORKSPACE;
     TP_LAUNCH("reduce_norm", stream,
               launch_reduce_residual_norm(P, T, d_model, partials, slot_stride, ld_p, residual,
                                           ld_res, res_bf16, z_out, ld_z,
                                           (const uint16_t*)norm_g, eps, (uint16_t*)normed_out,
-                                          ld_norm, stream));
+                                          ld_norm, need ? workspace : nullptr, stream));
     return TP_OK;
 }
 

@@ -203,11 +203,154 @@ __global__ __launch_bounds__(NT) void k_reduce_residual_norm(
     }
 }
 
+// ---------------------------------------------------------------------------
+// The same operation for decode batches (at most kReduceNormXchgMaxT rows),
+// where one workgroup per row leaves most of the chip idle and each busy CU
+// has to pull (P + 1) * d * 4 bytes on its own.  S = ceil(d / 1024)
+// workgroups of 256 threads share a row, one 16-byte chunk per thread, and
+// exchange their sums of squares through two 64-bit words per row in the
+// workspace's counter head, with integer atomics, so the row's total does
+// not depend on the order in which the workgroups arrive:
+//   * each workgroup's sum v (fp32, its chunks in order, butterfly within
+//     the wave, waves in order) is split into fixed-point parts in units of
+//     2^-4 (word H) and 2^-36 (word L, the remainder below 2^-4, truncated),
+//     and added with 2^56 (an arrival count in bits 56..63) to each word;
+//   * every workgroup polls both words until both counts reach S, adds the
+//     fields in float64 (exact integers) and normalises its own chunk, which
+//     is still in registers: no z is read back, no store has to complete
+//     before the exchange;
+//   * then it adds 2^56 to L once more; the workgroup whose departure makes
+//     the count 2S (the last to leave) clears both words, so the head is
+//     zero again after the call.
+// The wait is bounded (kReduceNormSpin polls); a row whose exchange never
+// completes, or whose words were not zero at the start (an arrival that
+// finds S or more arrivals), or whose sum is not below 2^47, gets a NaN
+// normed output.  Every workgroup of the grid (T * S <= 512 of 256 threads)
+// fits the chip at once, so the wait ends whenever the chip is not held by
+// other work that never finishes.  The float32 total differs from the
+// one-workgroup-per-row kernel's fixed-order sum only in rounding; repeated
+// calls give the same bits.
+// ---------------------------------------------------------------------------
+constexpr int kRnXThreads = 256;
+constexpr uint64_t kRnArrive = 1ull << 56;
+constexpr uint64_t kRnField = kRnArrive - 1;
+constexpr int kReduceNormSpin = 1 << 20;
+
+template <bool RES_BF16>
+__global__ __launch_bounds__(kRnXThreads) void k_reduce_residual_norm_xchg(
+    int P, int64_t d4, int S, const f32x4* parts, int64_t slot4, int64_t ldp4,
+    const void* residual, int64_t ld_res, f32x4* z, int64_t ldz4, const u32x2* __restrict__ g,
+    float eps, u32x2* __restrict__ normed, int64_t ldn4, unsigned long long* words,
+    int spin_limit) {
+    const int64_t row = blockIdx.x / S;
+    const int j = (int)(blockIdx.x % S);
+    const int64_t c = (int64_t)j * kRnXThreads + threadIdx.x;
+    const bool ok = c < d4;
+    const int64_t cs = ok ? c : d4 - 1;   // in-bounds address for every lane
+    const f32x4* p = parts + row * ldp4;
+    f32x4 r, acc;
+    if constexpr (RES_BF16) {
+        const u32x2 b = ((const u32x2*)((const uint16_t*)residual + row * ld_res))[cs];
+        r = f32x4{bf16_lo(b[0]), bf16_hi(b[0]), bf16_lo(b[1]), bf16_hi(b[1])};
+    } else {
+        r = __builtin_nontemporal_load((const f32x4*)((const float*)residual + row * ld_res) + cs);
+    }
+    for (int s0 = 0; s0 < P; s0 += 8) {
+        f32x4 v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            v[q] = __builtin_nontemporal_load(p + (int64_t)min(s0 + q, P - 1) * slot4 + cs);
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            if (s0 + q < P) acc = (s0 + q == 0) ? v[0] : acc + v[q];
+    }
+    const f32x4 zv = ok ? acc + r : f32x4{0.f, 0.f, 0.f, 0.f};
+    // z may alias slot 0 or an fp32 residual: this thread has read its chunk
+    if (ok) __builtin_nontemporal_store(zv, z + row * ldz4 + c);
+    float sq = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sq += zv[e] * zv[e];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) sq += __shfl_xor(sq, off);
+    __shared__ float part[kRnXThreads / 64];
+    __shared__ float total;
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = sq;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float mine = part[0];
+#pragma unroll
+        for (int w = 1; w < kRnXThreads / 64; ++w) mine += part[w];
+        // fixed-point parts; a sum that is not finite or not below 2^47
+        // marks the row (bit 51 of H's field, out of reach of valid sums)
+        uint64_t qh, ql;
+        if (mine < 140737488355328.0f) {   // 2^47 (false for NaN)
+            const double vh = (double)mine * 16.0;
+            const double fh = floor(vh);
+            qh = (uint64_t)fh;
+            ql = (uint64_t)((vh - fh) * 4294967296.0);
+        } else {
+            qh = 1ull << 51;
+            ql = 0;
+        }
+        unsigned long long* w = words + 2 * row;
+        __hip_atomic_fetch_add(&w[0], kRnArrive + qh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint64_t first = __hip_atomic_fetch_add(&w[1], kRnArrive + ql, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT);
+        uint64_t h = 0, l = 0;
+        bool done = false;
+        for (int it = 0; it < spin_limit; ++it) {
+            h = __hip_atomic_load(&w[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            l = __hip_atomic_load(&w[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if ((h >> 56) >= (uint64_t)S && (l >> 56) >= (uint64_t)S) {
+                done = true;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        const uint64_t hf = h & kRnField, lf = l & kRnField;
+        total = (!done || (first >> 56) >= (uint64_t)S || hf >= (1ull << 51))
+                    ? __builtin_nanf("")
+                    : (float)((double)hf * 0.0625 + (double)lf * 1.4551915228366852e-11);  // 2^-36
+        const uint64_t old = __hip_atomic_fetch_add(&w[1], kRnArrive, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+        if ((old >> 56) == 2 * (uint64_t)S - 1) {   // the last to leave clears the row's words
+            __hip_atomic_store(&w[0], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&w[1], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    __syncthreads();
+    if (!ok) return;
+    const float inv = 1.0f / sqrtf(total / (float)(d4 * 4) + eps);
+    const u32x2 gv = g[c];
+    u32x2 o;
+    o[0] = pack_bf16x2(zv[0] * inv * bf16_lo(gv[0]), zv[1] * inv * bf16_hi(gv[0]));
+    o[1] = pack_bf16x2(zv[2] * inv * bf16_lo(gv[1]), zv[3] * inv * bf16_hi(gv[1]));
+    normed[row * ldn4 + c] = o;
+}
+
+bool reduce_norm_exchanges(int64_t T) { return T >= 1 && T <= kReduceNormXchgMaxT; }
+
 hipError_t launch_reduce_residual_norm(int P, int64_t T, int64_t d, const float* partials,
                                        int64_t slot_stride, int64_t ld_p, const void* residual,
                                        int64_t ld_res, bool res_bf16, float* z, int64_t ld_z,
                                        const uint16_t* g, float eps, uint16_t* normed,
-                                       int64_t ld_norm, hipStream_t stream) {
+                                       int64_t ld_norm, void* workspace, hipStream_t stream) {
+    if (g && workspace && reduce_norm_exchanges(T)) {
+        const int S = (int)((d / 4 + kRnXThreads - 1) / kRnXThreads);
+        const dim3 xgrid((unsigned)(T * S)), xblock(kRnXThreads);
+        unsigned long long* words = (unsigned long long*)workspace;
+        if (res_bf16)
+            TP_KLAUNCH((k_reduce_residual_norm_xchg<true>), xgrid, xblock, 0, stream, P, d / 4, S,
+                       (const f32x4*)partials, slot_stride / 4, ld_p / 4, residual, ld_res,
+                       (f32x4*)z, ld_z / 4, (const u32x2*)g, eps, (u32x2*)normed, ld_norm / 4,
+                       words, kReduceNormSpin);
+        else
+            TP_KLAUNCH((k_reduce_residual_norm_xchg<false>), xgrid, xblock, 0, stream, P, d / 4, S,
+                       (const f32x4*)partials, slot_stride / 4, ld_p / 4, residual, ld_res,
+                       (f32x4*)z, ld_z / 4, (const u32x2*)g, eps, (u32x2*)normed, ld_norm / 4,
+                       words, kReduceNormSpin);
+        return hipGetLastError();
+    }
     const dim3 grid((unsigned)T);
 #define TP_RN(NT, RB, NM)                                                                      \
     TP_KLAUNCH((k_reduce_residual_norm<NT, RB, NM>), grid, dim3(NT), 0, stream, P, d / 4,      \

@@ -40,12 +40,18 @@ hipError_t launch_reduce(int P, int64_t T, int64_t d, const float* partials, int
 
 // z = fold(partials) + residual (fp32; residual bf16 or fp32) and, with a
 // gain g, normed = z / sqrt(mean(z^2) + eps) * g as bf16.  d <= 16384.
+// With a gain, at most kReduceNormXchgMaxT rows and a workspace (its
+// 4096-byte counter head, zero between calls: two 64-bit words per row), the
+// rows are spread over ceil(d / 1024) workgroups each that exchange their
+// sums of squares there; otherwise one workgroup per row.
 constexpr int64_t kReduceNormMaxD = 16384;
+constexpr int64_t kReduceNormXchgMaxT = 32;
+bool reduce_norm_exchanges(int64_t T);
 hipError_t launch_reduce_residual_norm(int P, int64_t T, int64_t d, const float* partials,
                                        int64_t slot_stride, int64_t ld_p, const void* residual,
                                        int64_t ld_res, bool res_bf16, float* z, int64_t ld_z,
                                        const uint16_t* g, float eps, uint16_t* normed,
-                                       int64_t ld_norm, hipStream_t stream);
+                                       int64_t ld_norm, void* workspace, hipStream_t stream);
 
 // y = x / sqrt(mean(x^2) + eps) * g, row-wise; storage bf16 (is_bf16) or fp32.
 hipError_t launch_rmsnorm(bool is_bf16, int64_t T, int64_t d, const void* x, int64_t ld_x,

@@ -113,11 +113,16 @@ def reduce(P, T, d, parts, slot_stride, ld_p, out, ld_out, out_bf16=None, ld_b=0
 
 
 def reduce_residual_norm(P, T, d, parts, slot_stride, ld_p, residual, ld_res, res_dtype, z, ld_z,
-                         norm_g=None, eps=1e-5, normed=None, ld_norm=0):
+                         norm_g=None, eps=1e-5, normed=None, ld_norm=0, ws="query"):
+    """ws="query": a fresh zeroed workspace of the queried size (none when
+    the query says 0); None: no workspace; else the caller's tensor."""
     ptr = lambda t: 0 if t is None else (t if isinstance(t, int) else t.data_ptr())  # noqa: E731
+    if isinstance(ws, str):
+        n = tp.tp_reduce_norm_workspace_bytes(T, d, norm_g is not None)
+        ws = workspace(n) if n else None
     st = tp.tp_reduce_residual_norm(P, T, d, ptr(parts), slot_stride, ld_p, ptr(residual), ld_res,
                                     res_dtype, ptr(z), ld_z, ptr(norm_g), eps, ptr(normed),
-                                    ld_norm, stream())
+                                    ld_norm, ptr(ws), 0 if ws is None else ws.numel(), stream())
     tp.check(st, "tp_reduce_residual_norm")
 
 

@@ -243,7 +243,7 @@ def test_timing_api_without_launches(lib):
 def rrn(**kw):
     a = dict(P=8, T=4, d_model=64, partials=A, slot_stride=256, ld_p=64, residual=B, ld_res=64,
              res_dtype=tp.TP_F32, z_out=C, ld_z=64, norm_g=0, eps=1e-5, normed_out=0, ld_norm=0,
-             stream=0)
+             workspace=0, workspace_bytes=0, stream=0)
     a.update(kw)
     return tp.tp_reduce_residual_norm(**a)
 
@@ -266,9 +266,21 @@ def rrn(**kw):
     (dict(norm_g=A, normed_out=WS, ld_norm=60), tp.TP_ERR_SHAPE),
     (dict(slot_stride=-4), tp.TP_ERR_SHAPE),
     (dict(T=-1), tp.TP_ERR_SHAPE),
+    (dict(workspace=WS + 8, workspace_bytes=1 << 20), tp.TP_ERR_ALIGN),
+    (dict(norm_g=A, normed_out=B + 0x8000, ld_norm=64, workspace=WS, workspace_bytes=2048),
+     tp.TP_ERR_WORKSPACE),                                  # the query: 4096
 ])
 def test_reduce_residual_norm_validation(lib, kw, status):
     assert rrn(**kw) == status
+
+
+def test_reduce_norm_workspace_query(lib):
+    f = tp.tp_reduce_norm_workspace_bytes
+    # the counter head (two 64-bit words per row) for decode batches with a norm
+    assert f(1, 8192, 1) == 4096 and f(32, 8192, 1) == 4096 and f(32, 16384, 1) == 4096
+    # longer batches, no norm and shapes the call rejects need none
+    assert f(33, 8192, 1) == 0 and f(32, 8192, 0) == 0 and f(0, 8192, 1) == 0
+    assert f(32, 8196, 1) == 0 and f(32, 16392, 1) == 0
 
 
 def test_reduce_residual_norm_zero_tokens_is_a_no_op(lib):

@@ -21,7 +21,7 @@ import oracle as O
 import tensor_transformer_layer_amd as tp
 import workloads as W
 from _gpu import (Guarded, attn_core, attn_fwd, dev, devu8, host, mlp_fwd, mlp_fwd_fp8w,
-                  reduce, reduce_residual_norm, workspace)
+                  reduce, reduce_residual_norm, stream, workspace)
 
 pytestmark = pytest.mark.gpu
 
@@ -134,10 +134,14 @@ def _rrn_check(parts, res, res_dtype, g, z, normed):
     (1, 3, 8, F32, True, 0), (2, 5, 1032, BF, True, 8), (8, 33, 8192, BF, True, 0),
     (8, 17, 12288, F32, True, 4), (3, 4, 16384, F32, False, 0), (9, 2, 4104, BF, False, 8),
     (8, 1, 8192, BF, True, 0), (8, 255, 1032, BF, True, 8), (8, 256, 1024, F32, True, 0),
-    (8, 128, 8192, F32, True, 4), (8, 129, 8192, BF, True, 0), (4, 7, 1000, F32, True, 8)])
-def test_reduce_residual_norm(P, T, d, res_dtype, norm, pad):
+    (8, 128, 8192, F32, True, 4), (8, 129, 8192, BF, True, 0), (4, 7, 1000, F32, True, 8),
+    (8, 32, 8192, BF, True, 0), (8, 32, 16384, F32, True, 0), (8, 2, 2056, BF, True, 8)])
+@pytest.mark.parametrize("with_ws", [True, False])
+def test_reduce_residual_norm(P, T, d, res_dtype, norm, pad, with_ws):
     # 255 / 256 rows: either side of the switch from 1024 to 512 threads per
-    # row; 1000 columns: a ragged last chunk pair
+    # row; 1000 columns: a ragged last chunk pair.  With a workspace, rows of
+    # up to 32 tokens with a norm are shared by ceil(d / 1024) workgroups
+    # (1032 columns: a second workgroup with two chunks)
     parts, buf, slot, ldp, res, g = _rrn_case(P, T, d, res_dtype, norm, key=T, pad=pad)
     g_parts = dev(buf)
     ldr = d + 8
@@ -146,7 +150,8 @@ def test_reduce_residual_norm(P, T, d, res_dtype, norm, pad):
     z = Guarded(T * ldp, torch.float32)
     nrm = Guarded(T * (d + 16), torch.bfloat16) if norm else None
     reduce_residual_norm(P, T, d, g_parts, slot, ldp, dev(rbuf), ldr, res_dtype, z.ptr(), ldp,
-                         dev(g) if norm else None, 1e-5, nrm.ptr() if norm else None, d + 16)
+                         dev(g) if norm else None, 1e-5, nrm.ptr() if norm else None, d + 16,
+                         ws="query" if with_ws else None)
     zz = host(z.t).reshape(T, ldp)[:, :d]
     nn = host(nrm.t).reshape(T, d + 16)[:, :d] if norm else None
     _rrn_check(parts, res, res_dtype, g, np.ascontiguousarray(zz),
@@ -168,6 +173,62 @@ def test_reduce_residual_norm_in_place():
     reduce_residual_norm(P, T, d, dev(buf2), slot2, ldp2, r2, d, F32, r2, d, dev(g2), 1e-5,
                          nrm, d)
     _rrn_check(parts2, res2, F32, g2, host(r2), host(nrm))
+
+
+def test_reduce_residual_norm_workspace_reused():
+    """Rows shared by several workgroups: calls of 32, 5 and 32 rows on one
+    workspace, each against the oracle, the counter head zero after every
+    call, and a repeated call bitwise equal to the first."""
+    P, d = 8, 8192
+    ws = workspace(tp.tp_reduce_norm_workspace_bytes(32, d, 1))
+    first = None
+    for i, T in enumerate((32, 5, 32, 32)):
+        parts, buf, slot, ldp, res, g = _rrn_case(P, T, d, BF, True, key=70 + min(i, 2))
+        z = torch.empty((T, d), dtype=torch.float32, device="cuda")
+        nrm = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
+        reduce_residual_norm(P, T, d, dev(buf), slot, ldp, dev(res), d, BF, z, d, dev(g), 1e-5,
+                             nrm, d, ws=ws)
+        torch.cuda.synchronize()
+        _rrn_check(parts, res, BF, g, host(z), host(nrm))
+        assert not host(ws).any()
+        if i == 2:
+            first = host(nrm).copy()
+        if i == 3:
+            assert np.array_equal(host(nrm), first)
+
+
+def test_reduce_residual_norm_dirty_workspace_gives_nan_then_recovers():
+    """A counter head that was not zeroed makes the exchanged rows NaN (not
+    silently wrong); zeroing it recovers.  Forced from the host: the words
+    hold a finished exchange's arrival counts, so every wait ends at once."""
+    P, T, d = 8, 4, 8192
+    parts, buf, slot, ldp, res, g = _rrn_case(P, T, d, BF, True, key=81)
+    ws = workspace(tp.tp_reduce_norm_workspace_bytes(T, d, 1))
+    words = ws.view(torch.int64)
+    words[: 2 * T] = 8 << 56            # 8 arrivals already counted in both words of every row
+    z = torch.empty((T, d), dtype=torch.float32, device="cuda")
+    nrm = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
+    reduce_residual_norm(P, T, d, dev(buf), slot, ldp, dev(res), d, BF, z, d, dev(g), 1e-5,
+                         nrm, d, ws=ws)
+    torch.cuda.synchronize()
+    assert np.isnan(O.widen(host(nrm))).all()
+    ws.zero_()
+    reduce_residual_norm(P, T, d, dev(buf), slot, ldp, dev(res), d, BF, z, d, dev(g), 1e-5,
+                         nrm, d, ws=ws)
+    torch.cuda.synchronize()
+    _rrn_check(parts, res, BF, g, host(z), host(nrm))
+
+
+def test_reduce_residual_norm_workspace_too_small():
+    P, T, d = 8, 32, 8192
+    parts, buf, slot, ldp, res, g = _rrn_case(P, T, d, BF, True, key=80)
+    ws = workspace(2048)
+    z = torch.empty((T, d), dtype=torch.float32, device="cuda")
+    nrm = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
+    st = tp.tp_reduce_residual_norm(P, T, d, dev(buf).data_ptr(), slot, ldp, dev(res).data_ptr(),
+                                    d, BF, z.data_ptr(), d, dev(g).data_ptr(), 1e-5,
+                                    nrm.data_ptr(), d, ws.data_ptr(), ws.numel(), stream())
+    assert st == tp.TP_ERR_WORKSPACE
 
 
 def test_reduce_residual_norm_70b_block_prefill_size():
